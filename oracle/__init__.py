@@ -1,0 +1,24 @@
+"""Float64 CPU oracle for jagged HSTU attention — test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never calls it.
+"""
+
+from .hstu_oracle import (  # noqa: F401
+    attn_bwd,
+    attn_fwd,
+    bucket_edges,
+    bucketize,
+    causal_pairs,
+    chunk_bounds,
+    cp_attn_bwd,
+    cp_attn_fwd,
+    cp_local_offsets,
+    cp_rank_pairs,
+    rank_chunks,
+    rank_rows,
+    reorder,
+    reorder_index,
+    silu,
+    silu_grad,
+)

@@ -1,0 +1,339 @@
+"""Float64 CPU oracle for jagged HSTU attention (test infrastructure only).
+
+This module is the independent reference that the HIP path is checked against.
+It is test infrastructure: only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import it.  It shares no code with the HIP
+library (``jagged_hstu_attention_amd``) and imports nothing from it.
+
+Sources (the pages; titles abbreviated):
+
+* [CP]   "Scaling Generative Recommendations with Context Parallelism on
+         Hierarchical Sequential Transducers" (arXiv 2508.04711, LaTeX source).
+* [HSTU] "Actions Speak Louder than Words: Trillion-Parameter Sequential
+         Transducers for Generative Recommendations" (arXiv 2402.17152v3 summary).
+* [REV]  Pith review of the CP paper (pith.science).
+
+What is computed, with the readings taken where the pages are open
+(each reading is listed again in the design notes):
+
+1. Attention, [CP] §2.1 HSTUAttention equation:
+   O = Mask(SiLU((Q Kᵀ + Bias) / sqrt(d_k))) V.  No softmax or any other
+   normalisation of the weights ([HSTU] §3.1, pointwise aggregated attention).
+   d_k is the Q/K width.  The bias sits inside the division (equation as set).
+   SiLU(x) = x * sigmoid(x).  Mask is causal, including the diagonal, and
+   block-diagonal over the jagged sequences ([CP] §2.3 causal mask).
+2. Bias, [CP] §2.1 (timestamp bias paragraph): a difference of timestamps,
+   a transformation, then a grouping into bucket indices that select from the
+   learnable ``ts_weights``.  Reading: the difference is taken per query/key
+   pair (Δ = ts_query - ts_key; [REV] speaks of biases for query-key pairs),
+   the transformation is log2|Δ|, and the grouping is NB equal-width bins of
+   log2|Δ| over [0, 32), i.e. bucket(Δ) = #{k in [1, NB): |Δ| >= E_k} with
+   E_k = ceil(2^(32 k / NB)).  The integer edge table is the definition; it is
+   computed here exactly with Python integers.
+3. Backward: plain calculus of 1-2 (gradients w.r.t. Q, K, V and ts_weights);
+   the weights are never normalised, so no statistics are needed.
+4. Context-parallel share, [CP] §2.3 load balancing: each sequence is cut into
+   2C mini-chunks and rank r holds chunks r and 2C-1-r.  Chunk k of a length-L
+   sequence is rows [floor(kL/2C), floor((k+1)L/2C)) (reading for L not divisible
+   by 2C).  A rank's query rows keep their global positions and global
+   timestamps, and attend to their causal key prefix of the full sequence.
+5. Reorder, [CP] §2.3 (memory-reordering data shuffle): the rank-major
+   permutation of rows; rank, then sequence, then chunk r then chunk 2C-1-r.
+
+All floating-point arithmetic is float64; timestamps stay exact integers.
+Every function takes the exact values the device sees (bf16 inputs widened
+exactly to float64).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+BUCKET_LOG2_SPAN = 32  # the bins of log2|Δ| cover [0, 32)
+
+
+# --------------------------------------------------------------------------
+# 2. Timestamp bucketing ([CP] §2.1, timestamp bias paragraph)
+# --------------------------------------------------------------------------
+
+def _ceil_root_pow2(exponent: int, n: int) -> int:
+    """Smallest integer x >= 0 with x**n >= 2**exponent, exactly."""
+    target = 1 << exponent
+    x = int(math.ceil(2.0 ** (exponent / n)))
+    while x > 0 and (x - 1) ** n >= target:
+        x -= 1
+    while x ** n < target:
+        x += 1
+    return x
+
+
+def bucket_edges(num_buckets: int) -> List[int]:
+    """Exact integer edges E_k = ceil(2^(32 k / NB)) for k = 1 .. NB-1.
+
+    Edge k is the smallest integer x with x^NB >= 2^(32 k).  The returned list
+    has NB-1 entries (index k-1 holds E_k); it is non-decreasing and may repeat
+    values for small k when NB > 32.
+    """
+    if num_buckets < 1:
+        raise ValueError("num_buckets must be >= 1")
+    return [_ceil_root_pow2(BUCKET_LOG2_SPAN * k, num_buckets) for k in range(1, num_buckets)]
+
+
+def bucketize(delta: np.ndarray, num_buckets: int) -> np.ndarray:
+    """bucket(Δ) = #{k in [1, NB): |Δ| >= E_k}, exact on int64 Δ (|Δ| < 2^63)."""
+    delta = np.asarray(delta, dtype=np.int64)
+    mag = np.abs(delta)
+    edges = np.asarray(bucket_edges(num_buckets), dtype=np.int64)
+    if edges.size == 0:
+        return np.zeros(mag.shape, dtype=np.int64)
+    return np.searchsorted(edges, mag, side="right").astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# 1. Forward ([CP] §2.1 HSTUAttention equation)
+# --------------------------------------------------------------------------
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def silu_grad(x):
+    s = 1.0 / (1.0 + np.exp(-x))
+    return s * (1.0 + x * (1.0 - s))
+
+
+def _seq_scores(qb, kb, tsq, tsk, wh, nb, alpha):
+    """s = alpha * (q·k + w[bucket(ts_q - ts_k)]) for one (sequence, head)."""
+    raw = qb @ kb.T
+    bucket = bucketize(tsq[:, None] - tsk[None, :], nb)
+    return alpha * (raw + wh[bucket]), bucket
+
+
+def attn_fwd(q, k, v, offsets, ts, w, num_buckets) -> np.ndarray:
+    """Jagged HSTU attention forward.
+
+    q, k: [T, H, d_qk]; v: [T, H, d_v]; offsets: int64 [B+1]; ts: int64 [T];
+    w: [H, NB].  Returns O [T, H, d_v] in float64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    w = np.asarray(w, np.float64)
+    ts = np.asarray(ts, np.int64)
+    T, H, dqk = q.shape
+    alpha = 1.0 / math.sqrt(dqk)
+    out = np.zeros((T, H, v.shape[2]), dtype=np.float64)
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi <= lo:
+            continue
+        n = hi - lo
+        mask = np.tril(np.ones((n, n), dtype=bool))
+        for h in range(H):
+            s, _ = _seq_scores(q[lo:hi, h], k[lo:hi, h], ts[lo:hi], ts[lo:hi], w[h],
+                               num_buckets, alpha)
+            a = np.where(mask, silu(s), 0.0)
+            out[lo:hi, h] = a @ v[lo:hi, h]
+    return out
+
+
+# --------------------------------------------------------------------------
+# 3. Backward
+# --------------------------------------------------------------------------
+
+def attn_bwd(dout, q, k, v, offsets, ts, w, num_buckets):
+    """Gradients of sum(dout * O) w.r.t. q, k, v and w (float64).
+
+    With s = alpha*(q·k + w[bucket]) and a = SiLU(s)*mask:
+      dP = dO Vᵀ;  G = alpha * dP * SiLU'(s) * mask;
+      dV = aᵀ dO;  dQ = G K;  dK = Gᵀ Q;  dW[h, b] = sum of G over pairs in bucket b.
+    Returns (dq, dk, dv, dw) with dw of shape [H, NB].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    w = np.asarray(w, np.float64)
+    dout = np.asarray(dout, np.float64)
+    ts = np.asarray(ts, np.int64)
+    T, H, dqk = q.shape
+    alpha = 1.0 / math.sqrt(dqk)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dw = np.zeros((H, num_buckets), dtype=np.float64)
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi <= lo:
+            continue
+        n = hi - lo
+        mask = np.tril(np.ones((n, n), dtype=bool))
+        for h in range(H):
+            s, bucket = _seq_scores(q[lo:hi, h], k[lo:hi, h], ts[lo:hi], ts[lo:hi], w[h],
+                                    num_buckets, alpha)
+            a = np.where(mask, silu(s), 0.0)
+            dp = dout[lo:hi, h] @ v[lo:hi, h].T
+            g = np.where(mask, alpha * dp * silu_grad(s), 0.0)
+            dv[lo:hi, h] = a.T @ dout[lo:hi, h]
+            dq[lo:hi, h] = g @ k[lo:hi, h]
+            dk[lo:hi, h] = g.T @ q[lo:hi, h]
+            dw[h] += np.bincount(bucket[mask], weights=g[mask], minlength=num_buckets)
+    return dq, dk, dv, dw
+
+
+# --------------------------------------------------------------------------
+# 4. Context-parallel share ([CP] §2.3, load-balanced mini-chunks)
+# --------------------------------------------------------------------------
+
+def chunk_bounds(length: int, cp_size: int, chunk: int) -> Tuple[int, int]:
+    """Rows [floor(k L / 2C), floor((k+1) L / 2C)) of mini-chunk k."""
+    nchunks = 2 * cp_size
+    return (chunk * length) // nchunks, ((chunk + 1) * length) // nchunks
+
+
+def rank_chunks(cp_size: int, rank: int) -> Tuple[int, int]:
+    """Rank r holds mini-chunks r and 2C-1-r."""
+    return rank, 2 * cp_size - 1 - rank
+
+
+def reorder_index(offsets: Sequence[int], cp_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Row permutation of the load-balanced layout, by explicit nested loops.
+
+    Returns (idx, out_offsets): output row i is input row idx[i]; out_offsets
+    has cp_size*B + 1 entries, one segment per (rank, sequence).
+    """
+    B = len(offsets) - 1
+    idx: List[int] = []
+    out_offsets = [0]
+    for r in range(cp_size):
+        for b in range(B):
+            start = int(offsets[b])
+            length = int(offsets[b + 1]) - start
+            for c in rank_chunks(cp_size, r):
+                c0, c1 = chunk_bounds(length, cp_size, c)
+                for row in range(c0, c1):
+                    idx.append(start + row)
+            out_offsets.append(len(idx))
+    return np.asarray(idx, dtype=np.int64), np.asarray(out_offsets, dtype=np.int64)
+
+
+def reorder(x: np.ndarray, offsets, cp_size: int, inverse: bool = False):
+    """Apply the load-balanced permutation to the leading (row) axis of x."""
+    idx, out_offsets = reorder_index(offsets, cp_size)
+    x = np.asarray(x)
+    if not inverse:
+        return x[idx], out_offsets
+    out = np.empty_like(x)
+    out[idx] = x
+    return out, out_offsets
+
+
+def rank_rows(offsets, cp_size: int, rank: int):
+    """For one rank: per sequence, the list of (global row, position) it holds,
+    in the rank's local order (chunk r then chunk 2C-1-r)."""
+    rows = []
+    for b in range(len(offsets) - 1):
+        start = int(offsets[b])
+        length = int(offsets[b + 1]) - start
+        seq_rows = []
+        for c in rank_chunks(cp_size, rank):
+            c0, c1 = chunk_bounds(length, cp_size, c)
+            seq_rows.extend((start + p, p) for p in range(c0, c1))
+        rows.append(seq_rows)
+    return rows
+
+
+def cp_local_offsets(offsets, cp_size: int, rank: int) -> np.ndarray:
+    lens = [len(r) for r in rank_rows(offsets, cp_size, rank)]
+    out = np.zeros(len(lens) + 1, dtype=np.int64)
+    out[1:] = np.cumsum(lens)
+    return out
+
+
+def cp_attn_fwd(q_local, k, v, offsets, ts, w, num_buckets, cp_size, rank):
+    """One rank's share of the forward.
+
+    q_local: [Tr, H, d_qk], the rank's query rows in local order; k, v, ts are
+    the full global tensors.  Each local row at global position p attends to
+    keys 0..p of its sequence with global timestamps.  Returns [Tr, H, d_v].
+    """
+    q_local = np.asarray(q_local, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    w = np.asarray(w, np.float64)
+    ts = np.asarray(ts, np.int64)
+    H, dqk = q_local.shape[1], q_local.shape[2]
+    alpha = 1.0 / math.sqrt(dqk)
+    out = np.zeros((q_local.shape[0], H, v.shape[2]), dtype=np.float64)
+    local = 0
+    for b, seq_rows in enumerate(rank_rows(offsets, cp_size, rank)):
+        start = int(offsets[b])
+        for (grow, p) in seq_rows:
+            keys = slice(start, start + p + 1)
+            for h in range(H):
+                s, _ = _seq_scores(q_local[local:local + 1, h], k[keys, h],
+                                   ts[grow:grow + 1], ts[keys], w[h], num_buckets, alpha)
+                out[local, h] = silu(s)[0] @ v[keys, h]
+            local += 1
+    return out
+
+
+def cp_attn_bwd(dout_local, q_local, k, v, offsets, ts, w, num_buckets, cp_size, rank):
+    """One rank's share of the backward.
+
+    Returns (dq_local [Tr,H,d_qk], dk [T,H,d_qk], dv [T,H,d_v], dw [H,NB]) where
+    dk, dv and dw are this rank's partial sums (zeros for keys no local row
+    reaches); summing them over all ranks gives the unsharded gradients.
+    """
+    q_local = np.asarray(q_local, np.float64)
+    dout_local = np.asarray(dout_local, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    w = np.asarray(w, np.float64)
+    ts = np.asarray(ts, np.int64)
+    H, dqk = q_local.shape[1], q_local.shape[2]
+    alpha = 1.0 / math.sqrt(dqk)
+    dq = np.zeros_like(q_local)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dw = np.zeros((H, num_buckets), dtype=np.float64)
+    local = 0
+    for b, seq_rows in enumerate(rank_rows(offsets, cp_size, rank)):
+        start = int(offsets[b])
+        for (grow, p) in seq_rows:
+            keys = slice(start, start + p + 1)
+            for h in range(H):
+                s, bucket = _seq_scores(q_local[local:local + 1, h], k[keys, h],
+                                        ts[grow:grow + 1], ts[keys], w[h], num_buckets, alpha)
+                s = s[0]
+                bucket = bucket[0]
+                a = silu(s)
+                dp = v[keys, h] @ dout_local[local, h]
+                g = alpha * dp * silu_grad(s)
+                dv[keys, h] += np.outer(a, dout_local[local, h])
+                dq[local, h] = g @ k[keys, h]
+                dk[keys, h] += np.outer(g, q_local[local, h])
+                dw[h] += np.bincount(bucket, weights=g, minlength=num_buckets)
+            local += 1
+    return dq, dk, dv, dw
+
+
+# --------------------------------------------------------------------------
+# Counting (for the measurement: causal-effective pairs)
+# --------------------------------------------------------------------------
+
+def causal_pairs(lengths) -> int:
+    """Number of (i, j) with j <= i inside each sequence, summed."""
+    return int(sum(int(n) * (int(n) + 1) // 2 for n in lengths))
+
+
+def cp_rank_pairs(lengths, cp_size: int, rank: int) -> int:
+    """Causal pairs whose query row belongs to the rank's two mini-chunks."""
+    total = 0
+    for n in lengths:
+        for c in rank_chunks(cp_size, rank):
+            c0, c1 = chunk_bounds(int(n), cp_size, c)
+            total += sum(p + 1 for p in range(c0, c1))
+    return total
