@@ -1,0 +1,150 @@
+/*
+ * hstu.h — C ABI of the MI355X (gfx950) jagged HSTU attention library.
+ *
+ * The operation (Scaling Generative Recommendations with Context Parallelism on
+ * Hierarchical Sequential Transducers, §2.1, HSTUAttention equation):
+ *
+ *     O = Mask( SiLU( (Q Kᵀ + Bias) / sqrt(d_qk) ) ) V
+ *
+ * over jagged sequences packed token-major with int64 offsets (same paper, §2.2
+ * "Jagged Tensors": values plus offsets plus max_lengths).  Mask is causal
+ * (key position <= query position, diagonal included) within each sequence.
+ * There is no softmax: the SiLU weights are used as they are.
+ *
+ * Bias (same paper, §2.1, timestamp-bias paragraph): for query i and key j of
+ * one sequence, Δ = ts[i] - ts[j]; bucket = #{k in [1, NB) : |Δ| >= E_k} with
+ * integer edges E_k = ceil(2^(32 k / NB)), i.e. NB equal-width bins of log2|Δ|
+ * over [0, 32) (|Δ| <= 1 falls in bucket 0, |Δ| >= 2^32 in bucket NB-1);
+ * Bias = ts_weights[head, bucket].  The bias is inside the division by
+ * sqrt(d_qk), as the equation is set.
+ *
+ * Context-parallel share (same paper, §2.3, load-balanced mini-chunks): with
+ * cp_size = C > 1 and cp_rank = r, every sequence of length L is cut into 2C
+ * mini-chunks, chunk k being positions [floor(kL/2C), floor((k+1)L/2C)), and the
+ * rank holds chunks r and 2C-1-r.  Its query rows keep their global positions
+ * and global timestamps and attend to the causal key prefix of the full
+ * sequence (K, V and ts are passed whole).
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless marked "host".  Tensors are dense,
+ *     row-major, 16-byte aligned.  Jagged tensors are [rows, H, d].
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise the device with the host.  Host metadata
+ *     (max_seq_len, totals) comes from the caller.
+ *   - The caller owns all memory.  The library allocates no device memory and
+ *     keeps no state between calls except lazily loaded code objects and cached
+ *     device attributes (thread-safe).  Scratch memory is the caller's
+ *     `workspace` of at least hstu_workspace_size() bytes; it may be reused as
+ *     soon as the call's work on `stream` has finished.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Argument errors are detected on the host before anything is launched:
+ *     the call returns a non-zero hstu_status_t and hstu_last_error() gives a
+ *     message.  Device-side data contracts (offsets non-decreasing with
+ *     offsets[0] = 0 and offsets[B] = total_kv, |ts| < 2^62) are the caller's.
+ */
+#ifndef HSTU_H
+#define HSTU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { HSTU_BF16 = 0, HSTU_FP32 = 1 } hstu_dtype_t;
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_EINVAL = 1,        /* bad argument (null pointer, bad size, bad rank) */
+  HSTU_EUNSUPPORTED = 2,  /* valid but not built: head dim, bucket count     */
+  HSTU_EWORKSPACE = 3,    /* workspace missing or smaller than required      */
+  HSTU_EHIP = 4           /* a HIP runtime call or kernel launch failed      */
+} hstu_status_t;
+
+/* Problem description shared by the attention calls. */
+typedef struct {
+  int32_t dtype;        /* hstu_dtype_t of q, k, v, out, dout, ts_weights, dq, dk, dv */
+  int32_t reserved;     /* must be 0 */
+  int64_t num_seqs;     /* B >= 0 */
+  int64_t num_heads;    /* H >= 1 */
+  int64_t d_qk;         /* Q/K head width; supported: 32, 64, 128 */
+  int64_t d_v;          /* V head width; must equal d_qk in this build */
+  int64_t num_buckets;  /* NB in [1, 512] */
+  int64_t max_seq_len;  /* host copy of max_b (offsets[b+1] - offsets[b]) (the full
+                           global length when cp_size > 1); an upper bound is fine */
+  int64_t total_kv;     /* T = offsets[B]: rows of k, v, ts (and dk, dv) */
+  int64_t total_q;      /* rows of q, out, dout, dq: T when cp_size == 1, else the
+                           rank's row count sum_b (|chunk r| + |chunk 2C-1-r|) */
+  int64_t cp_size;      /* C >= 1 (1 = whole sequences) */
+  int64_t cp_rank;      /* r in [0, C) */
+} hstu_problem_t;
+
+/* Bytes of workspace needed by hstu_jagged_attn_fwd (backward = 0) or
+ * hstu_jagged_attn_bwd (backward = 1).  Returns 0 if the problem is invalid
+ * (hstu_last_error() then says why). */
+size_t hstu_workspace_size(const hstu_problem_t* p, int backward);
+
+/* Forward.  HSTUAttention equation (CP paper §2.1) on jagged inputs.
+ *   q        [total_q, H, d_qk]  (cp_size > 1: the rank's rows, chunk r then
+ *                                 chunk 2C-1-r per sequence, sequence-major —
+ *                                 exactly the rank-r slice of hstu_cp_reorder)
+ *   k        [total_kv, H, d_qk]
+ *   v        [total_kv, H, d_v]
+ *   offsets  int64 [B+1], global sequence offsets into k, v, ts
+ *   timestamps int64 [total_kv], per-token timestamps (global)
+ *   ts_weights [H, NB], bucket weights (dtype of q)
+ *   out      [total_q, H, d_v] (written)
+ *   workspace, workspace_bytes: scratch, >= hstu_workspace_size(p, 0)
+ * Arithmetic: bf16 operands with fp32 accumulation (bf16), or fp32 throughout. */
+int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k,
+                         const void* v, const int64_t* offsets,
+                         const int64_t* timestamps, const void* ts_weights,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Backward of the forward above for upstream gradient dout [total_q, H, d_v].
+ * Writes dq [total_q, H, d_qk], dk [total_kv, H, d_qk], dv [total_kv, H, d_v]
+ * (all in the input dtype, accumulated in fp32) and d_ts_weights [H, NB] (fp32).
+ * With cp_size > 1, dk, dv and d_ts_weights are this rank's partial sums (zero
+ * rows for keys no local query reaches); summing them over the C ranks gives
+ * the gradients of the unsharded problem.  Nothing is normalised, so no
+ * forward statistics are needed: the score tile is recomputed. */
+int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* q,
+                         const void* k, const void* v, const int64_t* offsets,
+                         const int64_t* timestamps, const void* ts_weights,
+                         void* dq, void* dk, void* dv, float* d_ts_weights,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Load-balanced chunk-pair reorder (CP paper §2.3, memory-reordering shuffle).
+ * A pure row permutation of `in` [total_rows, row_bytes] into `out` (same size,
+ * must not overlap `in`).  inverse = 0: sequence-major -> rank-major, i.e. for
+ * r in 0..C-1, for b in 0..B-1: rows of mini-chunk r then of mini-chunk 2C-1-r
+ * of sequence b.  inverse = 1: the opposite direction.  Bit-exact for any
+ * row_bytes (the bytes are copied, not interpreted); rows are copied with the
+ * widest of 16/8/4/1-byte accesses that row_bytes and the pointers allow.
+ * out_offsets (device, may be NULL): receives the int64 [C*B + 1] offsets of
+ * the rank-major segments (segment r*B + b = rank r's rows of sequence b),
+ * whichever the direction.  offsets: int64 [B+1] sequence offsets of the
+ * sequence-major layout; total_rows = offsets[B]. */
+int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes,
+                    const int64_t* offsets, int64_t num_seqs, int64_t total_rows,
+                    int64_t max_seq_len, int64_t cp_size, int inverse,
+                    int64_t* out_offsets, void* stream);
+
+/* Host helper: the integer bucket edges the kernels use.  Writes NB+1 uint32
+ * values to host memory edges_out: edges_out[0] = 0, edges_out[k] = E_k =
+ * ceil(2^(32k/NB)) for 1 <= k < NB, edges_out[NB] = 0xFFFFFFFF (sentinel). */
+int hstu_bucket_edges(int64_t num_buckets, uint32_t* edges_out);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* hstu_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int hstu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H */

@@ -1,0 +1,154 @@
+"""Jagged HSTU attention for MI355X (gfx950): thin Python binding of libhstu.so.
+
+Every function here only marshals arguments (device pointers taken from torch
+tensors, torch's current HIP stream) and calls the C ABI declared in
+include/hstu.h; all computation runs in the library's HIP kernels.  torch is
+used for device memory and streams only.
+
+    out = jagged_attn_fwd(q, k, v, offsets, ts, ts_weights, max_seq_len)
+    dq, dk, dv, dw = jagged_attn_bwd(dout, q, k, v, offsets, ts, ts_weights, max_seq_len)
+    y, seg_offsets = cp_reorder(x, offsets, max_seq_len, cp_size)
+
+Shapes: q, k, v, out, dout are [rows, H, d] (bf16 or fp32, contiguous, on the
+GPU); offsets int64 [B+1]; ts int64 [T]; ts_weights [H, NB] in the dtype of q.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import HSTU_BF16, HSTU_FP32, HstuError, Problem  # noqa: F401
+
+__all__ = [
+    "Problem", "HstuError", "problem", "workspace_size", "jagged_attn_fwd", "jagged_attn_bwd",
+    "cp_reorder", "bucket_edges", "version", "library_path",
+]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def version() -> int:
+    return _lib.load().hstu_version()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return HSTU_BF16
+    if t.dtype == torch.float32:
+        return HSTU_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def problem(q, k, v, offsets, ts_weights, max_seq_len: int, *, cp_size: int = 1, cp_rank: int = 0) -> Problem:
+    """Fill the hstu_problem_t for these tensors (host metadata only)."""
+    p = Problem()
+    p.dtype = _dtype_code(q)
+    p.reserved = 0
+    p.num_seqs = int(offsets.shape[0]) - 1
+    p.num_heads = int(q.shape[1])
+    p.d_qk = int(q.shape[2])
+    p.d_v = int(v.shape[2])
+    p.num_buckets = int(ts_weights.shape[1])
+    p.max_seq_len = int(max_seq_len)
+    p.total_kv = int(k.shape[0])
+    p.total_q = int(q.shape[0])
+    p.cp_size = int(cp_size)
+    p.cp_rank = int(cp_rank)
+    return p
+
+
+def workspace_size(p: Problem, backward: bool) -> int:
+    n = _lib.load().hstu_workspace_size(ctypes.byref(p), 1 if backward else 0)
+    if n == 0:
+        _lib.check(1)
+    return int(n)
+
+
+def _workspace(p: Problem, backward: bool, device, workspace=None):
+    torch = _torch()
+    need = workspace_size(p, backward)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, int(workspace.numel() * workspace.element_size())
+
+
+def jagged_attn_fwd(q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1, cp_rank: int = 0,
+                    out=None, workspace=None):
+    """Forward of jagged HSTU attention; returns out [total_q, H, d_v]."""
+    torch = _torch()
+    p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    ws, ws_bytes = _workspace(p, False, q.device, workspace)
+    lib = _lib.load()
+    _lib.check(lib.hstu_jagged_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets), _ptr(ts),
+                                        _ptr(ts_weights), _ptr(out), _ptr(ws), ws_bytes, _stream(q.device)))
+    return out
+
+
+def jagged_attn_bwd(dout, q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1,
+                    cp_rank: int = 0, dq=None, dk=None, dv=None, dw=None, workspace=None):
+    """Backward; returns (dq, dk, dv, d_ts_weights) with d_ts_weights in fp32."""
+    torch = _torch()
+    p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dw = torch.empty(ts_weights.shape, dtype=torch.float32, device=q.device) if dw is None else dw
+    ws, ws_bytes = _workspace(p, True, q.device, workspace)
+    lib = _lib.load()
+    _lib.check(lib.hstu_jagged_attn_bwd(ctypes.byref(p), _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                                        _ptr(ts), _ptr(ts_weights), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw),
+                                        _ptr(ws), ws_bytes, _stream(q.device)))
+    return dq, dk, dv, dw
+
+
+def cp_reorder(x, offsets, max_seq_len: int, cp_size: int, *, inverse: bool = False, out=None,
+               out_offsets=None, want_offsets: bool = True) -> Tuple[object, Optional[object]]:
+    """Load-balanced chunk-pair row permutation of x [rows, ...] (bit-exact).
+
+    Returns (y, seg_offsets) where seg_offsets (int64 [cp_size*B + 1], or None)
+    delimits the rank-major segments (rank r, sequence b) -> index r*B + b."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    B = int(offsets.shape[0]) - 1
+    if want_offsets and out_offsets is None:
+        out_offsets = torch.empty(cp_size * B + 1, dtype=torch.int64, device=x.device)
+    row_bytes = x.element_size() * math.prod(x.shape[1:])
+    lib = _lib.load()
+    _lib.check(lib.hstu_cp_reorder(_ptr(x), _ptr(out), row_bytes, _ptr(offsets), B, int(x.shape[0]),
+                                   int(max_seq_len), int(cp_size), 1 if inverse else 0,
+                                   _ptr(out_offsets) if out_offsets is not None else None, _stream(x.device)))
+    return out, out_offsets
+
+
+def bucket_edges(num_buckets: int):
+    """The library's integer edge table E[0..NB] (host computation) as a list."""
+    arr = (ctypes.c_uint32 * (num_buckets + 1))()
+    _lib.check(_lib.load().hstu_bucket_edges(int(num_buckets), arr))
+    return list(arr)

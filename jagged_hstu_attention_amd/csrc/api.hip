@@ -1,0 +1,402 @@
+// Host side of the C ABI declared in include/hstu.h: argument validation,
+// workspace layout, the integer bucket-edge table, and kernel launches on the
+// caller's stream.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "attn.h"
+#include "hstu.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HSTU_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// Bucket edges E_k = ceil(2^(32k/NB)).  For 32k/NB integral the edge is an
+// exact power of two.  Otherwise 2^(32k/NB) is irrational and the long-double
+// value is accurate to ~2^-31 absolute; a candidate is accepted once a
+// multi-word integer comparison confirms (E-1)^NB < 2^(32k) <= E^NB.
+// ---------------------------------------------------------------------------
+struct BigU {
+  std::vector<uint32_t> w;  // little-endian words
+  explicit BigU(uint64_t v = 0) {
+    while (v) {
+      w.push_back((uint32_t)v);
+      v >>= 32;
+    }
+  }
+  void mul(uint32_t m) {
+    uint64_t carry = 0;
+    for (auto& x : w) {
+      const uint64_t t = (uint64_t)x * m + carry;
+      x = (uint32_t)t;
+      carry = t >> 32;
+    }
+    if (carry) w.push_back((uint32_t)carry);
+  }
+  // compare with 2^e: -1, 0, 1
+  int cmp_pow2(int64_t e) const {
+    size_t n = w.size();
+    while (n && w[n - 1] == 0) --n;
+    if (n == 0) return -1;
+    const int64_t top = (int64_t)(n - 1) * 32 + (31 - __builtin_clz(w[n - 1]));
+    if (top != e) return top < e ? -1 : 1;
+    // leading bit matches: equal iff all lower bits are zero
+    if (w[n - 1] & ~(1u << (top % 32))) return 1;
+    for (size_t i = 0; i + 1 < n; ++i)
+      if (w[i]) return 1;
+    return 0;
+  }
+};
+
+int cmp_pow_vs_pow2(uint64_t x, int64_t n, int64_t e) {  // sign of x^n - 2^e
+  BigU v(1);
+  for (int64_t i = 0; i < n; ++i) v.mul((uint32_t)x);
+  return v.cmp_pow2(e);
+}
+
+bool edge_ok(uint64_t c, int64_t k, int64_t nb) {
+  // c^nb >= 2^(32k) and (c-1)^nb < 2^(32k)
+  return cmp_pow_vs_pow2(c, nb, 32 * k) >= 0 && (c == 0 || cmp_pow_vs_pow2(c - 1, nb, 32 * k) < 0);
+}
+
+void compute_edges(int64_t nb, uint32_t* e) {
+  e[0] = 0;
+  for (int64_t k = 1; k < nb; ++k) {
+    const int64_t num = 32 * k;
+    uint64_t c;
+    if (num % nb == 0) {
+      c = 1ull << (num / nb);
+    } else {
+      const long double y = std::exp2((long double)num / (long double)nb);
+      c = (uint64_t)std::ceil(y);
+      const long double frac_lo = y - std::floor(y);
+      if (frac_lo < 1e-6L || frac_lo > 1.0L - 1e-6L) {
+        // near an integer: settle exactly
+        if (!edge_ok(c, k, nb)) c = edge_ok(c + 1, k, nb) ? c + 1 : c - 1;
+      }
+    }
+    e[k] = (uint32_t)c;
+  }
+  e[nb] = 0xFFFFFFFFu;
+}
+
+struct EdgeCache {
+  std::mutex mu;
+  int64_t nb = -1;
+  hstu::EdgeArg arg;
+};
+EdgeCache g_edges;
+
+void get_edges(int64_t nb, hstu::EdgeArg* out) {
+  std::lock_guard<std::mutex> lk(g_edges.mu);
+  if (g_edges.nb != nb) {
+    std::memset(&g_edges.arg, 0, sizeof(g_edges.arg));
+    compute_edges(nb, g_edges.arg.e);
+    g_edges.nb = nb;
+  }
+  *out = g_edges.arg;
+}
+
+// Cached compute-unit count per device.
+int cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t ctr, edges, local_off, qitems, kitems, total;
+  int64_t max_qtiles, max_ktiles;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Layout layout_for(const hstu_problem_t* p, bool backward) {
+  Layout l{};
+  const int64_t segs = p->cp_size == 1 ? 1 : 2;
+  l.max_qtiles = cdiv(p->total_q, hstu::attn_q_tile_rows()) + segs * p->num_seqs;
+  l.max_ktiles = backward ? cdiv(p->total_kv, hstu::attn_bwd_key_tile()) + p->num_seqs : 0;
+  size_t off = 0;
+  l.ctr = off;
+  off = align_up(off + hstu::kCtrCount * sizeof(int));
+  l.edges = off;
+  off = align_up(off + (hstu::kMaxBuckets + 4) * sizeof(uint32_t));
+  l.local_off = off;
+  off = align_up(off + (size_t)(p->num_seqs + 1) * sizeof(int64_t));
+  l.qitems = off;
+  off = align_up(off + (size_t)l.max_qtiles * sizeof(hstu::Item));
+  l.kitems = off;
+  off = align_up(off + (size_t)l.max_ktiles * sizeof(hstu::Item));
+  l.total = off;
+  return l;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+int validate(const hstu_problem_t* p) {
+  if (!p) return fail(HSTU_EINVAL, "problem is NULL");
+  if (p->dtype != HSTU_BF16 && p->dtype != HSTU_FP32) return fail(HSTU_EINVAL, "dtype %d is not bf16 (0) or fp32 (1)", p->dtype);
+  if (p->reserved != 0) return fail(HSTU_EINVAL, "reserved field must be 0");
+  if (p->num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)p->num_seqs);
+  if (p->num_heads < 1) return fail(HSTU_EINVAL, "num_heads %lld < 1", (long long)p->num_heads);
+  if (p->d_qk != 32 && p->d_qk != 64 && p->d_qk != 128)
+    return fail(HSTU_EUNSUPPORTED, "d_qk %lld not in {32, 64, 128}", (long long)p->d_qk);
+  if (p->d_v != p->d_qk) return fail(HSTU_EUNSUPPORTED, "d_v %lld != d_qk %lld", (long long)p->d_v, (long long)p->d_qk);
+  if (p->num_buckets < 1) return fail(HSTU_EINVAL, "num_buckets %lld < 1", (long long)p->num_buckets);
+  if (p->num_buckets > hstu::kMaxBuckets)
+    return fail(HSTU_EUNSUPPORTED, "num_buckets %lld > %d", (long long)p->num_buckets, hstu::kMaxBuckets);
+  if (p->cp_size < 1) return fail(HSTU_EINVAL, "cp_size %lld < 1", (long long)p->cp_size);
+  if (p->cp_rank < 0 || p->cp_rank >= p->cp_size)
+    return fail(HSTU_EINVAL, "cp_rank %lld not in [0, %lld)", (long long)p->cp_rank, (long long)p->cp_size);
+  if (p->cp_size > 1024) return fail(HSTU_EUNSUPPORTED, "cp_size %lld > 1024", (long long)p->cp_size);
+  if (p->total_kv < 0 || p->total_q < 0) return fail(HSTU_EINVAL, "negative row count");
+  if (p->cp_size == 1 && p->total_q != p->total_kv)
+    return fail(HSTU_EINVAL, "total_q %lld != total_kv %lld with cp_size 1", (long long)p->total_q, (long long)p->total_kv);
+  if (p->total_q > p->total_kv) return fail(HSTU_EINVAL, "total_q > total_kv");
+  if (p->max_seq_len < 0) return fail(HSTU_EINVAL, "max_seq_len %lld < 0", (long long)p->max_seq_len);
+  if (p->max_seq_len > p->total_kv) return fail(HSTU_EINVAL, "max_seq_len %lld > total_kv %lld", (long long)p->max_seq_len, (long long)p->total_kv);
+  if (p->total_kv > 0 && p->max_seq_len == 0) return fail(HSTU_EINVAL, "max_seq_len is 0 but total_kv > 0");
+  if (p->total_kv >= (1ll << 31)) return fail(HSTU_EUNSUPPORTED, "total_kv %lld >= 2^31", (long long)p->total_kv);
+  if (p->num_seqs >= (1ll << 30)) return fail(HSTU_EUNSUPPORTED, "num_seqs too large");
+  if (p->num_heads * p->d_qk >= (1ll << 24)) return fail(HSTU_EUNSUPPORTED, "num_heads * d too large");
+  const Layout l = layout_for(p, true);
+  if ((l.max_qtiles + l.max_ktiles) * p->num_heads >= (1ll << 31)) return fail(HSTU_EUNSUPPORTED, "too many work items");
+  return HSTU_OK;
+}
+
+#define CHECK_PTR(ptr, name)                                                               \
+  do {                                                                                     \
+    if (!(ptr)) return fail(HSTU_EINVAL, "%s is NULL", name);                              \
+    if (!aligned16(ptr)) return fail(HSTU_EINVAL, "%s is not 16-byte aligned", name);      \
+  } while (0)
+
+#define CHECK_PTR8(ptr, name)                                                              \
+  do {                                                                                     \
+    if (!(ptr)) return fail(HSTU_EINVAL, "%s is NULL", name);                              \
+    if (((uintptr_t)(ptr) & 7) != 0) return fail(HSTU_EINVAL, "%s is not 8-byte aligned", name); \
+  } while (0)
+
+int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, char* ws, float* dw,
+             hipStream_t s, bool backward) {
+  hstu::SchedParams sp{};
+  sp.offsets = offsets;
+  sp.B = p->num_seqs;
+  sp.cp_size = (int)p->cp_size;
+  sp.cp_rank = (int)p->cp_rank;
+  sp.q_tile = hstu::attn_q_tile_rows();
+  sp.q_cost_tile = hstu::attn_k_tile_keys();
+  sp.k_tile = backward ? hstu::attn_bwd_key_tile() : 0;
+  sp.k_cost_tile = hstu::attn_bwd_q_step();
+  sp.hist_size = hstu::kSchedHist;
+  sp.local_off = reinterpret_cast<int64_t*>(ws + l.local_off);
+  sp.qitems = reinterpret_cast<hstu::Item*>(ws + l.qitems);
+  sp.kitems = reinterpret_cast<hstu::Item*>(ws + l.kitems);
+  sp.ctr = reinterpret_cast<int*>(ws + l.ctr);
+  sp.edges_out = reinterpret_cast<uint32_t*>(ws + l.edges);
+  sp.dw = dw;
+  sp.dw_count = (int)(p->num_heads * p->num_buckets);
+  sp.NB = (int)p->num_buckets;
+  hstu::EdgeArg edges;
+  get_edges(p->num_buckets, &edges);
+  const hipError_t e = hstu::launch_sched(sp, edges, s);
+  if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+  return HSTU_OK;
+}
+
+hstu::AttnParams attn_params(const hstu_problem_t* p, const Layout& l, char* ws) {
+  hstu::AttnParams a{};
+  a.local_off = reinterpret_cast<const int64_t*>(ws + l.local_off);
+  a.qitems = reinterpret_cast<const hstu::Item*>(ws + l.qitems);
+  a.kitems = reinterpret_cast<const hstu::Item*>(ws + l.kitems);
+  a.ctr = reinterpret_cast<int*>(ws + l.ctr);
+  a.edges = reinterpret_cast<const uint32_t*>(ws + l.edges);
+  a.H = (int)p->num_heads;
+  a.NB = (int)p->num_buckets;
+  a.cp_size = (int)p->cp_size;
+  a.cp_rank = (int)p->cp_rank;
+  a.alpha = (float)(1.0 / std::sqrt((double)p->d_qk));
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hstu_version(void) { return 100; }
+
+const char* hstu_last_error(void) { return g_last_error.c_str(); }
+
+int hstu_bucket_edges(int64_t num_buckets, uint32_t* edges_out) {
+  if (!edges_out) return fail(HSTU_EINVAL, "edges_out is NULL");
+  if (num_buckets < 1) return fail(HSTU_EINVAL, "num_buckets %lld < 1", (long long)num_buckets);
+  if (num_buckets > hstu::kMaxBuckets)
+    return fail(HSTU_EUNSUPPORTED, "num_buckets %lld > %d", (long long)num_buckets, hstu::kMaxBuckets);
+  hstu::EdgeArg e;
+  get_edges(num_buckets, &e);
+  std::memcpy(edges_out, e.e, sizeof(uint32_t) * (num_buckets + 1));
+  return HSTU_OK;
+}
+
+size_t hstu_workspace_size(const hstu_problem_t* p, int backward) {
+  if (validate(p) != HSTU_OK) return 0;
+  return layout_for(p, backward != 0).total;
+}
+
+int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+                         const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc != HSTU_OK) return rc;
+  if (p->total_q == 0 || p->num_seqs == 0) return HSTU_OK;
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(out, "out");
+  CHECK_PTR8(offsets, "offsets");
+  CHECK_PTR8(timestamps, "timestamps");
+  if (!ts_weights) return fail(HSTU_EINVAL, "ts_weights is NULL");
+  const Layout l = layout_for(p, false);
+  if (!workspace) return fail(HSTU_EWORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(HSTU_EINVAL, "workspace is not 16-byte aligned");
+  if (workspace_bytes < l.total)
+    return fail(HSTU_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  rc = schedule(p, l, offsets, ws, nullptr, s, false);
+  if (rc != HSTU_OK) return rc;
+  hstu::AttnParams a = attn_params(p, l, ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.offsets = offsets;
+  a.ts = timestamps;
+  a.w = ts_weights;
+  a.out = out;
+  const int max_items = (int)(l.max_qtiles * p->num_heads);
+  const hipError_t e = hstu::launch_attn(a, p->dtype == HSTU_BF16, (int)p->d_qk, 0, max_items, cu_count(), s);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return HSTU_OK;
+}
+
+int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* q, const void* k, const void* v,
+                         const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* dq,
+                         void* dk, void* dv, float* d_ts_weights, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int rc = validate(p);
+  if (rc != HSTU_OK) return rc;
+  if (p->num_seqs == 0 || p->total_kv == 0) {
+    // Nothing to attend: gradients of an empty problem.  d_ts_weights still
+    // has to be written (zeros); use the scheduler with no lists.
+    if (!d_ts_weights) return fail(HSTU_EINVAL, "d_ts_weights is NULL");
+    const Layout l = layout_for(p, true);
+    if (!workspace || workspace_bytes < l.total) return fail(HSTU_EWORKSPACE, "workspace too small");
+    return schedule(p, l, offsets, static_cast<char*>(workspace), d_ts_weights, static_cast<hipStream_t>(stream),
+                    true);
+  }
+  CHECK_PTR(dout, "dout");
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(dq, "dq");
+  CHECK_PTR(dk, "dk");
+  CHECK_PTR(dv, "dv");
+  CHECK_PTR8(offsets, "offsets");
+  CHECK_PTR8(timestamps, "timestamps");
+  if (!ts_weights) return fail(HSTU_EINVAL, "ts_weights is NULL");
+  if (!d_ts_weights) return fail(HSTU_EINVAL, "d_ts_weights is NULL");
+  if (((uintptr_t)d_ts_weights & 3) != 0) return fail(HSTU_EINVAL, "d_ts_weights is not 4-byte aligned");
+  const Layout l = layout_for(p, true);
+  if (!workspace) return fail(HSTU_EWORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(HSTU_EINVAL, "workspace is not 16-byte aligned");
+  if (workspace_bytes < l.total)
+    return fail(HSTU_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  rc = schedule(p, l, offsets, ws, d_ts_weights, s, true);
+  if (rc != HSTU_OK) return rc;
+  hstu::AttnParams a = attn_params(p, l, ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.offsets = offsets;
+  a.ts = timestamps;
+  a.w = ts_weights;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw = d_ts_weights;
+  const bool bf16 = p->dtype == HSTU_BF16;
+  hipError_t e = hstu::launch_attn(a, bf16, (int)p->d_qk, 1, (int)(l.max_ktiles * p->num_heads), cu_count(), s);
+  if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  if (p->total_q > 0) {
+    e = hstu::launch_attn(a, bf16, (int)p->d_qk, 2, (int)(l.max_qtiles * p->num_heads), cu_count(), s);
+    if (e != hipSuccess) return hip_fail(e, "dQ launch");
+  }
+  return HSTU_OK;
+}
+
+int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t num_seqs,
+                    int64_t total_rows, int64_t max_seq_len, int64_t cp_size, int inverse, int64_t* out_offsets,
+                    void* stream) {
+  if (num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)num_seqs);
+  if (total_rows < 0) return fail(HSTU_EINVAL, "total_rows %lld < 0", (long long)total_rows);
+  if (row_bytes < 1) return fail(HSTU_EINVAL, "row_bytes %lld < 1", (long long)row_bytes);
+  if (cp_size < 1) return fail(HSTU_EINVAL, "cp_size %lld < 1", (long long)cp_size);
+  if (cp_size > 1024) return fail(HSTU_EUNSUPPORTED, "cp_size %lld > 1024", (long long)cp_size);
+  if (max_seq_len < 0 || max_seq_len > total_rows)
+    return fail(HSTU_EINVAL, "max_seq_len %lld not in [0, total_rows]", (long long)max_seq_len);
+  if (total_rows > 0 && max_seq_len == 0) return fail(HSTU_EINVAL, "max_seq_len is 0 but total_rows > 0");
+  if (num_seqs == 0) return HSTU_OK;
+  if (cp_size * num_seqs >= (1ll << 31)) return fail(HSTU_EUNSUPPORTED, "cp_size * num_seqs too large");
+  if (!in || !out) return fail(HSTU_EINVAL, "in/out is NULL");
+  CHECK_PTR8(offsets, "offsets");
+  if (out_offsets && ((uintptr_t)out_offsets & 7)) return fail(HSTU_EINVAL, "out_offsets is not 8-byte aligned");
+  const char* ib = static_cast<const char*>(in);
+  const char* ob = static_cast<const char*>(out);
+  const int64_t bytes = total_rows * row_bytes;
+  if (total_rows > 0 && ib < ob + bytes && ob < ib + bytes) return fail(HSTU_EINVAL, "in and out overlap");
+  const int64_t nch = 2 * cp_size;
+  const int64_t max_pair_bytes = 2 * ((max_seq_len + nch - 1) / nch) * row_bytes;
+  if (max_pair_bytes / (64 * 1024) >= 65535) return fail(HSTU_EUNSUPPORTED, "sequence too long for the reorder grid");
+  const hipError_t e = hstu::launch_reorder(in, out, row_bytes, offsets, num_seqs, total_rows, max_seq_len,
+                                            (int)cp_size, inverse != 0, out_offsets, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reorder launch");
+  return HSTU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Parameters and launchers of the attention kernels (internal interface
+// between the host library and the device code).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace hstu {
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const int64_t* offsets;    // [B+1] global
+  const int64_t* local_off;  // [B+1] rank-local query offsets
+  const int64_t* ts;         // [T]
+  const void* w;             // [H, NB]
+  void* out;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw;                 // [H, NB] fp32, zeroed by the scheduler
+  const Item* qitems;
+  const Item* kitems;
+  int* ctr;
+  const uint32_t* edges;     // [NB+1]
+  int H;
+  int NB;
+  int cp_size;
+  int cp_rank;
+  float alpha;
+};
+
+// which: 0 forward, 1 dK/dV/dW pass, 2 dQ pass.  max_items bounds the number
+// of (tile, head) work items (the grid never exceeds it).
+hipError_t launch_attn(const AttnParams& p, bool bf16, int d, int which, int max_items, int cus, hipStream_t s);
+
+int attn_q_tile_rows();   // query rows per forward / dQ item
+int attn_k_tile_keys();   // keys per tile in the forward / dQ loops
+int attn_bwd_key_tile();  // keys per dK/dV item
+int attn_bwd_q_step();    // query rows per step of the dK/dV loop
+
+// Scheduler: builds the descending-cost tile lists, the rank-local offsets,
+// the edge table copy and zero-fills dw.
+struct SchedParams {
+  const int64_t* offsets;
+  int64_t B;
+  int cp_size;
+  int cp_rank;
+  int q_tile;        // rows per query tile (0 = no query list)
+  int q_cost_tile;   // key-tile size used in a query tile's cost
+  int k_tile;        // keys per key tile (0 = no key list)
+  int k_cost_tile;   // query rows per step used in a key tile's cost
+  int hist_size;     // cost histogram bins (costs are clamped to hist_size-1)
+  int64_t* local_off;
+  Item* qitems;
+  Item* kitems;
+  int* ctr;
+  uint32_t* edges_out;
+  float* dw;         // zero-filled when non-null
+  int dw_count;
+  int NB;
+};
+
+struct EdgeArg {
+  uint32_t e[kMaxBuckets + 1];
+};
+
+hipError_t launch_sched(const SchedParams& p, const EdgeArg& edges, hipStream_t s);
+
+constexpr int kSchedHist = 4096;
+
+hipError_t launch_reorder(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t B,
+                          int64_t total_rows, int64_t max_seq_len, int cp_size, bool inverse,
+                          int64_t* out_offsets, hipStream_t s);
+
+}  // namespace hstu

@@ -1,0 +1,127 @@
+// Device-side building blocks shared by the gfx950 kernels: MFMA operand
+// traits, the exact timestamp bucket, SiLU, and the work-item format.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxBuckets = 512;
+
+// Work item: one tile of rows of one sequence.  For query tiles `row0` is the
+// row in q/out (rank-local when context-parallel), `pos0` the position inside
+// the sequence of the first row, `n` the row count.  For key tiles `row0` is
+// the global row in k/v.
+struct Item {
+  int32_t b;
+  int32_t row0;
+  int32_t pos0;
+  int32_t n;
+};
+
+// Counters written by the scheduler, read by the attention kernels.
+enum Ctr : int {
+  kCtrQTiles = 0,   // number of query tiles in the list
+  kCtrQNext = 1,    // work counter popped by the forward / dQ kernel
+  kCtrKTiles = 2,   // number of key tiles
+  kCtrKNext = 3,    // work counter popped by the dK/dV kernel
+  kCtrQNext2 = 4,   // second query-tile counter (backward dQ pass)
+  kCtrCount = 64
+};
+
+// ---------------------------------------------------------------------------
+// MFMA operand traits.  Both element types use the 32x32 output block, whose
+// accumulator layout is: lane l holds column (l % 32), and its 16 values hold
+// rows 8*(i/4) + 4*(l/32) + (i%4), i = 0..15.  An A operand lane (r, g) =
+// (l % 32, l / 32) supplies row r and the K slice [g*EPL, (g+1)*EPL) of one
+// instruction; a B operand lane supplies column r and the same K slice.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<__bf16> {
+  using operand = bf16x8;
+  static constexpr int kK = 16;   // contraction length per instruction
+  static constexpr int kEpl = 8;  // operand elements per lane
+  __device__ static inline f32x16 mma(operand a, operand b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline operand load(const __bf16* p) {
+    return __builtin_bit_cast(operand, *reinterpret_cast<const u32x4*>(p));
+  }
+};
+
+template <> struct Mma<float> {
+  using operand = float;
+  static constexpr int kK = 2;
+  static constexpr int kEpl = 1;
+  __device__ static inline f32x16 mma(operand a, operand b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline operand load(const float* p) { return *p; }
+};
+
+// Row (within its 32-row block) of accumulator value i held by lane group g.
+__device__ __forceinline__ int acc_row(int i, int g) { return ((i >> 2) << 3) + (g << 2) + (i & 3); }
+
+// ---------------------------------------------------------------------------
+// Transposed bf16 tiles.  A product that contracts over rows of a row-major
+// tile (P·V over keys, Gᵀ·Q over queries, ...) needs, per lane, 8 values of one
+// column taken from 8 different rows.  Such tiles are stored transposed in LDS
+// ([col][row]) with the rows of each 32-row block permuted so that the 8 rows
+// one lane needs are adjacent: row ρ of a block sits at slot
+//   16*u + 8*g + j  with  i = 4*(ρ/8) + ρ%4,  u = i/8,  j = i%8,  g = (ρ/4)%2,
+// which is exactly the order in which accumulator values i of lane group g
+// enumerate rows (acc_row above).  Four consecutive rows 4m..4m+3 land in four
+// consecutive slots, so the tile can be written with 8-byte stores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tslot(int rho) {
+  const int blk = rho >> 5, r = rho & 31;
+  const int i = ((r >> 3) << 2) + (r & 3);
+  return (blk << 5) + ((i >> 3) << 4) + (((r >> 2) & 1) << 3) + (i & 7);
+}
+
+// ---------------------------------------------------------------------------
+// Exact timestamp bucket: #{k in [1, NB) : |delta| >= E_k}.  A float estimate
+// floor(NB/32 * log2|delta|) is within one of the exact count (the count equals
+// floor of the real-valued NB*log2|delta|/32 for integer |delta|), and one
+// comparison against each neighbouring integer edge fixes it.  `edges` is the
+// LDS copy of E[0..NB] (E[0] = 0, E[NB] = sentinel).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int bucket_of(int64_t delta, int nb, float nb_over_32,
+                                         const uint32_t* __restrict__ edges) {
+  const uint64_t mag = delta < 0 ? (uint64_t)(-delta) : (uint64_t)delta;
+  if (mag >> 32) return nb - 1;
+  const uint32_t x = (uint32_t)mag;
+  const float f = fmaxf((float)x, 1.0f);
+  int k = (int)floorf(__log2f(f) * nb_over_32);
+  k = min(max(k, 0), nb - 1);
+  if (x < edges[k]) {
+    --k;
+  } else if (k + 1 < nb && x >= edges[k + 1]) {
+    ++k;
+  }
+  return k;
+}
+
+// SiLU and its derivative, fp32.  sigmoid via exp2 and a hardware reciprocal.
+__device__ __forceinline__ float fast_sigmoid(float s) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
+
+}  // namespace hstu

@@ -1,0 +1,188 @@
+// Jagged tile scheduler (one workgroup).  From the int64 offsets it builds
+//   - the rank-local query offsets (context-parallel share: chunks r and
+//     2C-1-r of every sequence; Scaling Generative Recommendations with Context
+//     Parallelism on HSTU, §2.3, load-balanced mini-chunks),
+//   - the list of query tiles and the list of key tiles, each sorted by
+//     descending cost with a counting sort, so that persistent workgroups that
+//     pop items in order take the longest work first,
+// and resets the work counters.  Tiles lying entirely above the causal
+// diagonal are never emitted: a query tile's key range stops at its last row.
+#include "attn.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int kSchedThreads = 1024;
+
+struct SegInfo {
+  int n;
+  int pos0[2];
+  int len[2];
+  int64_t lrow0[2];
+};
+
+__device__ __forceinline__ int chunk_lo(int64_t L, int k, int nch) { return (int)((int64_t)k * L / nch); }
+
+__device__ __forceinline__ SegInfo seq_segments(const SchedParams& p, int b, int64_t local0) {
+  const int64_t o0 = p.offsets[b];
+  const int L = (int)(p.offsets[b + 1] - o0);
+  SegInfo s;
+  if (p.cp_size == 1) {
+    s.n = 1;
+    s.pos0[0] = 0;
+    s.len[0] = L;
+    s.lrow0[0] = o0;
+    return s;
+  }
+  const int nch = 2 * p.cp_size;
+  const int c0 = p.cp_rank, c1 = nch - 1 - p.cp_rank;
+  s.n = 2;
+  s.pos0[0] = chunk_lo(L, c0, nch);
+  s.len[0] = chunk_lo(L, c0 + 1, nch) - s.pos0[0];
+  s.pos0[1] = chunk_lo(L, c1, nch);
+  s.len[1] = chunk_lo(L, c1 + 1, nch) - s.pos0[1];
+  s.lrow0[0] = local0;
+  s.lrow0[1] = local0 + s.len[0];
+  return s;
+}
+
+__device__ __forceinline__ int local_len(const SchedParams& p, int b) {
+  const int64_t L = p.offsets[b + 1] - p.offsets[b];
+  if (p.cp_size == 1) return (int)L;
+  const int nch = 2 * p.cp_size;
+  const int c0 = p.cp_rank, c1 = nch - 1 - p.cp_rank;
+  return (chunk_lo(L, c0 + 1, nch) - chunk_lo(L, c0, nch)) + (chunk_lo(L, c1 + 1, nch) - chunk_lo(L, c1, nch));
+}
+
+// Exclusive scan of one value per thread across the block; returns the
+// thread's prefix and writes the block total to *total.
+__device__ int64_t block_scan(int64_t v, int64_t* buf, int64_t* total) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    const int64_t add = t >= off ? buf[t - off] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  const int64_t incl = buf[t];
+  *total = buf[kSchedThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__device__ __forceinline__ int clampc(int64_t c, int hs) { return (int)(c < hs - 1 ? c : hs - 1); }
+
+}  // namespace
+
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams p, const EdgeArg edges) {
+  __shared__ int histq[kSchedHist];
+  __shared__ int histk[kSchedHist];
+  __shared__ int64_t scan[kSchedThreads];
+  const int t = threadIdx.x;
+  const int hs = p.hist_size;
+
+  for (int i = t; i <= p.NB; i += kSchedThreads) p.edges_out[i] = edges.e[i];
+  if (p.dw)
+    for (int i = t; i < p.dw_count; i += kSchedThreads) p.dw[i] = 0.0f;
+  for (int i = t; i < hs; i += kSchedThreads) {
+    histq[i] = 0;
+    histk[i] = 0;
+  }
+
+  // Rank-local offsets.
+  int64_t carry = 0;
+  for (int64_t base = 0; base < p.B; base += kSchedThreads) {
+    const int64_t b = base + t;
+    const int64_t len = b < p.B ? local_len(p, (int)b) : 0;
+    int64_t tot;
+    const int64_t pre = block_scan(len, scan, &tot);
+    if (b < p.B) p.local_off[b] = carry + pre;
+    carry += tot;
+  }
+  if (t == 0) p.local_off[p.B] = carry;
+  __syncthreads();
+
+  // Pass 1: cost histograms.
+  for (int64_t b = t; b < p.B; b += kSchedThreads) {
+    const SegInfo s = seq_segments(p, (int)b, p.local_off[b]);
+    if (p.q_tile > 0) {
+      for (int sg = 0; sg < s.n; ++sg)
+        for (int r = 0; r < s.len[sg]; r += p.q_tile) {
+          const int end = s.pos0[sg] + min(p.q_tile, s.len[sg] - r) + r;
+          atomicAdd(&histq[clampc((end + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
+        }
+    }
+    if (p.k_tile > 0) {
+      const int L = (int)(p.offsets[b + 1] - p.offsets[b]);
+      for (int k0 = 0; k0 < L; k0 += p.k_tile) {
+        int64_t cost = 0;
+        for (int sg = 0; sg < s.n; ++sg) {
+          const int from = max(s.pos0[sg], k0), to = s.pos0[sg] + s.len[sg];
+          if (to > from) cost += (to - from + p.k_cost_tile - 1) / p.k_cost_tile;
+        }
+        atomicAdd(&histk[clampc(cost, hs)], 1);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Descending exclusive scan: start[c] = number of tiles with cost > c.
+  for (int which = 0; which < 2; ++which) {
+    int* hist = which == 0 ? histq : histk;
+    int64_t carry2 = 0;
+    for (int base = 0; base < hs; base += kSchedThreads) {
+      const int c = hs - 1 - (base + t);
+      const int64_t v = c >= 0 ? hist[c] : 0;
+      int64_t tot;
+      const int64_t pre = block_scan(v, scan, &tot);
+      __syncthreads();
+      if (c >= 0) hist[c] = (int)(carry2 + pre);
+      carry2 += tot;
+      __syncthreads();
+    }
+    if (t == 0) p.ctr[which == 0 ? kCtrQTiles : kCtrKTiles] = (int)carry2;
+  }
+  __syncthreads();
+
+  // Pass 2: scatter.
+  for (int64_t b = t; b < p.B; b += kSchedThreads) {
+    const SegInfo s = seq_segments(p, (int)b, p.local_off[b]);
+    if (p.q_tile > 0) {
+      for (int sg = 0; sg < s.n; ++sg)
+        for (int r = 0; r < s.len[sg]; r += p.q_tile) {
+          const int n = min(p.q_tile, s.len[sg] - r);
+          const int pos0 = s.pos0[sg] + r;
+          const int slot = atomicAdd(&histq[clampc((pos0 + n + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
+          p.qitems[slot] = Item{(int)b, (int)(s.lrow0[sg] + r), pos0, n};
+        }
+    }
+    if (p.k_tile > 0) {
+      const int64_t o0 = p.offsets[b];
+      const int L = (int)(p.offsets[b + 1] - o0);
+      for (int k0 = 0; k0 < L; k0 += p.k_tile) {
+        int64_t cost = 0;
+        for (int sg = 0; sg < s.n; ++sg) {
+          const int from = max(s.pos0[sg], k0), to = s.pos0[sg] + s.len[sg];
+          if (to > from) cost += (to - from + p.k_cost_tile - 1) / p.k_cost_tile;
+        }
+        const int slot = atomicAdd(&histk[clampc(cost, hs)], 1);
+        p.kitems[slot] = Item{(int)b, (int)(o0 + k0), k0, min(p.k_tile, L - k0)};
+      }
+    }
+  }
+  if (t == 0) {
+    p.ctr[kCtrQNext] = 0;
+    p.ctr[kCtrKNext] = 0;
+    p.ctr[kCtrQNext2] = 0;
+  }
+}
+
+hipError_t launch_sched(const SchedParams& p, const EdgeArg& edges, hipStream_t s) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, s, p, edges);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -6,7 +6,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 from .hstu_oracle import (  # noqa: F401
     attn_bwd,
+    attn_bwd_kv_rows,
+    attn_bwd_q_rows,
     attn_fwd,
+    attn_fwd_rows,
     bucket_edges,
     bucketize,
     causal_pairs,

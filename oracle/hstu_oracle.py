@@ -337,3 +337,69 @@ def cp_rank_pairs(lengths, cp_size: int, rank: int) -> int:
             c0, c1 = chunk_bounds(int(n), cp_size, c)
             total += sum(p + 1 for p in range(c0, c1))
     return total
+
+
+# --------------------------------------------------------------------------
+# Per-row forms, for checking sampled outputs of large problems.  Same
+# arithmetic as above, restricted to the requested rows.
+# --------------------------------------------------------------------------
+
+def _row_seq(offsets, row):
+    b = int(np.searchsorted(np.asarray(offsets), row, side="right")) - 1
+    return b, int(offsets[b]), int(offsets[b + 1])
+
+
+def attn_fwd_rows(q, k, v, offsets, ts, w, num_buckets, rows):
+    """O[rows] of attn_fwd (all heads): [len(rows), H, d_v]."""
+    q = np.asarray(q)
+    H, dqk = q.shape[1], q.shape[2]
+    alpha = 1.0 / math.sqrt(dqk)
+    out = np.zeros((len(rows), H, v.shape[2]), dtype=np.float64)
+    for n, i in enumerate(rows):
+        _, lo, _ = _row_seq(offsets, i)
+        keys = slice(lo, i + 1)
+        for h in range(H):
+            s, _ = _seq_scores(np.asarray(q[i:i + 1, h], np.float64), np.asarray(k[keys, h], np.float64),
+                               ts[i:i + 1], ts[keys], np.asarray(w[h], np.float64), num_buckets, alpha)
+            out[n, h] = silu(s)[0] @ np.asarray(v[keys, h], np.float64)
+    return out
+
+
+def attn_bwd_q_rows(dout, q, k, v, offsets, ts, w, num_buckets, rows):
+    """dQ[rows] of attn_bwd: [len(rows), H, d_qk]."""
+    H, dqk = q.shape[1], q.shape[2]
+    alpha = 1.0 / math.sqrt(dqk)
+    dq = np.zeros((len(rows), H, dqk), dtype=np.float64)
+    for n, i in enumerate(rows):
+        _, lo, _ = _row_seq(offsets, i)
+        keys = slice(lo, i + 1)
+        for h in range(H):
+            kk = np.asarray(k[keys, h], np.float64)
+            s, _ = _seq_scores(np.asarray(q[i:i + 1, h], np.float64), kk, ts[i:i + 1], ts[keys],
+                               np.asarray(w[h], np.float64), num_buckets, alpha)
+            dp = np.asarray(v[keys, h], np.float64) @ np.asarray(dout[i, h], np.float64)
+            g = alpha * dp * silu_grad(s[0])
+            dq[n, h] = g @ kk
+    return dq
+
+
+def attn_bwd_kv_rows(dout, q, k, v, offsets, ts, w, num_buckets, rows):
+    """(dK[rows], dV[rows]) of attn_bwd: each [len(rows), H, d]."""
+    H, dqk = q.shape[1], q.shape[2]
+    alpha = 1.0 / math.sqrt(dqk)
+    dk = np.zeros((len(rows), H, dqk), dtype=np.float64)
+    dv = np.zeros((len(rows), H, v.shape[2]), dtype=np.float64)
+    for n, j in enumerate(rows):
+        _, _, hi = _row_seq(offsets, j)
+        qs = slice(j, hi)
+        for h in range(H):
+            qq = np.asarray(q[qs, h], np.float64)
+            s, _ = _seq_scores(qq, np.asarray(k[j:j + 1, h], np.float64), ts[qs], ts[j:j + 1],
+                               np.asarray(w[h], np.float64), num_buckets, alpha)
+            s = s[:, 0]
+            dd = np.asarray(dout[qs, h], np.float64)
+            dp = dd @ np.asarray(v[j, h], np.float64)
+            g = alpha * dp * silu_grad(s)
+            dv[n, h] = silu(s) @ dd
+            dk[n, h] = g @ qq
+    return dk, dv

@@ -1,0 +1,124 @@
+"""The C-ABI library: it loads, exports what include/hstu.h declares, its host
+logic (edge table, validation, workspace sizing) is right.  CPU only: no call
+here reaches a kernel launch (validation rejects every argument set first)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import jagged_hstu_attention_amd as hstu
+from jagged_hstu_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_version():
+    assert hstu.version() == 100
+
+
+@pytest.mark.parametrize("nb", [1, 2, 7, 32, 100, 128, 256, 512])
+def test_library_edge_table_equals_oracle(nb):
+    got = hstu.bucket_edges(nb)
+    want = [0] + oracle.bucket_edges(nb) + [0xFFFFFFFF]
+    assert got == want
+
+
+def test_edge_table_rejects_bad_sizes():
+    with pytest.raises(hstu.HstuError) as e:
+        hstu.bucket_edges(0)
+    assert e.value.status == 1
+    with pytest.raises(hstu.HstuError) as e:
+        hstu.bucket_edges(513)
+    assert e.value.status == 2
+
+
+def make_problem(**kw):
+    p = hstu.Problem()
+    base = dict(dtype=0, reserved=0, num_seqs=4, num_heads=2, d_qk=64, d_v=64, num_buckets=128,
+                max_seq_len=100, total_kv=300, total_q=300, cp_size=1, cp_rank=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_workspace_size_valid_and_monotone():
+    small = hstu.workspace_size(make_problem(), False)
+    bwd = hstu.workspace_size(make_problem(), True)
+    big = hstu.workspace_size(make_problem(total_kv=30000, total_q=30000, max_seq_len=10000), False)
+    assert 0 < small <= bwd
+    assert big > small
+    assert small % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), 1), (dict(reserved=1), 1), (dict(num_seqs=-1), 1), (dict(num_heads=0), 1),
+    (dict(d_qk=48, d_v=48), 2), (dict(d_v=32), 2), (dict(num_buckets=0), 1), (dict(num_buckets=1000), 2),
+    (dict(cp_size=0), 1), (dict(cp_size=2, cp_rank=2), 1), (dict(cp_rank=-1), 1),
+    (dict(total_q=10), 1), (dict(max_seq_len=400), 1), (dict(max_seq_len=0), 1),
+    (dict(cp_size=2, cp_rank=0, total_q=400), 1),
+])
+def test_validation_errors(kw, status):
+    p = make_problem(**kw)
+    lib = _lib.load()
+    assert lib.hstu_workspace_size(ctypes.byref(p), 0) == 0
+    dummy = ctypes.c_void_p(16)
+    rc = lib.hstu_jagged_attn_fwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                  1 << 30, None)
+    assert rc == status
+    assert lib.hstu_last_error()
+
+
+def test_null_and_misaligned_pointers_rejected():
+    p = make_problem()
+    lib = _lib.load()
+    good = ctypes.c_void_p(1 << 20)
+    bad = ctypes.c_void_p((1 << 20) + 2)
+    ws = hstu.workspace_size(p, False)
+    args = [good] * 8
+    rc = lib.hstu_jagged_attn_fwd(ctypes.byref(p), None, *args[1:7], good, ws, None)
+    assert rc == 1 and b"q is NULL" in lib.hstu_last_error()
+    rc = lib.hstu_jagged_attn_fwd(ctypes.byref(p), bad, *args[1:7], good, ws, None)
+    assert rc == 1 and b"aligned" in lib.hstu_last_error()
+    # workspace too small
+    rc = lib.hstu_jagged_attn_fwd(ctypes.byref(p), *args[:7], good, ws - 1, None)
+    assert rc == 3
+    rc = lib.hstu_jagged_attn_fwd(ctypes.byref(p), *args[:7], None, ws, None)
+    assert rc == 3
+    # backward: d_ts_weights NULL
+    wsb = hstu.workspace_size(p, True)
+    rc = lib.hstu_jagged_attn_bwd(ctypes.byref(p), *([good] * 10), None, good, wsb, None)
+    assert rc == 1 and b"d_ts_weights" in lib.hstu_last_error()
+
+
+def test_reorder_validation():
+    lib = _lib.load()
+    g = ctypes.c_void_p(1 << 20)
+    o = ctypes.c_void_p(1 << 21)
+    assert lib.hstu_cp_reorder(g, o, 0, g, 2, 10, 5, 2, 0, None, None) == 1    # row_bytes
+    assert lib.hstu_cp_reorder(g, o, 8, g, 2, 10, 5, 0, 0, None, None) == 1    # cp_size
+    assert lib.hstu_cp_reorder(g, o, 8, g, 2, 10, 11, 2, 0, None, None) == 1   # max_seq_len > rows
+    assert lib.hstu_cp_reorder(g, g, 8, g, 2, 10, 5, 2, 0, None, None) == 1    # overlap
+    assert lib.hstu_cp_reorder(None, o, 8, g, 2, 10, 5, 2, 0, None, None) == 1
+    # nothing to do: no launch, OK
+    assert lib.hstu_cp_reorder(g, o, 8, g, 0, 0, 0, 2, 0, None, None) == 0

@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from hstu_testlib import assert_close, errors, sample_rows, to_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def hstu():
+    import jagged_hstu_attention_amd as m
+    return m
+
+
+def run_fwd(wl, d):
+    return hstu().jagged_attn_fwd(d["q"], d["k"], d["v"], d["offsets"], d["ts"], d["w"], wl.max_seq_len)
+
+
+def run_bwd(wl, d):
+    return hstu().jagged_attn_bwd(d["dout"], d["q"], d["k"], d["v"], d["offsets"], d["ts"], d["w"], wl.max_seq_len)
+
+
+def oracle_fwd(wl):
+    return oracle.attn_fwd(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
+
+
+def oracle_bwd(wl):
+    return oracle.attn_bwd(wl.dout.f64, wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
+
+
+def test_native_library_is_loaded():
+    import jagged_hstu_attention_amd as m
+    lib = m._lib.load()
+    assert lib.hstu_version() == 100
+
+
+# --------------------------------------------------------------------------
+# The tiny fp32 workload: literal 1e-5 tolerances.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [1001, 1101])
+def test_tiny_fp32_forward(seed):
+    wl = synth.config("tiny_fp32", seed=seed)
+    d = upload(wl)
+    out = run_fwd(wl, d)
+    assert_close(to_f64(out), oracle_fwd(wl), "fp32", "out", literal=True)
+
+
+@pytest.mark.parametrize("seed", [1001, 1101])
+def test_tiny_fp32_backward(seed):
+    wl = synth.config("tiny_fp32", seed=seed)
+    d = upload(wl)
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    assert_close(to_f64(dq), rq, "fp32", "dq", literal=True)
+    assert_close(to_f64(dk), rk, "fp32", "dk", literal=True)
+    assert_close(to_f64(dv), rv, "fp32", "dv", literal=True)
+    assert_close(to_f64(dw), rw, "fp32", "dw", literal=True)
+
+
+# --------------------------------------------------------------------------
+# Ragged shapes spanning several tiles, all head widths, both dtypes.
+# --------------------------------------------------------------------------
+
+RAGGED = [1, 63, 64, 65, 0, 127, 128, 129, 300, 2]
+
+
+@pytest.mark.parametrize("dtype,dim,nb", [("bf16", 128, 128), ("bf16", 64, 256), ("bf16", 32, 7),
+                                          ("fp32", 128, 128), ("fp32", 64, 256), ("fp32", 32, 100)])
+def test_ragged_forward_backward(dtype, dim, nb):
+    wl = synth.custom(RAGGED, num_heads=3, d_qk=dim, d_v=dim, num_buckets=nb, dtype=dtype, gap_mean=3600.0,
+                      seed=dim + nb, w_std=0.5)
+    d = upload(wl)
+    out = run_fwd(wl, d)
+    assert_close(to_f64(out), oracle_fwd(wl), dtype, "out")
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    for name, got, ref in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(to_f64(got), ref, dtype, name)
+
+
+def test_forward_is_deterministic():
+    wl = synth.custom([700, 33, 1000], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=3)
+    d = upload(wl)
+    a = run_fwd(wl, d).clone()
+    b = run_fwd(wl, d)
+    import torch
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# Bias- and mask-sensitive cases (the bf16 tolerance alone would not pin the
+# bias: its effect on O is small for N(0, 0.02) weights).
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nb", [128, 256])
+def test_q_zero_constant_bias_cumsum_bf16(nb):
+    import torch
+    wl = synth.custom([200, 77, 513], num_heads=2, d_qk=128, d_v=128, num_buckets=nb, dtype="bf16", seed=11)
+    d = upload(wl)
+    d["q"] = torch.zeros_like(d["q"])
+    c = 1.5
+    d["w"] = torch.full_like(d["w"], c)
+    out = to_f64(run_fwd(wl, d))
+    alpha = 1 / math.sqrt(128)
+    sc = alpha * c / (1 + math.exp(-alpha * c))
+    for b in range(3):
+        lo, hi = wl.offsets[b], wl.offsets[b + 1]
+        ref = sc * np.cumsum(wl.v.f64[lo:hi], axis=0)
+        assert_close(out[lo:hi], ref, "bf16", f"seq{b}")
+
+
+@pytest.mark.parametrize("nb,gap", [(128, 3600.0), (256, 600.0), (128, 3.0)])
+def test_q_zero_one_hot_bias_bf16(nb, gap):
+    import torch
+    wl = synth.custom([300, 150, 64], num_heads=2, d_qk=64, d_v=64, num_buckets=nb, dtype="bf16", gap_mean=gap,
+                      seed=12)
+    d = upload(wl)
+    d["q"] = torch.zeros_like(d["q"])
+    qz = np.zeros_like(wl.q.f64)
+    buckets = oracle.bucketize(wl.ts[:, None] - wl.ts[None, :], nb)
+    used = np.unique(buckets)
+    for target in used[:: max(1, len(used) // 4)]:
+        w = np.zeros((2, nb))
+        w[0, target] = 4.0
+        w[1, target] = -3.0
+        d["w"] = torch.from_numpy(w).to(torch.bfloat16).cuda()
+        out = to_f64(run_fwd(wl, d))
+        ref = oracle.attn_fwd(qz, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, w, nb)
+        assert_close(out, ref, "bf16", f"target {target}")
+
+
+def test_large_bias_weights_bf16():
+    # w ~ N(0, 1): the bias moves scores by O(alpha) and is visible in O.
+    wl = synth.custom([513, 1000, 31], num_heads=4, d_qk=128, d_v=128, num_buckets=128, dtype="bf16",
+                      seed=13, w_std=1.0)
+    d = upload(wl)
+    out = to_f64(run_fwd(wl, d))
+    ref = oracle_fwd(wl)
+    assert_close(out, ref, "bf16", "out")
+    no_bias = oracle.attn_fwd(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, np.zeros_like(wl.w.f64), 128)
+    # the comparison above is meaningful: dropping the bias would fail it
+    assert errors(no_bias, ref)["rel_l2"] > 5e-3
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    for name, got, r in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(to_f64(got), r, "bf16", name)
+
+
+def test_single_token_and_empty_sequences():
+    wl = synth.custom([1, 0, 1, 1, 0, 0, 1], num_heads=2, d_qk=64, d_v=64, dtype="fp32", seed=14, w_std=0.7)
+    d = upload(wl)
+    out = to_f64(run_fwd(wl, d))
+    alpha = 1 / 8.0
+    for i in range(wl.total):
+        for h in range(2):
+            s = alpha * (wl.q.f64[i, h] @ wl.k.f64[i, h] + wl.w.f64[h, 0])
+            np.testing.assert_allclose(out[i, h], s / (1 + math.exp(-s)) * wl.v.f64[i, h], atol=1e-5, rtol=0)
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    assert_close(to_f64(dq), rq, "fp32", "dq")
+    assert_close(to_f64(dw), rw, "fp32", "dw")
+
+
+def test_all_sequences_empty():
+    import torch
+    wl = synth.custom([0, 0, 0], num_heads=2, d_qk=64, d_v=64, dtype="bf16", seed=15)
+    d = upload(wl)
+    # one valid row so that tensors are allocated; offsets say nothing is there
+    out = hstu().jagged_attn_fwd(d["q"], d["k"], d["v"], d["offsets"], d["ts"], d["w"], 0)
+    assert out.shape[0] == 0
+    dq, dk, dv, dw = run_bwd(wl, d)
+    torch.cuda.synchronize()
+    assert float(dw.abs().max()) == 0.0
+
+
+def test_causality_on_gpu():
+    import torch
+    wl = synth.custom([400], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=16)
+    d = upload(wl)
+    base = run_fwd(wl, d).clone()
+    cut = 200
+    d2 = dict(d)
+    d2["k"] = d["k"].clone()
+    d2["v"] = d["v"].clone()
+    d2["k"][cut + 1:] += 3.0
+    d2["v"][cut + 1:] -= 5.0
+    pert = run_fwd(wl, d2)
+    assert torch.equal(pert[:cut + 1], base[:cut + 1])
+
+
+# --------------------------------------------------------------------------
+# Workload-sized checks.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [1002, 1102])
+def test_bf16_forward_u256_1024(seed):
+    wl = synth.config("bf16_fwd_u256_1024", seed=seed, with_dout=False)
+    d = upload(wl)
+    out = to_f64(run_fwd(wl, d))
+    assert_close(out, oracle_fwd(wl), "bf16", "out")
+
+
+def test_len3072_forward_backward_sampled():
+    wl = synth.config("bf16_len3072")
+    d = upload(wl)
+    out = to_f64(run_fwd(wl, d))
+    dq, dk, dv, dw = [to_f64(x) for x in run_bwd(wl, d)]
+    rows = sample_rows(wl.offsets, 48, seed=1)
+    args = (wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
+    assert_close(out[rows], oracle.attn_fwd_rows(*args, rows), "bf16", "out")
+    assert_close(dq[rows], oracle.attn_bwd_q_rows(wl.dout.f64, *args, rows), "bf16", "dq")
+    rk, rv = oracle.attn_bwd_kv_rows(wl.dout.f64, *args, rows)
+    assert_close(dk[rows], rk, "bf16", "dk")
+    assert_close(dv[rows], rv, "bf16", "dv")
+    # d(ts_weights) of head 0 over the whole batch, from the oracle on head 0 only
+    sub = lambda x: x[:, :1]
+    _, _, _, rw = oracle.attn_bwd(sub(wl.dout.f64), sub(wl.q.f64), sub(wl.k.f64), sub(wl.v.f64), wl.offsets,
+                                  wl.ts, wl.w.f64[:1], wl.num_buckets)
+    assert_close(dw[:1], rw, "bf16", "dw[head 0]")
+
+
+def test_skewed_powerlaw_sampled():
+    wl = synth.config("skewed_powerlaw")
+    d = upload(wl)
+    out = to_f64(run_fwd(wl, d))
+    dq, dk, dv, dw = [to_f64(x) for x in run_bwd(wl, d)]
+    longest = int(np.argmax(wl.lengths))
+    rows = sample_rows(wl.offsets, 40, seed=2)
+    rows += [int(wl.offsets[longest + 1]) - 1, int(wl.offsets[longest])]
+    rows = sorted(set(rows))
+    args = (wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
+    assert_close(out[rows], oracle.attn_fwd_rows(*args, rows), "bf16", "out")
+    assert_close(dq[rows], oracle.attn_bwd_q_rows(wl.dout.f64, *args, rows), "bf16", "dq")
+    rk, rv = oracle.attn_bwd_kv_rows(wl.dout.f64, *args, rows)
+    assert_close(dk[rows], rk, "bf16", "dk")
+    assert_close(dv[rows], rv, "bf16", "dv")
+
+
+def test_skewed_powerlaw_subset_full():
+    # the first 24 sequences of the skewed batch, every output and dW
+    wl = synth.config("skewed_powerlaw", num_seqs=24)
+    d = upload(wl)
+    assert_close(to_f64(run_fwd(wl, d)), oracle_fwd(wl), "bf16", "out")
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    for name, got, r in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(to_f64(got), r, "bf16", name)
