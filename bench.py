@@ -1,0 +1,314 @@
+"""Benchmark of the jagged HSTU attention hot path on one MI355X.
+
+A step is one forward plus one backward of jagged HSTU attention over the
+3072-length batch: B=16 sequences of length 3072, H=4 heads, d_qk=d_v=128,
+bf16 inputs with fp32 accumulation, 128 timestamp buckets (synthetic, seeded).
+The printed `value` is causal-effective TFLOP/s of the whole step: counted
+FLOPs are 2*(d_qk+d_v) per causal pair and head for the forward and
+2*(3*d_qk+2*d_v) for the backward, over pairs j <= i inside each sequence.
+
+Inputs, outputs and workspaces are allocated before the timed region; each
+step calls the C ABI (forward, then backward) on torch's current stream.
+
+Besides the JSON contract fields it reports:
+  roofline      the kernel with the largest time (timed alone with HIP events
+                on the stream it runs on) against the bf16 dense MFMA peak;
+  cpu_baseline  the float64 oracle on a bounded sample of the same workload;
+  extra         the other workloads: the CP=8 rank-3 share at length 16384
+                (forward+backward), its chunk-pair reorder in GB/s, the skewed
+                power-law batch (forward+backward) and the uniform 256..1024
+                forward.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s dense)
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def causal_pairs(lengths):
+    return int(sum(int(n) * (int(n) + 1) // 2 for n in lengths))
+
+
+def cp_rank_pairs(lengths, cp_size, rank):
+    """Causal pairs whose query row lies in mini-chunks r and 2C-1-r."""
+    total = 0
+    for n in lengths:
+        n = int(n)
+        for c in (rank, 2 * cp_size - 1 - rank):
+            lo, hi = c * n // (2 * cp_size), (c + 1) * n // (2 * cp_size)
+            total += (hi * (hi + 1) - lo * (lo + 1)) // 2
+    return total
+
+
+def flops(pairs, heads, dqk, dv):
+    fwd = 2 * (dqk + dv) * pairs * heads
+    bwd = 2 * (3 * dqk + 2 * dv) * pairs * heads
+    return fwd, bwd
+
+
+class Case:
+    """A workload uploaded once, with preallocated outputs and workspaces."""
+
+    def __init__(self, wl, *, cp_size=1, cp_rank=0):
+        import numpy as np
+        import torch
+        import jagged_hstu_attention_amd as m
+        self.m = m
+        self.wl = wl
+
+        def up(t):
+            if t.dtype == "bf16":
+                return torch.from_numpy(t.raw.view(np.int16).copy()).view(torch.bfloat16).cuda()
+            return torch.from_numpy(t.raw.copy()).cuda()
+
+        self.k, self.v, self.w = up(wl.k), up(wl.v), up(wl.w)
+        self.offsets = torch.from_numpy(wl.offsets).cuda()
+        self.ts = torch.from_numpy(wl.ts).cuda()
+        q, do = up(wl.q), up(wl.dout)
+        self.cp_size, self.cp_rank = cp_size, cp_rank
+        if cp_size > 1:
+            qr, seg = m.cp_reorder(q, self.offsets, wl.max_seq_len, cp_size)
+            dr, _ = m.cp_reorder(do, self.offsets, wl.max_seq_len, cp_size)
+            seg = seg.cpu().numpy()
+            B = wl.num_seqs
+            lo, hi = int(seg[cp_rank * B]), int(seg[(cp_rank + 1) * B])
+            q, do = qr[lo:hi].contiguous(), dr[lo:hi].contiguous()
+        self.q, self.dout = q, do
+        self.out = torch.empty((q.shape[0], q.shape[1], self.v.shape[2]), dtype=q.dtype, device="cuda")
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(self.k)
+        self.dv = torch.empty_like(self.v)
+        self.dw = torch.empty(self.w.shape, dtype=torch.float32, device="cuda")
+        p = m.problem(q, self.k, self.v, self.offsets, self.w, wl.max_seq_len, cp_size=cp_size, cp_rank=cp_rank)
+        self.ws_f = torch.empty(m.workspace_size(p, False), dtype=torch.uint8, device="cuda")
+        self.ws_b = torch.empty(m.workspace_size(p, True), dtype=torch.uint8, device="cuda")
+
+    def fwd(self):
+        self.m.jagged_attn_fwd(self.q, self.k, self.v, self.offsets, self.ts, self.w, self.wl.max_seq_len,
+                               cp_size=self.cp_size, cp_rank=self.cp_rank, out=self.out, workspace=self.ws_f)
+
+    def bwd(self):
+        self.m.jagged_attn_bwd(self.dout, self.q, self.k, self.v, self.offsets, self.ts, self.w,
+                               self.wl.max_seq_len, cp_size=self.cp_size, cp_rank=self.cp_rank, dq=self.dq,
+                               dk=self.dk, dv=self.dv, dw=self.dw, workspace=self.ws_b)
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+
+def time_loop(fn, steps, warmup):
+    """Average ms per call over `steps` calls, bracketed by HIP events on the
+    current stream (the stream every launch goes to)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(max_seconds=30.0):
+    """The float64 oracle, as it stands, on a bounded sample of the 3072-length
+    workload: whole sequences (all 4 heads, forward + backward), as many as fit
+    in about 15 s, scaled to causal-effective TFLOP/s."""
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        blas_threads = max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    n_done, t_total = 0, 0.0
+    wl = synth.config("bf16_len3072", num_seqs=4)
+    for b in range(4):
+        lo, hi = int(wl.offsets[b]), int(wl.offsets[b + 1])
+        off = [0, hi - lo]
+        sl = slice(lo, hi)
+        t0 = time.perf_counter()
+        oracle.attn_fwd(wl.q.f64[sl], wl.k.f64[sl], wl.v.f64[sl], off, wl.ts[sl], wl.w.f64, wl.num_buckets)
+        oracle.attn_bwd(wl.dout.f64[sl], wl.q.f64[sl], wl.k.f64[sl], wl.v.f64[sl], off, wl.ts[sl], wl.w.f64,
+                        wl.num_buckets)
+        t_total += time.perf_counter() - t0
+        n_done += 1
+        if t_total > max_seconds / 2:
+            break
+    f, bw = flops(causal_pairs([3072] * n_done), 4, 128, 128)
+    return {
+        "value": (f + bw) / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{n_done} of 16 sequences (length 3072, 4 heads, d=128), forward+backward in float64 numpy, "
+                  f"{t_total:.1f} s; BLAS threads={blas_threads}, elementwise numpy single-threaded; "
+                  f"host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def reorder_bandwidth(m, steps):
+    """Chunk-pair reorder of the CP=8, length-16384 bf16 [65536, 4, 128] tensor.
+    Buffer pairs are rotated so the working set (5 x 128 MiB) exceeds the
+    256 MB last-level cache; a plain device copy of the same bytes is timed
+    the same way."""
+    import torch
+    import synth
+    B, L, C = 4, 16384, 8
+    off = torch.from_numpy(synth.offsets_from_lengths([L] * B)).cuda()
+    nbuf = 5
+    src = [torch.randn(B * L, 4, 128, device="cuda").to(torch.bfloat16) for _ in range(nbuf)]
+    dst = [torch.empty_like(s) for s in src]
+    seg = torch.empty(C * B + 1, dtype=torch.int64, device="cuda")
+    it = [0]
+
+    def one():
+        i = it[0] % nbuf
+        it[0] += 1
+        m.cp_reorder(src[i], off, L, C, out=dst[i], out_offsets=seg)
+
+    def cp():
+        i = it[0] % nbuf
+        it[0] += 1
+        dst[i].copy_(src[i])
+
+    ms = time_loop(one, steps, 3)
+    ms_copy = time_loop(cp, steps, 3)
+    nbytes = 2 * src[0].numel() * 2
+    return {"gbs": nbytes / ms / 1e6, "ms": ms, "copy_gbs": nbytes / ms_copy / 1e6, "bytes_moved": nbytes}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import jagged_hstu_attention_amd as m
+    import synth
+
+    m._lib.load()
+    torch.cuda.set_device(0)
+    log("uploading the 3072-length workload")
+    wl = synth.config("bf16_len3072")
+    case = Case(wl)
+    pairs = causal_pairs(wl.lengths)
+    f_fwd, f_bwd = flops(pairs, wl.num_heads, wl.d_qk, wl.d_v)
+
+    log(f"timing {args.steps} steps after {args.warmup} warmup")
+    ms_step = time_loop(case.step, args.steps, args.warmup)
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms -> {value:.1f} TFLOP/s")
+
+    ms_fwd = time_loop(case.fwd, args.steps, 2)
+    ms_bwd = time_loop(case.bwd, args.steps, 2)
+    log(f"forward {ms_fwd:.3f} ms, backward {ms_bwd:.3f} ms")
+    if ms_bwd >= ms_fwd:
+        dom_name, dom_ms, dom_flops = "backward (hstu_jagged_attn_bwd: bwd_kernel)", ms_bwd, f_bwd
+    else:
+        dom_name, dom_ms, dom_flops = "forward (hstu_jagged_attn_fwd: fwd_kernel)", ms_fwd, f_fwd
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom_name,
+                "ms_per_launch": round(dom_ms, 4)}
+
+    extra = {
+        "len3072_forward": {"ms": round(ms_fwd, 4), "tflops": round(f_fwd / ms_fwd / 1e9, 2)},
+        "len3072_backward": {"ms": round(ms_bwd, 4), "tflops": round(f_bwd / ms_bwd / 1e9, 2)},
+    }
+    if not args.no_extra:
+        del case
+        torch.cuda.empty_cache()
+        log("CP=8 rank-3 share, length 16384")
+        wl4 = synth.config("cp8_rank3_len16384")
+        c4 = Case(wl4, cp_size=synth.CP_SIZE, cp_rank=synth.CP_RANK)
+        p4 = cp_rank_pairs(wl4.lengths, synth.CP_SIZE, synth.CP_RANK)
+        f4f, f4b = flops(p4, wl4.num_heads, wl4.d_qk, wl4.d_v)
+        t4f = time_loop(c4.fwd, args.steps, 2)
+        t4b = time_loop(c4.bwd, args.steps, 2)
+        extra["cp8_rank3_len16384"] = {"fwd_ms": round(t4f, 4), "bwd_ms": round(t4b, 4),
+                                       "tflops": round((f4f + f4b) / (t4f + t4b) / 1e9, 2)}
+        del c4
+        torch.cuda.empty_cache()
+        log("reorder bandwidth")
+        rb = reorder_bandwidth(m, args.steps)
+        extra["cp8_reorder_len16384"] = {"gbs": round(rb["gbs"], 1), "frac_hbm": round(rb["gbs"] / HBM_PEAK_GBS, 4),
+                                         "copy_gbs": round(rb["copy_gbs"], 1), "ms": round(rb["ms"], 4)}
+        torch.cuda.empty_cache()
+        log("skewed power-law batch")
+        wl5 = synth.config("skewed_powerlaw")
+        c5 = Case(wl5)
+        f5f, f5b = flops(causal_pairs(wl5.lengths), wl5.num_heads, wl5.d_qk, wl5.d_v)
+        t5f = time_loop(c5.fwd, args.steps, 2)
+        t5b = time_loop(c5.bwd, args.steps, 2)
+        extra["skewed_powerlaw"] = {"fwd_ms": round(t5f, 4), "bwd_ms": round(t5b, 4),
+                                    "tflops": round((f5f + f5b) / (t5f + t5b) / 1e9, 2)}
+        del c5
+        torch.cuda.empty_cache()
+        log("uniform 256..1024 forward")
+        wl2 = synth.config("bf16_fwd_u256_1024", with_dout=True)
+        c2 = Case(wl2)
+        f2f, _ = flops(causal_pairs(wl2.lengths), wl2.num_heads, wl2.d_qk, wl2.d_v)
+        t2f = time_loop(c2.fwd, args.steps, 2)
+        extra["u256_1024_forward"] = {"fwd_ms": round(t2f, 4), "tflops": round(f2f / t2f / 1e9, 2)}
+        del c2
+
+    cpu = None
+    if not args.no_cpu:
+        log("CPU oracle baseline (bounded sample)")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": "jagged HSTU attention TFLOPS (causal-effective) and % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 forward+backward, B=16 x length 3072, H=4, d_qk=d_v=128, 128 buckets",
+                   "global_batch": 16, "seq_len": 3072, "parallelism": "none (1 GPU)",
+                   "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -221,7 +221,9 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   sp.q_cost_tile = hstu::attn_k_tile_keys();
   sp.k_tile = backward ? hstu::attn_bwd_key_tile() : 0;
   sp.k_cost_tile = hstu::attn_bwd_q_step();
-  sp.hist_size = hstu::kSchedHist;
+  // costs are at most ceil(max_seq_len / 64) + 2 tiles
+  const int64_t max_cost = cdiv(p->max_seq_len, std::min(hstu::attn_k_tile_keys(), hstu::attn_bwd_q_step())) + 3;
+  sp.hist_size = (int)std::min<int64_t>(hstu::kSchedHist, std::max<int64_t>(max_cost, 1));
   sp.local_off = reinterpret_cast<int64_t*>(ws + l.local_off);
   sp.qitems = reinterpret_cast<hstu::Item*>(ws + l.qitems);
   sp.kitems = reinterpret_cast<hstu::Item*>(ws + l.kitems);

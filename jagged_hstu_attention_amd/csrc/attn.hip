@@ -9,7 +9,16 @@
 //   O_i  = sum_j a_ij v_j
 // Backward: dP = dO Vᵀ, G = alpha * dP * SiLU'(s) * mask, dV = aᵀ dO,
 // dK = Gᵀ Q, dQ = G K, dW[h, b] = sum of G over pairs in bucket b.
+//
+// Every lane owns one row for the whole item (a query in the forward and dQ
+// passes, a key in the dK/dV pass), so the timestamp of its row, its causal
+// limit and its bias plan (epilogue.h) are per-lane scalars.  Tiles of the
+// other side are loaded into registers one tile ahead and stored to LDS after
+// the previous tile has been consumed.
+#include <type_traits>
+
 #include "attn.h"
+#include "epilogue.h"
 #include "tiles.h"
 
 namespace hstu {
@@ -17,37 +26,42 @@ namespace hstu {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
+constexpr int BM = 128;        // query rows per forward / dQ item (32 per wave)
+constexpr int BN = 64;         // keys per tile in the forward / dQ loops
+constexpr int BK = 128;        // keys per dK/dV item (32 per wave)
+constexpr int BQ = 64;         // query rows per step of the dK/dV loop
 
-template <typename T, int D> struct FwdCfg {
-  static constexpr int BM = 128;  // query rows per item (32 per wave)
-  static constexpr int BN = 64;   // keys per tile
-};
-
-template <typename T, int D, int BN> struct alignas(16) KvTiles {
-  T k[BN * Pitch<T, D>::row];
-  // bf16: V transposed ([d][slot]); fp32: V row-major.
-  T v[sizeof(T) == 2 ? D * TPitch<BN>::col : BN * Pitch<T, D>::row];
-  int64_t ts[BN];
-};
+// d(ts_weights) bins are kept in kDwCopies interleaved copies (lane l adds to
+// copy l % kDwCopies) so that lanes of one instruction that hit the same bucket
+// mostly hit different addresses; the copies are summed at flush time.
+constexpr int kDwCopies = 8;
 
 struct alignas(16) Tables {
-  float w[kMaxBuckets];          // alpha * ts_weights[h, :]
-  uint32_t e[kMaxBuckets + 4];   // bucket edges E[0..NB]
-  float dw[kMaxBuckets];         // per-item d(ts_weights) bins (backward)
+  float w[kMaxBuckets];                         // alpha * ts_weights[h, :]
+  u32x2 ep[kMaxBuckets];                        // bucket edge pairs (E[k], E[k+1])
+  float dw[kDwCopies][kMaxBuckets + 1];         // per-item d(ts_weights) bins (backward)
   int item;
 };
 
-__device__ __forceinline__ void load_edges(Tables& t, const AttnParams& p, int tid) {
-  for (int i = tid; i <= p.NB; i += kThreads) t.e[i] = p.edges[i];
+struct alignas(16) TablesFwd {
+  float w[kMaxBuckets];
+  u32x2 ep[kMaxBuckets];
+  int item;
+};
+
+template <typename TB>
+__device__ __forceinline__ void load_edges(TB& t, const AttnParams& p, int tid) {
+  for (int i = tid; i < p.NB; i += kThreads) t.ep[i] = u32x2{p.edges[i], p.edges[i + 1]};
 }
 
-template <typename T>
-__device__ __forceinline__ void load_wtab(Tables& t, const AttnParams& p, int h, int tid) {
+template <typename T, typename TB>
+__device__ __forceinline__ void load_wtab(TB& t, const AttnParams& p, int h, int tid) {
   const T* W = static_cast<const T*>(p.w) + (int64_t)h * p.NB;
   for (int i = tid; i < p.NB; i += kThreads) t.w[i] = p.alpha * to_f32<T>(W[i]);
 }
 
-__device__ __forceinline__ int pop_item(Tables& t, int* counter, int tid) {
+template <typename TB>
+__device__ __forceinline__ int pop_item(TB& t, int* counter, int tid) {
   __syncthreads();
   if (tid == 0) t.item = atomicAdd(counter, 1);
   __syncthreads();
@@ -79,25 +93,63 @@ __device__ __forceinline__ int q_segments(const AttnParams& p, int b, Seg* seg) 
   return 2;
 }
 
+// Steps of BQ query rows, over the segments, from position `start` on.
+struct StepIter {
+  Seg seg[2];
+  int nseg;
+  int start;
+  int si;
+  int q0;
+  __device__ __forceinline__ void norm() {
+    while (si < nseg && q0 >= seg[si].pos0 + seg[si].len) {
+      ++si;
+      if (si < nseg) q0 = max(seg[si].pos0, start);
+    }
+  }
+  __device__ __forceinline__ void init(const AttnParams& p, int b, int start_pos) {
+    nseg = q_segments(p, b, seg);
+    start = start_pos;
+    si = 0;
+    q0 = max(seg[0].pos0, start);
+    norm();
+  }
+  __device__ __forceinline__ bool valid() const { return si < nseg; }
+  __device__ __forceinline__ int nq() const { return min(BQ, seg[si].pos0 + seg[si].len - q0); }
+  __device__ __forceinline__ int64_t lrow() const { return seg[si].row0 + (q0 - seg[si].pos0); }
+  __device__ __forceinline__ void next() {
+    q0 += BQ;
+    norm();
+  }
+};
+
+template <typename T, int D, int ROWS>
+using TStageFor = typename std::conditional<sizeof(T) == 2, TStage<D, ROWS, kThreads>, RowStage<T, D, ROWS, kThreads>>::type;
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // Forward.  One item = (query tile of 128 rows, head).  Wave w owns query rows
-// 32w..32w+31 of the tile; lane (r32, g) owns query row 32w + r32 throughout:
-// the score tile is computed transposed, Sᵀ = K Qᵀ, so every accumulator value
-// of a lane belongs to its own query row, and the output is computed as
-// Oᵀ = Vᵀ Pᵀ with P taken straight from the Sᵀ accumulators.
+// 32w..32w+31 of the tile; lane (r32, g) owns query row 32w + r32: the score
+// tile is computed transposed, Sᵀ = K Qᵀ, so every accumulator value of a lane
+// belongs to its own query, and the output is Oᵀ = Vᵀ Pᵀ with P taken straight
+// from the Sᵀ accumulators.
 // ---------------------------------------------------------------------------
+template <typename T, int D> struct alignas(16) FwdSmem {
+  T k[BN * Pitch<T, D>::row];
+  T v[sizeof(T) == 2 ? D * TPitch<BN>::col : BN * Pitch<T, D>::row];
+  TsTile<BN> ts;
+};
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, D >= 128 ? 1 : 2) void fwd_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr int BN = FwdCfg<T, D>::BN;
-  __shared__ KvTiles<T, D, BN> kv;
-  __shared__ Tables tb;
+  __shared__ FwdSmem<T, D> sm;
+  __shared__ TablesFwd tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
-  const int H = p.H;
-  const float nb32 = p.NB * (1.0f / 32.0f);
+  const int H = p.H, NB = p.NB;
+  const float nb32 = NB * (1.0f / 32.0f);
+  const float alpha = p.alpha;
   const int64_t ld = (int64_t)H * D;
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
@@ -130,35 +182,58 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const AttnParams p) {
 
     const int kv_len = it.pos0 + it.n;
     const int n_kt = (kv_len + BN - 1) / BN;
+    const int wave_qmin = it.pos0 + wave * 32;
+    const T* Kh = K + seq0 * ld + h * D;
+    const T* Vh = V + seq0 * ld + h * D;
+    RowStage<T, D, BN, kThreads> kst;
+    TStageFor<T, D, BN> vst;
+    int64_t tsv = 0;
+    bool tsvalid = false;
+    auto prefetch = [&](int kt) {
+      const int key0 = kt * BN, nvalid = min(BN, kv_len - key0);
+      kst.load(Kh + key0 * ld, ld, nvalid, tid);
+      vst.load(Vh + key0 * ld, ld, nvalid, tid);
+      if (wave == 0) {
+        tsvalid = lane < nvalid;
+        tsv = tsvalid ? p.ts[seq0 + key0 + lane] : 0;
+      }
+    };
+    prefetch(0);
     for (int kt = 0; kt < n_kt; ++kt) {
       const int key0 = kt * BN;
       const int nvalid = min(BN, kv_len - key0);
       __syncthreads();
-      const int64_t krow = seq0 + key0;
-      stage_rows<T, D, BN, kThreads>(kv.k, K + krow * ld + h * D, ld, nvalid, tid);
-      if constexpr (sizeof(T) == 2)
-        stage_rows_t<D, BN, kThreads>(kv.v, V + krow * ld + h * D, ld, nvalid, tid);
-      else
-        stage_rows<T, D, BN, kThreads>(kv.v, V + krow * ld + h * D, ld, nvalid, tid);
-      for (int j = tid; j < BN; j += kThreads) kv.ts[j] = j < nvalid ? p.ts[krow + j] : 0;
+      kst.store(sm.k, tid);
+      vst.store(sm.v, tid);
+      if (wave == 0) ts_tile_fill<BN, false>(sm.ts, tsv, tsvalid, lane);
       __syncthreads();
+      if (kt + 1 < n_kt) prefetch(kt + 1);
 
-      float pv[BN / 32][16];
-      const bool diag = key0 + BN - 1 > it.pos0;
+      const int lim = min(nvalid - 1, qpos - key0);
+      const bool any = qvalid && lim >= 0;
+      const int li = any ? lim : 0;
+      const LaneBias lb = lane_bias<+1>(tsq, sm.ts.lo[li], sm.ts.hi[li], any, sm.ts.base, sm.ts.wide, tb.w, tb.ep,
+                                        NB, nb32);
+      const int mode = wave_mode(lb.n);
+      int32_t tsr_rel = 0;
+      const bool fast32 = mode == kModeExact && wave_fast32(tsq, sm.ts.base, sm.ts.wide, &tsr_rel);
+      const bool diag = key0 + BN - 1 > wave_qmin;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) {
-        const f32x16 s = mma_tile_rows<T, D>(kv.k, blk * 32 + r32, qop, g);
+        const f32x16 s = mma_tile_rows<T, D>(sm.k, blk * 32 + r32, qop, g);
+        float cb[16];
+        int bsel[16];
+        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, sm.ts, blk, g, tb.w, tb.ep, NB, nb32);
+        float pv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int kj = blk * 32 + acc_row(i, g);
-          const int bk = bucket_of(tsq - kv.ts[kj], p.NB, nb32, tb.e);
-          const float x = fmaf(s[i], p.alpha, tb.w[bk]);
+          const float x = fmaf(s[i], alpha, cb[i]);
           float a = x * fast_sigmoid(x);
-          if (diag && key0 + kj > qpos) a = 0.0f;
-          pv[blk][i] = a;
+          if (diag && key0 + blk * 32 + acc_row(i, g) > qpos) a = 0.0f;
+          pv[i] = a;
         }
+        mma_contract_block<T, D, BN>(oacc, sm.v, pv, blk, r32, g);
       }
-      mma_contract_rows<T, D, BN>(oacc, kv.v, pv, r32, g);
     }
     if (qvalid) store_row_from_acc<T, D>(O + qrow * ld + h * D, oacc, g);
   }
@@ -168,31 +243,29 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(const AttnParams p) {
 // Backward, key-major pass: dK, dV and d(ts_weights).  One item = (key tile of
 // 128 keys, head); lane (r32, g) of wave w owns key 32w + r32.  For each step of
 // 64 query rows it computes S = Q Kᵀ and dP = dO Vᵀ (so the lane's values all
-// belong to its own key), then dVᵀ += dOᵀ P and dKᵀ += Qᵀ G.
+// belong to its own key), then dVᵀ += dOᵀ P and dKᵀ += Qᵀ G.  Query rows past
+// the end of a step are zero-filled, which makes their P·dO and G terms vanish
+// without a mask.
 // ---------------------------------------------------------------------------
-template <typename T, int D> struct BwdKvCfg {
-  static constexpr int BK = 128;  // keys per item
-  static constexpr int BQ = 64;   // query rows per step
-};
-
-template <typename T, int D, int BQ> struct alignas(16) QdoTiles {
+template <typename T, int D> struct alignas(16) BwdKvSmem {
   T q[BQ * Pitch<T, D>::row];
   T dout[BQ * Pitch<T, D>::row];
-  T qt[sizeof(T) == 2 ? D * TPitch<BQ>::col : 1];
-  T doutt[sizeof(T) == 2 ? D * TPitch<BQ>::col : 1];
-  int64_t ts[BQ];
+  T qt[sizeof(T) == 2 ? D * TPitch<BQ>::col : 8];
+  T doutt[sizeof(T) == 2 ? D * TPitch<BQ>::col : 8];
+  TsTile<BQ> ts;
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_kv_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr int BQ = BwdKvCfg<T, D>::BQ;
-  __shared__ QdoTiles<T, D, BQ> qt;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  __shared__ BwdKvSmem<T, D> sm;
   __shared__ Tables tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
-  const int H = p.H;
-  const float nb32 = p.NB * (1.0f / 32.0f);
+  const int H = p.H, NB = p.NB;
+  const float nb32 = NB * (1.0f / 32.0f);
+  const float alpha = p.alpha;
   const int64_t ld = (int64_t)H * D;
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
@@ -225,65 +298,97 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(const AttnParams p) {
       }
     }
     load_wtab<T>(tb, p, h, tid);
-    for (int i = tid; i < p.NB; i += kThreads) tb.dw[i] = 0.0f;
+    for (int i = tid; i < kDwCopies * (kMaxBuckets + 1); i += kThreads) (&tb.dw[0][0])[i] = 0.0f;
+    float* dwl = tb.dw[lane % kDwCopies];
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
       dkacc[i] = f32x16{};
       dvacc[i] = f32x16{};
     }
+    const int wave_kmax = it.pos0 + wave * 32 + 31;
 
-    Seg seg[2];
-    const int nseg = q_segments(p, it.b, seg);
-    for (int sgi = 0; sgi < nseg; ++sgi) {
-      const Seg sg = seg[sgi];
-      const int segend = sg.pos0 + sg.len;
-      // queries at positions >= it.pos0 can see some key of the tile
-      const int start = max(sg.pos0, it.pos0);
-      for (int q0 = start; q0 < segend; q0 += BQ) {
-        const int nq = min(BQ, segend - q0);
-        const int64_t lrow = sg.row0 + (q0 - sg.pos0);
-        __syncthreads();
-        stage_rows<T, D, BQ, kThreads>(qt.q, Q + lrow * ld + h * D, ld, nq, tid);
-        stage_rows<T, D, BQ, kThreads>(qt.dout, dO + lrow * ld + h * D, ld, nq, tid);
-        if constexpr (sizeof(T) == 2) {
-          stage_rows_t<D, BQ, kThreads>(qt.qt, Q + lrow * ld + h * D, ld, nq, tid);
-          stage_rows_t<D, BQ, kThreads>(qt.doutt, dO + lrow * ld + h * D, ld, nq, tid);
-        }
-        for (int j = tid; j < BQ; j += kThreads) qt.ts[j] = j < nq ? p.ts[seq0 + q0 + j] : 0;
-        __syncthreads();
+    RowStage<T, D, BQ, kThreads> qst, dst;
+    TStage<D, BQ, kThreads> qtst, dtst;
+    int64_t tsv = 0;
+    bool tsvalid = false;
+    StepIter si;
+    si.init(p, it.b, it.pos0);
+    auto prefetch = [&](const StepIter& s) {
+      const int nq = s.nq();
+      const int64_t lrow = s.lrow();
+      qst.load(Q + lrow * ld + h * D, ld, nq, tid);
+      dst.load(dO + lrow * ld + h * D, ld, nq, tid);
+      if constexpr (kBf16) {
+        qtst.load(Q + lrow * ld + h * D, ld, nq, tid);
+        dtst.load(dO + lrow * ld + h * D, ld, nq, tid);
+      }
+      if (wave == 0) {
+        tsvalid = lane < nq;
+        tsv = tsvalid ? p.ts[seq0 + s.q0 + lane] : 0;
+      }
+    };
+    if (si.valid()) prefetch(si);
+    while (si.valid()) {
+      const int q0 = si.q0;
+      const int nq = si.nq();
+      __syncthreads();
+      qst.store(sm.q, tid);
+      dst.store(sm.dout, tid);
+      if constexpr (kBf16) {
+        qtst.store(sm.qt, tid);
+        dtst.store(sm.doutt, tid);
+      }
+      if (wave == 0) ts_tile_fill<BQ, true>(sm.ts, tsv, tsvalid, lane);
+      __syncthreads();
+      si.next();
+      if (si.valid()) prefetch(si);
 
-        float pv[BQ / 32][16], gv[BQ / 32][16];
+      const int first = max(0, kpos - q0);
+      const bool any = kvalid && first < nq;
+      const int fi = any ? first : 0;
+      const LaneBias lb = lane_bias<-1>(tsk, sm.ts.lo[fi], sm.ts.hi[fi], any, sm.ts.base, sm.ts.wide, tb.w, tb.ep,
+                                        NB, nb32);
+      const int mode = wave_mode(lb.n);
+      int32_t tsr_rel = 0;
+      const bool fast32 = mode == kModeExact && wave_fast32(tsk, sm.ts.base, sm.ts.wide, &tsr_rel);
+      const bool needmask = q0 < wave_kmax;
+      float dwb[kMaxEdges + 1] = {0.0f, 0.0f, 0.0f, 0.0f};  // bins b_lo + k
 #pragma unroll
-        for (int blk = 0; blk < BQ / 32; ++blk) {
-          const f32x16 s = mma_tile_rows<T, D>(qt.q, blk * 32 + r32, kop, g);
-          const f32x16 dp = mma_tile_rows<T, D>(qt.dout, blk * 32 + r32, vop, g);
+      for (int blk = 0; blk < BQ / 32; ++blk) {
+        const f32x16 s = mma_tile_rows<T, D>(sm.q, blk * 32 + r32, kop, g);
+        const f32x16 dp = mma_tile_rows<T, D>(sm.dout, blk * 32 + r32, vop, g);
+        float cb[16];
+        int bsel[16];
+        block_bias<-1, BQ>(cb, bsel, mode, lb, tsk, tsr_rel, fast32, sm.ts, blk, g, tb.w, tb.ep, NB, nb32);
+        float pv[16], gv[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qj = blk * 32 + acc_row(i, g);
-            const bool valid = kvalid && qj < nq && kpos <= q0 + qj;
-            const int bk = bucket_of(qt.ts[qj] - tsk, p.NB, nb32, tb.e);
-            const float x = fmaf(s[i], p.alpha, tb.w[bk]);
-            const float sg_ = fast_sigmoid(x);
-            float a = x * sg_;
-            float gg = p.alpha * dp[i] * (sg_ * (1.0f + x * (1.0f - sg_)));
-            if (!valid) {
-              a = 0.0f;
-              gg = 0.0f;
-            } else {
-              atomicAdd(&tb.dw[bk], gg);
-            }
-            pv[blk][i] = a;
-            gv[blk][i] = gg;
+        for (int i = 0; i < 16; ++i) {
+          const float x = fmaf(s[i], alpha, cb[i]);
+          const float sg = fast_sigmoid(x);
+          float a = x * sg;
+          float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
+          if (needmask && q0 + blk * 32 + acc_row(i, g) < kpos) {
+            a = 0.0f;
+            gg = 0.0f;
+          }
+          pv[i] = a;
+          gv[i] = gg;
+          if (mode == kModeExact) {
+            if (gg != 0.0f) atomicAdd(&dwl[bsel[i]], gg);
+          } else {
+#pragma unroll
+            for (int k = 0; k <= kMaxEdges; ++k)
+              if (k <= mode) dwb[k] += bsel[i] == k ? gg : 0.0f;
           }
         }
-        if constexpr (sizeof(T) == 2) {
-          mma_contract_rows<T, D, BQ>(dvacc, qt.doutt, pv, r32, g);
-          mma_contract_rows<T, D, BQ>(dkacc, qt.qt, gv, r32, g);
-        } else {
-          mma_contract_rows<T, D, BQ>(dvacc, qt.dout, pv, r32, g);
-          mma_contract_rows<T, D, BQ>(dkacc, qt.q, gv, r32, g);
-        }
+        mma_contract_block<T, D, BQ>(dvacc, kBf16 ? sm.doutt : sm.dout, pv, blk, r32, g);
+        mma_contract_block<T, D, BQ>(dkacc, kBf16 ? sm.qt : sm.q, gv, blk, r32, g);
+      }
+      if (mode != kModeExact) {
+#pragma unroll
+        for (int k = 0; k <= kMaxEdges; ++k)
+          if (dwb[k] != 0.0f) atomicAdd(&dwl[lb.b_lo + k], dwb[k]);
       }
     }
     if (kvalid) {
@@ -291,9 +396,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(const AttnParams p) {
       store_row_from_acc<T, D>(dV + krow * ld + h * D, dvacc, g);
     }
     __syncthreads();
-    for (int i = tid; i < p.NB; i += kThreads) {
-      const float v = tb.dw[i];
-      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * p.NB + i, v);
+    for (int i = tid; i < NB; i += kThreads) {
+      float v = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kDwCopies; ++c) v += tb.dw[c][i];
+      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, v);
     }
   }
 }
@@ -302,23 +409,24 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_kernel(const AttnParams p) {
 // Backward, query-major pass: dQ.  Same item list and lane ownership as the
 // forward; Sᵀ = K Qᵀ and dPᵀ = V dOᵀ are recomputed and dQᵀ += Kᵀ Gᵀ.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int BN> struct alignas(16) KvtTiles {
+template <typename T, int D> struct alignas(16) BwdQSmem {
   T k[BN * Pitch<T, D>::row];
   T v[BN * Pitch<T, D>::row];
-  T kt[sizeof(T) == 2 ? D * TPitch<BN>::col : 1];
-  int64_t ts[BN];
+  T kt[sizeof(T) == 2 ? D * TPitch<BN>::col : 8];
+  TsTile<BN> ts;
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_q_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_q_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr int BN = FwdCfg<T, D>::BN;
-  __shared__ KvtTiles<T, D, BN> kv;
-  __shared__ Tables tb;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  __shared__ BwdQSmem<T, D> sm;
+  __shared__ TablesFwd tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
-  const int H = p.H;
-  const float nb32 = p.NB * (1.0f / 32.0f);
+  const int H = p.H, NB = p.NB;
+  const float nb32 = NB * (1.0f / 32.0f);
+  const float alpha = p.alpha;
   const int64_t ld = (int64_t)H * D;
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
@@ -356,37 +464,62 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(const AttnParams p) {
 
     const int kv_len = it.pos0 + it.n;
     const int n_kt = (kv_len + BN - 1) / BN;
+    const int wave_qmin = it.pos0 + wave * 32;
+    const T* Kh = K + seq0 * ld + h * D;
+    const T* Vh = V + seq0 * ld + h * D;
+    RowStage<T, D, BN, kThreads> kst, vst;
+    TStage<D, BN, kThreads> ktst;
+    int64_t tsv = 0;
+    bool tsvalid = false;
+    auto prefetch = [&](int kt) {
+      const int key0 = kt * BN, nvalid = min(BN, kv_len - key0);
+      kst.load(Kh + key0 * ld, ld, nvalid, tid);
+      vst.load(Vh + key0 * ld, ld, nvalid, tid);
+      if constexpr (kBf16) ktst.load(Kh + key0 * ld, ld, nvalid, tid);
+      if (wave == 0) {
+        tsvalid = lane < nvalid;
+        tsv = tsvalid ? p.ts[seq0 + key0 + lane] : 0;
+      }
+    };
+    prefetch(0);
     for (int kt = 0; kt < n_kt; ++kt) {
       const int key0 = kt * BN;
       const int nvalid = min(BN, kv_len - key0);
       __syncthreads();
-      const int64_t krow = seq0 + key0;
-      stage_rows<T, D, BN, kThreads>(kv.k, K + krow * ld + h * D, ld, nvalid, tid);
-      stage_rows<T, D, BN, kThreads>(kv.v, V + krow * ld + h * D, ld, nvalid, tid);
-      if constexpr (sizeof(T) == 2) stage_rows_t<D, BN, kThreads>(kv.kt, K + krow * ld + h * D, ld, nvalid, tid);
-      for (int j = tid; j < BN; j += kThreads) kv.ts[j] = j < nvalid ? p.ts[krow + j] : 0;
+      kst.store(sm.k, tid);
+      vst.store(sm.v, tid);
+      if constexpr (kBf16) ktst.store(sm.kt, tid);
+      if (wave == 0) ts_tile_fill<BN, false>(sm.ts, tsv, tsvalid, lane);
       __syncthreads();
+      if (kt + 1 < n_kt) prefetch(kt + 1);
 
-      float gv[BN / 32][16];
+      const int lim = min(nvalid - 1, qpos - key0);
+      const bool any = qvalid && lim >= 0;
+      const int li = any ? lim : 0;
+      const LaneBias lb = lane_bias<+1>(tsq, sm.ts.lo[li], sm.ts.hi[li], any, sm.ts.base, sm.ts.wide, tb.w, tb.ep,
+                                        NB, nb32);
+      const int mode = wave_mode(lb.n);
+      int32_t tsr_rel = 0;
+      const bool fast32 = mode == kModeExact && wave_fast32(tsq, sm.ts.base, sm.ts.wide, &tsr_rel);
+      const bool diag = key0 + BN - 1 > wave_qmin;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) {
-        const f32x16 s = mma_tile_rows<T, D>(kv.k, blk * 32 + r32, qop, g);
-        const f32x16 dp = mma_tile_rows<T, D>(kv.v, blk * 32 + r32, dop, g);
+        const f32x16 s = mma_tile_rows<T, D>(sm.k, blk * 32 + r32, qop, g);
+        const f32x16 dp = mma_tile_rows<T, D>(sm.v, blk * 32 + r32, dop, g);
+        float cb[16];
+        int bsel[16];
+        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, sm.ts, blk, g, tb.w, tb.ep, NB, nb32);
+        float gv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int kj = blk * 32 + acc_row(i, g);
-          const int bk = bucket_of(tsq - kv.ts[kj], p.NB, nb32, tb.e);
-          const float x = fmaf(s[i], p.alpha, tb.w[bk]);
-          const float sg_ = fast_sigmoid(x);
-          float gg = p.alpha * dp[i] * (sg_ * (1.0f + x * (1.0f - sg_)));
-          if (key0 + kj > qpos || !qvalid) gg = 0.0f;
-          gv[blk][i] = gg;
+          const float x = fmaf(s[i], alpha, cb[i]);
+          const float sg = fast_sigmoid(x);
+          float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
+          if (diag && key0 + blk * 32 + acc_row(i, g) > qpos) gg = 0.0f;
+          gv[i] = gg;
         }
+        mma_contract_block<T, D, BN>(dqacc, kBf16 ? sm.kt : sm.k, gv, blk, r32, g);
       }
-      if constexpr (sizeof(T) == 2)
-        mma_contract_rows<T, D, BN>(dqacc, kv.kt, gv, r32, g);
-      else
-        mma_contract_rows<T, D, BN>(dqacc, kv.k, gv, r32, g);
     }
     if (qvalid) store_row_from_acc<T, D>(dQ + qrow * ld + h * D, dqacc, g);
   }
@@ -435,9 +568,9 @@ hipError_t launch_attn(const AttnParams& p, bool bf16, int d, int which, int max
   return bf16 ? launch_d<__bf16>(p, d, which, max_items, cus, s) : launch_d<float>(p, d, which, max_items, cus, s);
 }
 
-int attn_q_tile_rows() { return FwdCfg<float, 128>::BM; }
-int attn_k_tile_keys() { return FwdCfg<float, 128>::BN; }
-int attn_bwd_key_tile() { return BwdKvCfg<float, 128>::BK; }
-int attn_bwd_q_step() { return BwdKvCfg<float, 128>::BQ; }
+int attn_q_tile_rows() { return BM; }
+int attn_k_tile_keys() { return BN; }
+int attn_bwd_key_tile() { return BK; }
+int attn_bwd_q_step() { return BQ; }
 
 }  // namespace hstu

@@ -88,26 +88,25 @@ __device__ __forceinline__ int tslot(int rho) {
 }
 
 // ---------------------------------------------------------------------------
-// Exact timestamp bucket: #{k in [1, NB) : |delta| >= E_k}.  A float estimate
-// floor(NB/32 * log2|delta|) is within one of the exact count (the count equals
-// floor of the real-valued NB*log2|delta|/32 for integer |delta|), and one
-// comparison against each neighbouring integer edge fixes it.  `edges` is the
-// LDS copy of E[0..NB] (E[0] = 0, E[NB] = sentinel).
+// Exact timestamp bucket: #{k in [1, NB) : |delta| >= E_k}.  For integer |delta|
+// the count equals floor(NB/32 * log2|delta|) in exact arithmetic, so a float
+// estimate of that floor is within one of it (the estimate's error is far below
+// one bucket), and one comparison against each neighbouring integer edge fixes
+// it.  `ep[k]` is the LDS pair (E[k], E[k+1]) for k in [0, NB), with E[0] = 0
+// and E[NB] = 0xFFFFFFFF as sentinel.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int bucket_of(int64_t delta, int nb, float nb_over_32,
-                                         const uint32_t* __restrict__ edges) {
+__device__ __forceinline__ int bucket_u32(uint32_t x, int nb, float nb_over_32, const u32x2* __restrict__ ep) {
+  int k = (int)floorf(__log2f(fmaxf((float)x, 1.0f)) * nb_over_32);
+  k = min(max(k, 0), nb - 1);
+  const u32x2 e = ep[k];
+  k += (int)(x >= e.y) - (int)(x < e.x);
+  return min(k, nb - 1);  // only x = 2^32 - 1 reaches the sentinel
+}
+
+__device__ __forceinline__ int bucket_of(int64_t delta, int nb, float nb_over_32, const u32x2* __restrict__ ep) {
   const uint64_t mag = delta < 0 ? (uint64_t)(-delta) : (uint64_t)delta;
   if (mag >> 32) return nb - 1;
-  const uint32_t x = (uint32_t)mag;
-  const float f = fmaxf((float)x, 1.0f);
-  int k = (int)floorf(__log2f(f) * nb_over_32);
-  k = min(max(k, 0), nb - 1);
-  if (x < edges[k]) {
-    --k;
-  } else if (k + 1 < nb && x >= edges[k + 1]) {
-    ++k;
-  }
-  return k;
+  return bucket_u32((uint32_t)mag, nb, nb_over_32, ep);
 }
 
 // SiLU and its derivative, fp32.  sigmoid via exp2 and a hardware reciprocal.

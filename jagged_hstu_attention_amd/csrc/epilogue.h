@@ -1,0 +1,225 @@
+// Timestamp-bias selection for a score tile.
+//
+// Every lane of the attention kernels owns one row r (a query in the forward
+// and dQ passes, a key in the dK/dV pass) and computes, per tile, the scores of
+// its row against the tile's "other" rows o.  The bucket of a pair depends on
+// Δ = ts_query - ts_key (Scaling Generative Recommendations with Context
+// Parallelism on HSTU, §2.1, timestamp-bias paragraph), i.e. Δ = σ (ts_r - ts_o)
+// with σ = +1 when the lane owns the query and σ = -1 when it owns the key.
+//
+// The bucket is a monotone step function of |Δ|.  So, per lane and tile, the
+// range of Δ over the other rows the lane can actually see (causal mask)
+// bounds the buckets it can meet.  If that range crosses n <= 3 bucket edges
+// (and keeps one sign), the bucket of an element is b_lo plus the number of
+// edges it passes, and passing edge t is one compare of the element's 32-bit
+// timestamp offset against a per-lane threshold; the edges are nested, so the
+// bias is a chain of selects.  Otherwise (n > 3, a sign change, or timestamps
+// spread too wide for 32-bit offsets) the exact bucket is computed per element.
+// The wave takes the largest n of its lanes, so branches stay uniform.
+#pragma once
+
+#include "common.h"
+
+namespace hstu {
+
+constexpr int kMaxEdges = 3;   // threshold compares per element before the exact path
+constexpr int kModeExact = kMaxEdges + 1;
+
+// Timestamps of the tile's other rows, staged in LDS.  `lo`/`hi` hold running
+// minima/maxima over valid rows: prefix (element j covers rows 0..j) when the
+// lane owns queries (it sees keys up to its own position), suffix (rows j..N-1)
+// when the lane owns keys (it is seen by queries from its position on).
+template <int N> struct alignas(16) TsTile {
+  int64_t t64[N];
+  int64_t lo[N];
+  int64_t hi[N];
+  int32_t t32[N];   // t64 - base (valid when !wide)
+  int64_t base;
+  int wide;         // some |t64 - base| is 2^30 or more
+};
+
+// Filled by one wave (N == 64): lane j holds the timestamp of row j.
+template <int N, bool SUFFIX>
+__device__ __forceinline__ void ts_tile_fill(TsTile<N>& t, int64_t ts, bool valid, int lane) {
+  static_assert(N == 64, "one wave fills the tile");
+  int64_t vmin = valid ? ts : INT64_MAX;
+  int64_t vmax = valid ? ts : INT64_MIN;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t omin = SUFFIX ? __shfl_down(vmin, off) : __shfl_up(vmin, off);
+    const int64_t omax = SUFFIX ? __shfl_down(vmax, off) : __shfl_up(vmax, off);
+    const bool in = SUFFIX ? (lane + off < 64) : (lane >= off);
+    if (in) {
+      vmin = omin < vmin ? omin : vmin;
+      vmax = omax > vmax ? omax : vmax;
+    }
+  }
+  const int64_t base = __shfl(ts, 0);
+  const int64_t rel = ts - base;
+  const bool fits = !valid || (rel > -(1ll << 30) && rel < (1ll << 30));
+  const bool wide = __ballot(!fits) != 0;
+  t.t64[lane] = valid ? ts : 0;
+  t.lo[lane] = vmin;
+  t.hi[lane] = vmax;
+  t.t32[lane] = (valid && !wide) ? (int32_t)rel : 0;
+  if (lane == 0) {
+    t.base = base;
+    t.wide = wide ? 1 : 0;
+  }
+}
+
+struct LaneBias {
+  float c[kMaxEdges + 1];   // alpha * w[b_lo + k]
+  int32_t thr[kMaxEdges];   // element passes edge t iff (t32 <= thr[t]) != flip
+  int32_t flip;
+  int b_lo;
+  int n;                    // edges crossed (0..kMaxEdges) or kModeExact
+};
+
+__device__ __forceinline__ int32_t clamp_i32(int64_t x) {
+  return (int32_t)(x > 2147483647ll ? 2147483647ll : (x < -2147483647ll - 1 ? -2147483647ll - 1 : x));
+}
+
+// Per-lane bias plan.  tsr: the lane's own timestamp; [tmin, tmax]: range of
+// the other rows it sees (any == false: it sees none, everything is masked).
+template <int SIGMA>
+__device__ __forceinline__ LaneBias lane_bias(int64_t tsr, int64_t tmin, int64_t tmax, bool any, int64_t base,
+                                              int wide, const float* __restrict__ wtab,
+                                              const u32x2* __restrict__ ep, int nb, float nb32) {
+  LaneBias r;
+#pragma unroll
+  for (int t = 0; t <= kMaxEdges; ++t) r.c[t] = 0.0f;
+  r.flip = 0;
+#pragma unroll
+  for (int t = 0; t < kMaxEdges; ++t) r.thr[t] = INT32_MIN;  // never passed (flip == 0)
+  r.b_lo = 0;
+  r.n = 0;
+  if (!any) return r;
+  int64_t dmin, dmax;
+  if (SIGMA > 0) {
+    dmin = tsr - tmax;
+    dmax = tsr - tmin;
+  } else {
+    dmin = tmin - tsr;
+    dmax = tmax - tsr;
+  }
+  int dir;
+  int64_t mlo, mhi;
+  if (dmin >= 0) {
+    dir = 0;
+    mlo = dmin;
+    mhi = dmax;
+  } else if (dmax <= 0) {
+    dir = 1;
+    mlo = -dmax;
+    mhi = -dmin;
+  } else {
+    r.n = kModeExact;
+    return r;
+  }
+  const int blo = bucket_of(mlo, nb, nb32, ep);
+  const int bhi = bucket_of(mhi, nb, nb32, ep);
+  r.b_lo = blo;
+  const int n = bhi - blo;
+  if (n > kMaxEdges || (n > 0 && wide)) {
+    r.n = kModeExact;
+    return r;
+  }
+  r.n = n;
+  // Element |Δ| >= E passes the edge.  With Δ = σ(tsr - tso):
+  //   σ(tsr - tso) >= E  (dir 0) / -σ(tsr - tso) >= E  (dir 1)
+  // reduces to tso <= tsr - E (flip 0) or tso >= tsr + E, i.e. !(tso <= tsr + E - 1) (flip 1).
+  const int flip = SIGMA > 0 ? dir : 1 - dir;
+  r.flip = flip;
+#pragma unroll
+  for (int t = 0; t <= kMaxEdges; ++t) r.c[t] = wtab[min(blo + t, nb - 1)];
+#pragma unroll
+  for (int t = 0; t < kMaxEdges; ++t) {
+    if (t < n) {
+      const int64_t E = (int64_t)ep[blo + t + 1].x;
+      r.thr[t] = clamp_i32((flip ? tsr + E - 1 : tsr - E) - base);
+    } else {
+      r.thr[t] = flip ? INT32_MAX : INT32_MIN;  // never passed
+    }
+  }
+  return r;
+}
+
+// Bias values cb[i] for the 16 accumulator values of one 32-row block of the
+// tile (rows blk*32 + acc_row(i, g)) under wave mode `nw` (the largest n of the
+// wave's lanes).  bsel[i] receives the number of edges passed (threshold modes)
+// or the exact bucket (exact mode).  In exact mode, when every lane of the wave
+// has |tsr - base| < 2^30 (fast32) and the tile is not wide, |Δ| < 2^31 is
+// formed from 32-bit offsets.
+template <int SIGMA, int N>
+__device__ __forceinline__ void block_bias(float* cb, int* bsel, int nw, const LaneBias& lb, int64_t tsr,
+                                           int32_t tsr_rel, bool fast32, const TsTile<N>& t, int blk, int g,
+                                           const float* __restrict__ wtab, const u32x2* __restrict__ ep, int nb,
+                                           float nb32) {
+  if (nw == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      cb[i] = lb.c[0];
+      bsel[i] = 0;
+    }
+  } else if (nw <= kMaxEdges) {
+    const bool fl = lb.flip != 0;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int j0 = blk * 32 + q4 * 8 + 4 * g;
+      const int4 v = *reinterpret_cast<const int4*>(&t.t32[j0]);
+      const int32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool p0 = (vv[u] <= lb.thr[0]) != fl;
+        const bool p1 = (vv[u] <= lb.thr[1]) != fl;
+        const bool p2 = (vv[u] <= lb.thr[2]) != fl;
+        cb[q4 * 4 + u] = p2 ? lb.c[3] : (p1 ? lb.c[2] : (p0 ? lb.c[1] : lb.c[0]));
+        bsel[q4 * 4 + u] = (int)p0 + (int)p1 + (int)p2;
+      }
+    }
+  } else if (fast32) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int j0 = blk * 32 + q4 * 8 + 4 * g;
+      const int4 v = *reinterpret_cast<const int4*>(&t.t32[j0]);
+      const int32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int32_t d = SIGMA > 0 ? tsr_rel - vv[u] : vv[u] - tsr_rel;
+        const int b = bucket_u32((uint32_t)(d < 0 ? -d : d), nb, nb32, ep);
+        cb[q4 * 4 + u] = wtab[b];
+        bsel[q4 * 4 + u] = b;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = blk * 32 + acc_row(i, g);
+      const int64_t d = SIGMA > 0 ? tsr - t.t64[j] : t.t64[j] - tsr;
+      const int b = bucket_of(d, nb, nb32, ep);
+      cb[i] = wtab[b];
+      bsel[i] = b;
+    }
+  }
+}
+
+// Whether the lane's own timestamp is close enough to the tile base for the
+// 32-bit exact path (wave-uniform result).
+__device__ __forceinline__ bool wave_fast32(int64_t tsr, int64_t base, int wide, int32_t* rel) {
+  const int64_t d = tsr - base;
+  const bool ok = d > -(1ll << 30) && d < (1ll << 30);
+  *rel = ok ? (int32_t)d : 0;
+  return !wide && __ballot(!ok) == 0;
+}
+
+// Largest n over the wave's lanes.
+__device__ __forceinline__ int wave_mode(int n) {
+  if (__ballot(n == kModeExact)) return kModeExact;
+  if (__ballot(n == 3)) return 3;
+  if (__ballot(n == 2)) return 2;
+  if (__ballot(n == 1)) return 1;
+  return 0;
+}
+
+}  // namespace hstu

@@ -56,21 +56,27 @@ __device__ __forceinline__ int local_len(const SchedParams& p, int b) {
 }
 
 // Exclusive scan of one value per thread across the block; returns the
-// thread's prefix and writes the block total to *total.
+// thread's prefix and writes the block total to *total.  Wave-level inclusive
+// scans with shuffles, then one pass over the 16 wave totals.
 __device__ int64_t block_scan(int64_t v, int64_t* buf, int64_t* total) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int64_t add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int64_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  const int64_t incl = buf[t];
-  *total = buf[kSchedThreads - 1];
+  if (lane == 63) buf[wave] = incl;
   __syncthreads();
-  return incl - v;
+  int64_t before = 0, all = 0;
+  for (int i = 0; i < kSchedThreads / 64; ++i) {
+    const int64_t x = buf[i];
+    before += i < wave ? x : 0;
+    all += x;
+  }
+  *total = all;
+  __syncthreads();
+  return before + incl - v;
 }
 
 __device__ __forceinline__ int clampc(int64_t c, int hs) { return (int)(c < hs - 1 ? c : hs - 1); }
