@@ -12,14 +12,12 @@
 //
 // Every lane owns one row for the whole item (a query in the forward and dQ
 // passes, a key in the dK/dV pass), so the timestamp of its row, its causal
-// limit and its bias plan (epilogue.h) are per-lane scalars.  Tiles of the
-// other side are loaded into registers one tile ahead and stored to LDS after
-// the previous tile has been consumed.
-#include <type_traits>
-
+// limit and its bias plan (epilogue.h) are per-lane scalars.  The other side
+// streams through double-buffered, swizzled LDS tiles (swtile.h) filled with
+// direct-to-LDS loads one tile ahead; one barrier per tile.
 #include "attn.h"
 #include "epilogue.h"
-#include "tiles.h"
+#include "swtile.h"
 
 namespace hstu {
 
@@ -30,6 +28,7 @@ constexpr int BM = 128;        // query rows per forward / dQ item (32 per wave)
 constexpr int BN = 64;         // keys per tile in the forward / dQ loops
 constexpr int BK = 128;        // keys per dK/dV item (32 per wave)
 constexpr int BQ = 64;         // query rows per step of the dK/dV loop
+static_assert(BQ == BN, "the dK/dV step tiles share the key-tile shape");
 
 // d(ts_weights) bins are kept in kDwCopies interleaved copies (lane l adds to
 // copy l % kDwCopies) so that lanes of one instruction that hit the same bucket
@@ -122,9 +121,6 @@ struct StepIter {
   }
 };
 
-template <typename T, int D, int ROWS>
-using TStageFor = typename std::conditional<sizeof(T) == 2, TStage<D, ROWS, kThreads>, RowStage<T, D, ROWS, kThreads>>::type;
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -132,19 +128,26 @@ using TStageFor = typename std::conditional<sizeof(T) == 2, TStage<D, ROWS, kThr
 // 32w..32w+31 of the tile; lane (r32, g) owns query row 32w + r32: the score
 // tile is computed transposed, Sᵀ = K Qᵀ, so every accumulator value of a lane
 // belongs to its own query, and the output is Oᵀ = Vᵀ Pᵀ with P taken straight
-// from the Sᵀ accumulators.
+// from the Sᵀ accumulators (V read with transpose reads).
 // ---------------------------------------------------------------------------
-template <typename T, int D> struct alignas(16) FwdSmem {
-  T k[BN * Pitch<T, D>::row];
-  T v[sizeof(T) == 2 ? D * TPitch<BN>::col : BN * Pitch<T, D>::row];
-  TsTile<BN> ts;
+template <typename T, int D> struct alignas(16) KvSmem {
+  T k[2][BN * D];
+  T v[2][BN * D];
+  TsTile<BN> ts[2];
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, D >= 128 ? 1 : 2) void fwd_kernel(const AttnParams p) {
+__device__ __forceinline__ void issue_kv(KvSmem<T, D>& sm, int buf, const T* Kh, const T* Vh, int64_t ld, int key0,
+                                         int nvalid, int tid) {
+  tile_load_async<T, D, BN, kThreads>(sm.k[buf], Kh + key0 * ld, ld, nvalid, tid);
+  tile_load_async<T, D, BN, kThreads>(sm.v[buf], Vh + key0 * ld, ld, nvalid, tid);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  __shared__ FwdSmem<T, D> sm;
+  __shared__ KvSmem<T, D> sm;
   __shared__ TablesFwd tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
   const int H = p.H, NB = p.NB;
@@ -185,45 +188,41 @@ __global__ __launch_bounds__(kThreads, D >= 128 ? 1 : 2) void fwd_kernel(const A
     const int wave_qmin = it.pos0 + wave * 32;
     const T* Kh = K + seq0 * ld + h * D;
     const T* Vh = V + seq0 * ld + h * D;
-    RowStage<T, D, BN, kThreads> kst;
-    TStageFor<T, D, BN> vst;
     int64_t tsv = 0;
-    bool tsvalid = false;
-    auto prefetch = [&](int kt) {
-      const int key0 = kt * BN, nvalid = min(BN, kv_len - key0);
-      kst.load(Kh + key0 * ld, ld, nvalid, tid);
-      vst.load(Vh + key0 * ld, ld, nvalid, tid);
-      if (wave == 0) {
-        tsvalid = lane < nvalid;
-        tsv = tsvalid ? p.ts[seq0 + key0 + lane] : 0;
-      }
-    };
-    prefetch(0);
+    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid);
+    if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
+    if (wave == 0) ts_tile_fill<BN, false>(sm.ts[0], tsv, min(BN, kv_len), lane);
+    wait_loads();
+    __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
+      const int cur = kt & 1;
       const int key0 = kt * BN;
       const int nvalid = min(BN, kv_len - key0);
-      __syncthreads();
-      kst.store(sm.k, tid);
-      vst.store(sm.v, tid);
-      if (wave == 0) ts_tile_fill<BN, false>(sm.ts, tsv, tsvalid, lane);
-      __syncthreads();
-      if (kt + 1 < n_kt) prefetch(kt + 1);
+      const bool more = kt + 1 < n_kt;
+      if (more) {
+        const int nk0 = key0 + BN, nnv = min(BN, kv_len - nk0);
+        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid);
+        if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
+      }
+      const T* kt_ = sm.k[cur];
+      const T* vt_ = sm.v[cur];
+      const TsTile<BN>& ts = sm.ts[cur];
 
       const int lim = min(nvalid - 1, qpos - key0);
       const bool any = qvalid && lim >= 0;
-      const int li = any ? lim : 0;
-      const LaneBias lb = lane_bias<+1>(tsq, sm.ts.lo[li], sm.ts.hi[li], any, sm.ts.base, sm.ts.wide, tb.w, tb.ep,
-                                        NB, nb32);
+      int64_t tmin = 0, tmax = 0;
+      ts_tile_range<BN, false>(ts, 0, any ? lim : 0, &tmin, &tmax);
+      const LaneBias lb = lane_bias<+1>(tsq, tmin, tmax, any, ts.base, ts.wide, tb.w, tb.ep, NB, nb32);
       const int mode = wave_mode(lb.n);
       int32_t tsr_rel = 0;
-      const bool fast32 = mode == kModeExact && wave_fast32(tsq, sm.ts.base, sm.ts.wide, &tsr_rel);
+      const bool fast32 = mode == kModeExact && wave_fast32(tsq, ts.base, ts.wide, &tsr_rel);
       const bool diag = key0 + BN - 1 > wave_qmin;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) {
-        const f32x16 s = mma_tile_rows<T, D>(sm.k, blk * 32 + r32, qop, g);
+        const f32x16 s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
         float cb[16];
         int bsel[16];
-        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, sm.ts, blk, g, tb.w, tb.ep, NB, nb32);
+        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
         float pv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -232,8 +231,11 @@ __global__ __launch_bounds__(kThreads, D >= 128 ? 1 : 2) void fwd_kernel(const A
           if (diag && key0 + blk * 32 + acc_row(i, g) > qpos) a = 0.0f;
           pv[i] = a;
         }
-        mma_contract_block<T, D, BN>(oacc, sm.v, pv, blk, r32, g);
+        tile_contract_block<T, D>(oacc, vt_, pv, blk, lane);
       }
+      if (more && wave == 0) ts_tile_fill<BN, false>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane);
+      wait_loads();
+      __syncthreads();
     }
     if (qvalid) store_row_from_acc<T, D>(O + qrow * ld + h * D, oacc, g);
   }
@@ -243,24 +245,15 @@ __global__ __launch_bounds__(kThreads, D >= 128 ? 1 : 2) void fwd_kernel(const A
 // Backward, key-major pass: dK, dV and d(ts_weights).  One item = (key tile of
 // 128 keys, head); lane (r32, g) of wave w owns key 32w + r32.  For each step of
 // 64 query rows it computes S = Q Kᵀ and dP = dO Vᵀ (so the lane's values all
-// belong to its own key), then dVᵀ += dOᵀ P and dKᵀ += Qᵀ G.  Query rows past
-// the end of a step are zero-filled, which makes their P·dO and G terms vanish
-// without a mask.
+// belong to its own key), then dVᵀ += dOᵀ P and dKᵀ += Qᵀ G, reading Q and dO
+// transposed from the same tiles.  Query rows past the end of a step replicate
+// the last row; their P and G are masked to zero.
 // ---------------------------------------------------------------------------
-template <typename T, int D> struct alignas(16) BwdKvSmem {
-  T q[BQ * Pitch<T, D>::row];
-  T dout[BQ * Pitch<T, D>::row];
-  T qt[sizeof(T) == 2 ? D * TPitch<BQ>::col : 8];
-  T doutt[sizeof(T) == 2 ? D * TPitch<BQ>::col : 8];
-  TsTile<BQ> ts;
-};
-
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr bool kBf16 = sizeof(T) == 2;
-  __shared__ BwdKvSmem<T, D> sm;
+  __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
   __shared__ Tables tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
   const int H = p.H, NB = p.NB;
@@ -308,59 +301,47 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
     }
     const int wave_kmax = it.pos0 + wave * 32 + 31;
 
-    RowStage<T, D, BQ, kThreads> qst, dst;
-    TStage<D, BQ, kThreads> qtst, dtst;
     int64_t tsv = 0;
-    bool tsvalid = false;
     StepIter si;
     si.init(p, it.b, it.pos0);
-    auto prefetch = [&](const StepIter& s) {
-      const int nq = s.nq();
-      const int64_t lrow = s.lrow();
-      qst.load(Q + lrow * ld + h * D, ld, nq, tid);
-      dst.load(dO + lrow * ld + h * D, ld, nq, tid);
-      if constexpr (kBf16) {
-        qtst.load(Q + lrow * ld + h * D, ld, nq, tid);
-        dtst.load(dO + lrow * ld + h * D, ld, nq, tid);
-      }
-      if (wave == 0) {
-        tsvalid = lane < nq;
-        tsv = tsvalid ? p.ts[seq0 + s.q0 + lane] : 0;
-      }
-    };
-    if (si.valid()) prefetch(si);
+    int cur = 0;
+    if (si.valid()) {
+      issue_kv<T, D>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid);
+      if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
+      if (wave == 0) ts_tile_fill<BQ, true>(sm.ts[0], tsv, si.nq(), lane);
+    }
+    wait_loads();
+    __syncthreads();
     while (si.valid()) {
       const int q0 = si.q0;
       const int nq = si.nq();
-      __syncthreads();
-      qst.store(sm.q, tid);
-      dst.store(sm.dout, tid);
-      if constexpr (kBf16) {
-        qtst.store(sm.qt, tid);
-        dtst.store(sm.doutt, tid);
+      StepIter nx = si;
+      nx.next();
+      if (nx.valid()) {
+        issue_kv<T, D>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid);
+        if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
       }
-      if (wave == 0) ts_tile_fill<BQ, true>(sm.ts, tsv, tsvalid, lane);
-      __syncthreads();
-      si.next();
-      if (si.valid()) prefetch(si);
+      const T* qt_ = sm.k[cur];
+      const T* dt_ = sm.v[cur];
+      const TsTile<BQ>& ts = sm.ts[cur];
 
       const int first = max(0, kpos - q0);
       const bool any = kvalid && first < nq;
-      const int fi = any ? first : 0;
-      const LaneBias lb = lane_bias<-1>(tsk, sm.ts.lo[fi], sm.ts.hi[fi], any, sm.ts.base, sm.ts.wide, tb.w, tb.ep,
-                                        NB, nb32);
+      int64_t tmin = 0, tmax = 0;
+      ts_tile_range<BQ, true>(ts, any ? first : BQ - 1, BQ - 1, &tmin, &tmax);
+      const LaneBias lb = lane_bias<-1>(tsk, tmin, tmax, any, ts.base, ts.wide, tb.w, tb.ep, NB, nb32);
       const int mode = wave_mode(lb.n);
       int32_t tsr_rel = 0;
-      const bool fast32 = mode == kModeExact && wave_fast32(tsk, sm.ts.base, sm.ts.wide, &tsr_rel);
-      const bool needmask = q0 < wave_kmax;
+      const bool fast32 = mode == kModeExact && wave_fast32(tsk, ts.base, ts.wide, &tsr_rel);
+      const bool needmask = q0 < wave_kmax || nq < BQ;
       float dwb[kMaxEdges + 1] = {0.0f, 0.0f, 0.0f, 0.0f};  // bins b_lo + k
 #pragma unroll
       for (int blk = 0; blk < BQ / 32; ++blk) {
-        const f32x16 s = mma_tile_rows<T, D>(sm.q, blk * 32 + r32, kop, g);
-        const f32x16 dp = mma_tile_rows<T, D>(sm.dout, blk * 32 + r32, vop, g);
+        const f32x16 s = tile_mma_rows<T, D>(qt_, blk * 32 + r32, kop, g);
+        const f32x16 dp = tile_mma_rows<T, D>(dt_, blk * 32 + r32, vop, g);
         float cb[16];
         int bsel[16];
-        block_bias<-1, BQ>(cb, bsel, mode, lb, tsk, tsr_rel, fast32, sm.ts, blk, g, tb.w, tb.ep, NB, nb32);
+        block_bias<-1, BQ>(cb, bsel, mode, lb, tsk, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
         float pv[16], gv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -368,7 +349,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
           const float sg = fast_sigmoid(x);
           float a = x * sg;
           float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
-          if (needmask && q0 + blk * 32 + acc_row(i, g) < kpos) {
+          const int qj = blk * 32 + acc_row(i, g);
+          if (needmask && (q0 + qj < kpos || qj >= nq)) {
             a = 0.0f;
             gg = 0.0f;
           }
@@ -382,20 +364,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
               if (k <= mode) dwb[k] += bsel[i] == k ? gg : 0.0f;
           }
         }
-        mma_contract_block<T, D, BQ>(dvacc, kBf16 ? sm.doutt : sm.dout, pv, blk, r32, g);
-        mma_contract_block<T, D, BQ>(dkacc, kBf16 ? sm.qt : sm.q, gv, blk, r32, g);
+        tile_contract_block<T, D>(dvacc, dt_, pv, blk, lane);
+        tile_contract_block<T, D>(dkacc, qt_, gv, blk, lane);
       }
       if (mode != kModeExact) {
 #pragma unroll
         for (int k = 0; k <= kMaxEdges; ++k)
           if (dwb[k] != 0.0f) atomicAdd(&dwl[lb.b_lo + k], dwb[k]);
       }
+      if (nx.valid() && wave == 0) ts_tile_fill<BQ, true>(sm.ts[cur ^ 1], tsv, nx.nq(), lane);
+      wait_loads();
+      __syncthreads();
+      si = nx;
+      cur ^= 1;
     }
     if (kvalid) {
       store_row_from_acc<T, D>(dK + krow * ld + h * D, dkacc, g);
       store_row_from_acc<T, D>(dV + krow * ld + h * D, dvacc, g);
     }
-    __syncthreads();
     for (int i = tid; i < NB; i += kThreads) {
       float v = 0.0f;
 #pragma unroll
@@ -407,21 +393,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
 
 // ---------------------------------------------------------------------------
 // Backward, query-major pass: dQ.  Same item list and lane ownership as the
-// forward; Sᵀ = K Qᵀ and dPᵀ = V dOᵀ are recomputed and dQᵀ += Kᵀ Gᵀ.
+// forward; Sᵀ = K Qᵀ and dPᵀ = V dOᵀ are recomputed and dQᵀ += Kᵀ Gᵀ (K read
+// transposed from the same tile).
 // ---------------------------------------------------------------------------
-template <typename T, int D> struct alignas(16) BwdQSmem {
-  T k[BN * Pitch<T, D>::row];
-  T v[BN * Pitch<T, D>::row];
-  T kt[sizeof(T) == 2 ? D * TPitch<BN>::col : 8];
-  TsTile<BN> ts;
-};
-
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_q_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr bool kBf16 = sizeof(T) == 2;
-  __shared__ BwdQSmem<T, D> sm;
+  __shared__ KvSmem<T, D> sm;
   __shared__ TablesFwd tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
   const int H = p.H, NB = p.NB;
@@ -467,48 +446,42 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_q_kernel(const AttnParams p) 
     const int wave_qmin = it.pos0 + wave * 32;
     const T* Kh = K + seq0 * ld + h * D;
     const T* Vh = V + seq0 * ld + h * D;
-    RowStage<T, D, BN, kThreads> kst, vst;
-    TStage<D, BN, kThreads> ktst;
     int64_t tsv = 0;
-    bool tsvalid = false;
-    auto prefetch = [&](int kt) {
-      const int key0 = kt * BN, nvalid = min(BN, kv_len - key0);
-      kst.load(Kh + key0 * ld, ld, nvalid, tid);
-      vst.load(Vh + key0 * ld, ld, nvalid, tid);
-      if constexpr (kBf16) ktst.load(Kh + key0 * ld, ld, nvalid, tid);
-      if (wave == 0) {
-        tsvalid = lane < nvalid;
-        tsv = tsvalid ? p.ts[seq0 + key0 + lane] : 0;
-      }
-    };
-    prefetch(0);
+    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid);
+    if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
+    if (wave == 0) ts_tile_fill<BN, false>(sm.ts[0], tsv, min(BN, kv_len), lane);
+    wait_loads();
+    __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
+      const int cur = kt & 1;
       const int key0 = kt * BN;
       const int nvalid = min(BN, kv_len - key0);
-      __syncthreads();
-      kst.store(sm.k, tid);
-      vst.store(sm.v, tid);
-      if constexpr (kBf16) ktst.store(sm.kt, tid);
-      if (wave == 0) ts_tile_fill<BN, false>(sm.ts, tsv, tsvalid, lane);
-      __syncthreads();
-      if (kt + 1 < n_kt) prefetch(kt + 1);
+      const bool more = kt + 1 < n_kt;
+      if (more) {
+        const int nk0 = key0 + BN, nnv = min(BN, kv_len - nk0);
+        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid);
+        if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
+      }
+      const T* kt_ = sm.k[cur];
+      const T* vt_ = sm.v[cur];
+      const TsTile<BN>& ts = sm.ts[cur];
 
       const int lim = min(nvalid - 1, qpos - key0);
       const bool any = qvalid && lim >= 0;
-      const int li = any ? lim : 0;
-      const LaneBias lb = lane_bias<+1>(tsq, sm.ts.lo[li], sm.ts.hi[li], any, sm.ts.base, sm.ts.wide, tb.w, tb.ep,
-                                        NB, nb32);
+      int64_t tmin = 0, tmax = 0;
+      ts_tile_range<BN, false>(ts, 0, any ? lim : 0, &tmin, &tmax);
+      const LaneBias lb = lane_bias<+1>(tsq, tmin, tmax, any, ts.base, ts.wide, tb.w, tb.ep, NB, nb32);
       const int mode = wave_mode(lb.n);
       int32_t tsr_rel = 0;
-      const bool fast32 = mode == kModeExact && wave_fast32(tsq, sm.ts.base, sm.ts.wide, &tsr_rel);
+      const bool fast32 = mode == kModeExact && wave_fast32(tsq, ts.base, ts.wide, &tsr_rel);
       const bool diag = key0 + BN - 1 > wave_qmin;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) {
-        const f32x16 s = mma_tile_rows<T, D>(sm.k, blk * 32 + r32, qop, g);
-        const f32x16 dp = mma_tile_rows<T, D>(sm.v, blk * 32 + r32, dop, g);
+        const f32x16 s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
+        const f32x16 dp = tile_mma_rows<T, D>(vt_, blk * 32 + r32, dop, g);
         float cb[16];
         int bsel[16];
-        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, sm.ts, blk, g, tb.w, tb.ep, NB, nb32);
+        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
         float gv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -518,8 +491,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_q_kernel(const AttnParams p) 
           if (diag && key0 + blk * 32 + acc_row(i, g) > qpos) gg = 0.0f;
           gv[i] = gg;
         }
-        mma_contract_block<T, D, BN>(dqacc, kBf16 ? sm.kt : sm.k, gv, blk, r32, g);
+        tile_contract_block<T, D>(dqacc, kt_, gv, blk, lane);
       }
+      if (more && wave == 0) ts_tile_fill<BN, false>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane);
+      wait_loads();
+      __syncthreads();
     }
     if (qvalid) store_row_from_acc<T, D>(dQ + qrow * ld + h * D, dqacc, g);
   }

@@ -71,23 +71,6 @@ template <> struct Mma<float> {
 __device__ __forceinline__ int acc_row(int i, int g) { return ((i >> 2) << 3) + (g << 2) + (i & 3); }
 
 // ---------------------------------------------------------------------------
-// Transposed bf16 tiles.  A product that contracts over rows of a row-major
-// tile (P·V over keys, Gᵀ·Q over queries, ...) needs, per lane, 8 values of one
-// column taken from 8 different rows.  Such tiles are stored transposed in LDS
-// ([col][row]) with the rows of each 32-row block permuted so that the 8 rows
-// one lane needs are adjacent: row ρ of a block sits at slot
-//   16*u + 8*g + j  with  i = 4*(ρ/8) + ρ%4,  u = i/8,  j = i%8,  g = (ρ/4)%2,
-// which is exactly the order in which accumulator values i of lane group g
-// enumerate rows (acc_row above).  Four consecutive rows 4m..4m+3 land in four
-// consecutive slots, so the tile can be written with 8-byte stores.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int tslot(int rho) {
-  const int blk = rho >> 5, r = rho & 31;
-  const int i = ((r >> 3) << 2) + (r & 3);
-  return (blk << 5) + ((i >> 3) << 4) + (((r >> 2) & 1) << 3) + (i & 7);
-}
-
-// ---------------------------------------------------------------------------
 // Exact timestamp bucket: #{k in [1, NB) : |delta| >= E_k}.  For integer |delta|
 // the count equals floor(NB/32 * log2|delta|) in exact arithmetic, so a float
 // estimate of that floor is within one of it (the estimate's error is far below

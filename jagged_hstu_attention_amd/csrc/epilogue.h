@@ -25,10 +25,13 @@ namespace hstu {
 constexpr int kMaxEdges = 3;   // threshold compares per element before the exact path
 constexpr int kModeExact = kMaxEdges + 1;
 
-// Timestamps of the tile's other rows, staged in LDS.  `lo`/`hi` hold running
-// minima/maxima over valid rows: prefix (element j covers rows 0..j) when the
-// lane owns queries (it sees keys up to its own position), suffix (rows j..N-1)
-// when the lane owns keys (it is seen by queries from its position on).
+// Timestamps of the tile's other rows, staged in LDS.  Rows past the last
+// valid one repeat its timestamp.  The range of timestamps a lane sees is a
+// prefix (rows 0..j: the lane owns a query and sees keys up to its position)
+// or a suffix (rows j..N-1: the lane owns a key, seen by queries from its
+// position on).  For non-decreasing timestamps (the usual case, flagged
+// `sorted`) the range is read off t64 directly; otherwise `lo`/`hi` hold the
+// running minima/maxima.
 template <int N> struct alignas(16) TsTile {
   int64_t t64[N];
   int64_t lo[N];
@@ -36,35 +39,56 @@ template <int N> struct alignas(16) TsTile {
   int32_t t32[N];   // t64 - base (valid when !wide)
   int64_t base;
   int wide;         // some |t64 - base| is 2^30 or more
+  int sorted;       // t64 is non-decreasing
 };
 
-// Filled by one wave (N == 64): lane j holds the timestamp of row j.
+// Filled by one wave (N == 64): lane j holds the timestamp of row j; rows
+// >= nvalid (nvalid >= 1) are invalid.
 template <int N, bool SUFFIX>
-__device__ __forceinline__ void ts_tile_fill(TsTile<N>& t, int64_t ts, bool valid, int lane) {
+__device__ __forceinline__ void ts_tile_fill(TsTile<N>& t, int64_t ts, int nvalid, int lane) {
   static_assert(N == 64, "one wave fills the tile");
-  int64_t vmin = valid ? ts : INT64_MAX;
-  int64_t vmax = valid ? ts : INT64_MIN;
+  const int64_t last = __shfl(ts, nvalid - 1);
+  const int64_t v = lane < nvalid ? ts : last;
+  const int64_t prev = __shfl_up(v, 1);
+  const bool sorted = __ballot(lane > 0 && v < prev) == 0;
+  const int64_t base = __shfl(v, 0);
+  const int64_t rel = v - base;
+  const bool wide = __ballot(rel <= -(1ll << 30) || rel >= (1ll << 30)) != 0;
+  t.t64[lane] = v;
+  t.t32[lane] = wide ? 0 : (int32_t)rel;
+  if (!sorted) {
+    int64_t vmin = v, vmax = v;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t omin = SUFFIX ? __shfl_down(vmin, off) : __shfl_up(vmin, off);
-    const int64_t omax = SUFFIX ? __shfl_down(vmax, off) : __shfl_up(vmax, off);
-    const bool in = SUFFIX ? (lane + off < 64) : (lane >= off);
-    if (in) {
-      vmin = omin < vmin ? omin : vmin;
-      vmax = omax > vmax ? omax : vmax;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t omin = SUFFIX ? __shfl_down(vmin, off) : __shfl_up(vmin, off);
+      const int64_t omax = SUFFIX ? __shfl_down(vmax, off) : __shfl_up(vmax, off);
+      const bool in = SUFFIX ? (lane + off < 64) : (lane >= off);
+      if (in) {
+        vmin = omin < vmin ? omin : vmin;
+        vmax = omax > vmax ? omax : vmax;
+      }
     }
+    t.lo[lane] = vmin;
+    t.hi[lane] = vmax;
   }
-  const int64_t base = __shfl(ts, 0);
-  const int64_t rel = ts - base;
-  const bool fits = !valid || (rel > -(1ll << 30) && rel < (1ll << 30));
-  const bool wide = __ballot(!fits) != 0;
-  t.t64[lane] = valid ? ts : 0;
-  t.lo[lane] = vmin;
-  t.hi[lane] = vmax;
-  t.t32[lane] = (valid && !wide) ? (int32_t)rel : 0;
   if (lane == 0) {
     t.base = base;
     t.wide = wide ? 1 : 0;
+    t.sorted = sorted ? 1 : 0;
+  }
+}
+
+// Range of timestamps over rows [a, b] of the tile (a <= b): a prefix range
+// (a == 0) for SUFFIX == false, a suffix range (b == N-1) for SUFFIX == true.
+template <int N, bool SUFFIX>
+__device__ __forceinline__ void ts_tile_range(const TsTile<N>& t, int a, int b, int64_t* tmin, int64_t* tmax) {
+  if (t.sorted) {
+    *tmin = t.t64[a];
+    *tmax = t.t64[b];
+  } else {
+    const int j = SUFFIX ? a : b;
+    *tmin = t.lo[j];
+    *tmax = t.hi[j];
   }
 }
 
