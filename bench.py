@@ -114,6 +114,64 @@ class Case:
         self.bwd()
 
 
+def kernel_flops(pairs, heads, dqk, dv):
+    """Algorithmic FLOPs per launch of each attention kernel.  The dK/dV pass
+    computes S, dP, dV and dK; the dQ pass is credited with dQ only (its S and
+    dP are recomputation).  fwd + bwd_kv + bwd_q equals the counted total."""
+    return {"fwd": 2 * (dqk + dv) * pairs * heads,
+            "bwd_kv": 4 * (dqk + dv) * pairs * heads,
+            "bwd_q": 2 * dqk * pairs * heads}
+
+
+def source_digest():
+    """sha256 over the kernel sources (to tell whether stored counters are current)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "jagged_hstu_attention_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, or None when it
+    is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_len3072.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def time_kernels(case, steps):
+    """Per-kernel average milliseconds, from HIP events the library records on
+    the launch stream around each kernel (one forward + one backward per call)."""
+    import torch
+    m = case.m
+    torch.cuda.synchronize()
+    m.timing_reset()
+    m.timing_enable(True)
+    for _ in range(steps):
+        case.fwd()
+        case.bwd()
+    torch.cuda.synchronize()
+    m.timing_enable(False)
+    out = {}
+    for k in ("sched", "fwd", "bwd_kv", "bwd_q"):
+        ms, n = m.timing_read(k)
+        out[k] = ms / max(n, 1)
+    m.timing_reset()
+    return out
+
+
 def time_loop(fn, steps, warmup):
     """Average ms per call over `steps` calls, bracketed by HIP events on the
     current stream (the stream every launch goes to)."""
@@ -206,6 +264,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="for rocprofv3 --pmc: a 256 MiB device copy (calibration), then 3 forward+backward "
+                         "steps of the 3072-length workload; no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -218,6 +279,17 @@ def main():
 
     m._lib.load()
     torch.cuda.set_device(0)
+    if args.counter_run:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        case = Case(synth.config("bf16_len3072"))
+        for _ in range(3):
+            case.step()
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_run": True, "copy_bytes": src.numel()}), flush=True)
+        return
     log("uploading the 3072-length workload")
     wl = synth.config("bf16_len3072")
     case = Case(wl)
@@ -232,18 +304,21 @@ def main():
     ms_fwd = time_loop(case.fwd, args.steps, 2)
     ms_bwd = time_loop(case.bwd, args.steps, 2)
     log(f"forward {ms_fwd:.3f} ms, backward {ms_bwd:.3f} ms")
-    if ms_bwd >= ms_fwd:
-        dom_name, dom_ms, dom_flops = "backward (hstu_jagged_attn_bwd: bwd_kernel)", ms_bwd, f_bwd
-    else:
-        dom_name, dom_ms, dom_flops = "forward (hstu_jagged_attn_fwd: fwd_kernel)", ms_fwd, f_fwd
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    kms = time_kernels(case, args.steps)
+    kfl = kernel_flops(pairs, wl.num_heads, wl.d_qk, wl.d_v)
+    log("per kernel (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in kms.items()))
+    dom = max(("fwd", "bwd_kv", "bwd_q"), key=lambda k: kms[k])
+    achieved = kfl[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom_name,
-                "ms_per_launch": round(dom_ms, 4)}
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(dom),
+                "kernel": {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_kernel", "bwd_q": "bwd_q_kernel"}[dom],
+                "ms_per_launch": round(kms[dom], 4), "flop_per_launch": kfl[dom]}
 
     extra = {
         "len3072_forward": {"ms": round(ms_fwd, 4), "tflops": round(f_fwd / ms_fwd / 1e9, 2)},
         "len3072_backward": {"ms": round(ms_bwd, 4), "tflops": round(f_bwd / ms_bwd / 1e9, 2)},
+        "len3072_kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "len3072_kernels_tflops": {k: round(kfl[k] / kms[k] / 1e9, 2) for k in kfl},
     }
     if not args.no_extra:
         del case

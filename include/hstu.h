@@ -140,6 +140,25 @@ int hstu_bucket_edges(int64_t num_buckets, uint32_t* edges_out);
 /* Message for the last non-OK status returned on the calling thread. */
 const char* hstu_last_error(void);
 
+/* Optional per-kernel timing, for profiling.  While enabled, every kernel this
+ * library launches is bracketed by two HIP events recorded on the launch
+ * stream (so the measured interval is that kernel's execution on its stream).
+ * hstu_timing_read waits for the recorded events (host-blocking) and returns
+ * the milliseconds and launch count accumulated for one kernel since the last
+ * hstu_timing_reset.  Off by default; the events are created and destroyed by
+ * the library (no device memory).  Not for use inside a stream capture. */
+typedef enum {
+  HSTU_KERNEL_SCHED = 0,    /* tile scheduler (one workgroup) */
+  HSTU_KERNEL_FWD = 1,      /* forward attention */
+  HSTU_KERNEL_BWD_KV = 2,   /* backward, key-major pass: dK, dV, d(ts_weights) */
+  HSTU_KERNEL_BWD_Q = 3,    /* backward, query-major pass: dQ */
+  HSTU_KERNEL_REORDER = 4,  /* chunk-pair reorder */
+  HSTU_KERNEL_COUNT = 5
+} hstu_kernel_t;
+int hstu_timing_enable(int on);
+int hstu_timing_reset(void);
+int hstu_timing_read(int kernel, double* total_ms /* host */, int64_t* launches /* host */);
+
 /* Library version: major * 10000 + minor * 100 + patch. */
 int hstu_version(void);
 

@@ -24,7 +24,7 @@ from ._lib import HSTU_BF16, HSTU_FP32, HstuError, Problem  # noqa: F401
 
 __all__ = [
     "Problem", "HstuError", "problem", "workspace_size", "jagged_attn_fwd", "jagged_attn_bwd",
-    "cp_reorder", "bucket_edges", "version", "library_path",
+    "cp_reorder", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
 ]
 
 
@@ -152,3 +152,21 @@ def bucket_edges(num_buckets: int):
     arr = (ctypes.c_uint32 * (num_buckets + 1))()
     _lib.check(_lib.load().hstu_bucket_edges(int(num_buckets), arr))
     return list(arr)
+
+
+def timing_enable(on: bool = True) -> None:
+    """Record HIP events around every kernel launch (per-kernel timing)."""
+    _lib.check(_lib.load().hstu_timing_enable(1 if on else 0))
+
+
+def timing_reset() -> None:
+    _lib.check(_lib.load().hstu_timing_reset())
+
+
+def timing_read(kernel: str):
+    """(total milliseconds, launches) accumulated for one kernel since the last
+    reset; kernel is one of sched, fwd, bwd_kv, bwd_q, reorder."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _lib.check(_lib.load().hstu_timing_read(_lib.KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -43,7 +43,12 @@ EXPORTS = [
     "hstu_bucket_edges",
     "hstu_last_error",
     "hstu_version",
+    "hstu_timing_enable",
+    "hstu_timing_reset",
+    "hstu_timing_read",
 ]
+
+KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4}
 
 _lib = None
 
@@ -79,6 +84,12 @@ def load() -> ctypes.CDLL:
     lib.hstu_last_error.restype = ctypes.c_char_p
     lib.hstu_version.argtypes = []
     lib.hstu_version.restype = ctypes.c_int
+    lib.hstu_timing_enable.argtypes = [ctypes.c_int]
+    lib.hstu_timing_enable.restype = ctypes.c_int
+    lib.hstu_timing_reset.argtypes = []
+    lib.hstu_timing_reset.restype = ctypes.c_int
+    lib.hstu_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.hstu_timing_read.restype = ctypes.c_int
     _lib = lib
     return lib
 

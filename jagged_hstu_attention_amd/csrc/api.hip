@@ -210,6 +210,53 @@ int validate(const hstu_problem_t* p) {
     if (((uintptr_t)(ptr) & 7) != 0) return fail(HSTU_EINVAL, "%s is not 8-byte aligned", name); \
   } while (0)
 
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing (hstu_timing_*): events recorded on the launch
+// stream around each launch; resolved when read.
+// ---------------------------------------------------------------------------
+struct TimingRec {
+  int kernel;
+  hipEvent_t start, stop;
+};
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimingRec> pending;
+  double ms[HSTU_KERNEL_COUNT] = {};
+  int64_t launches[HSTU_KERNEL_COUNT] = {};
+};
+Timing g_timing;
+
+template <class F>
+hipError_t timed(int kernel, hipStream_t s, F&& launch) {
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on) return launch();
+  }
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
+  hipEventRecord(a, s);
+  const hipError_t e = launch();
+  hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.pending.push_back(TimingRec{kernel, a, b});
+  return e;
+}
+
+void timing_resolve_locked() {
+  for (auto& r : g_timing.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      g_timing.ms[r.kernel] += ms;
+      g_timing.launches[r.kernel] += 1;
+    }
+    hipEventDestroy(r.start);
+    hipEventDestroy(r.stop);
+  }
+  g_timing.pending.clear();
+}
+
+
 int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, char* ws, float* dw,
              hipStream_t s, bool backward) {
   hstu::SchedParams sp{};
@@ -234,7 +281,7 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   sp.NB = (int)p->num_buckets;
   hstu::EdgeArg edges;
   get_edges(p->num_buckets, &edges);
-  const hipError_t e = hstu::launch_sched(sp, edges, s);
+  const hipError_t e = timed(HSTU_KERNEL_SCHED, s, [&] { return hstu::launch_sched(sp, edges, s); });
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
   return HSTU_OK;
 }
@@ -254,11 +301,38 @@ hstu::AttnParams attn_params(const hstu_problem_t* p, const Layout& l, char* ws)
   return a;
 }
 
+
 }  // namespace
 
 extern "C" {
 
 int hstu_version(void) { return 100; }
+
+int hstu_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  return HSTU_OK;
+}
+
+int hstu_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  timing_resolve_locked();
+  for (int i = 0; i < HSTU_KERNEL_COUNT; ++i) {
+    g_timing.ms[i] = 0.0;
+    g_timing.launches[i] = 0;
+  }
+  return HSTU_OK;
+}
+
+int hstu_timing_read(int kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= HSTU_KERNEL_COUNT) return fail(HSTU_EINVAL, "kernel id %d out of range", kernel);
+  if (!total_ms || !launches) return fail(HSTU_EINVAL, "output pointer is NULL");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  timing_resolve_locked();
+  *total_ms = g_timing.ms[kernel];
+  *launches = g_timing.launches[kernel];
+  return HSTU_OK;
+}
 
 const char* hstu_last_error(void) { return g_last_error.c_str(); }
 
@@ -309,7 +383,9 @@ int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, 
   a.w = ts_weights;
   a.out = out;
   const int max_items = (int)(l.max_qtiles * p->num_heads);
-  const hipError_t e = hstu::launch_attn(a, p->dtype == HSTU_BF16, (int)p->d_qk, 0, max_items, cu_count(), s);
+  const hipError_t e = timed(HSTU_KERNEL_FWD, s, [&] {
+    return hstu::launch_attn(a, p->dtype == HSTU_BF16, (int)p->d_qk, 0, max_items, cu_count(), s);
+  });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return HSTU_OK;
 }
@@ -363,10 +439,14 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
   a.dv = dv;
   a.dw = d_ts_weights;
   const bool bf16 = p->dtype == HSTU_BF16;
-  hipError_t e = hstu::launch_attn(a, bf16, (int)p->d_qk, 1, (int)(l.max_ktiles * p->num_heads), cu_count(), s);
+  hipError_t e = timed(HSTU_KERNEL_BWD_KV, s, [&] {
+    return hstu::launch_attn(a, bf16, (int)p->d_qk, 1, (int)(l.max_ktiles * p->num_heads), cu_count(), s);
+  });
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
   if (p->total_q > 0) {
-    e = hstu::launch_attn(a, bf16, (int)p->d_qk, 2, (int)(l.max_qtiles * p->num_heads), cu_count(), s);
+    e = timed(HSTU_KERNEL_BWD_Q, s, [&] {
+      return hstu::launch_attn(a, bf16, (int)p->d_qk, 2, (int)(l.max_qtiles * p->num_heads), cu_count(), s);
+    });
     if (e != hipSuccess) return hip_fail(e, "dQ launch");
   }
   return HSTU_OK;
@@ -395,8 +475,11 @@ int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t*
   const int64_t nch = 2 * cp_size;
   const int64_t max_pair_bytes = 2 * ((max_seq_len + nch - 1) / nch) * row_bytes;
   if (max_pair_bytes / (64 * 1024) >= 65535) return fail(HSTU_EUNSUPPORTED, "sequence too long for the reorder grid");
-  const hipError_t e = hstu::launch_reorder(in, out, row_bytes, offsets, num_seqs, total_rows, max_seq_len,
-                                            (int)cp_size, inverse != 0, out_offsets, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(HSTU_KERNEL_REORDER, s, [&] {
+    return hstu::launch_reorder(in, out, row_bytes, offsets, num_seqs, total_rows, max_seq_len, (int)cp_size,
+                                inverse != 0, out_offsets, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "reorder launch");
   return HSTU_OK;
 }

@@ -92,29 +92,43 @@ __device__ __forceinline__ int q_segments(const AttnParams& p, int b, Seg* seg) 
   return 2;
 }
 
-// Steps of BQ query rows, over the segments, from position `start` on.
+// Steps of BQ query rows, over the (at most two) segments, from position
+// `start` on.  Segments are held in scalar fields (selected by index) so that
+// the iterator stays in registers.
 struct StepIter {
-  Seg seg[2];
+  int64_t r0, r1;  // local row of each segment's first position
+  int p0, p1;      // first position of each segment
+  int e0, e1;      // end position of each segment
   int nseg;
   int start;
   int si;
   int q0;
+  __device__ __forceinline__ int seg_pos(int i) const { return i == 0 ? p0 : p1; }
+  __device__ __forceinline__ int seg_end(int i) const { return i == 0 ? e0 : e1; }
   __device__ __forceinline__ void norm() {
-    while (si < nseg && q0 >= seg[si].pos0 + seg[si].len) {
-      ++si;
-      if (si < nseg) q0 = max(seg[si].pos0, start);
+    if (si == 0 && q0 >= e0) {
+      si = 1;
+      q0 = max(p1, start);
     }
+    if (si == 1 && (nseg < 2 || q0 >= e1)) si = 2;
   }
   __device__ __forceinline__ void init(const AttnParams& p, int b, int start_pos) {
+    Seg seg[2];
     nseg = q_segments(p, b, seg);
+    r0 = seg[0].row0;
+    p0 = seg[0].pos0;
+    e0 = seg[0].pos0 + seg[0].len;
+    r1 = nseg > 1 ? seg[1].row0 : 0;
+    p1 = nseg > 1 ? seg[1].pos0 : 0;
+    e1 = nseg > 1 ? seg[1].pos0 + seg[1].len : 0;
     start = start_pos;
     si = 0;
-    q0 = max(seg[0].pos0, start);
+    q0 = max(p0, start);
     norm();
   }
   __device__ __forceinline__ bool valid() const { return si < nseg; }
-  __device__ __forceinline__ int nq() const { return min(BQ, seg[si].pos0 + seg[si].len - q0); }
-  __device__ __forceinline__ int64_t lrow() const { return seg[si].row0 + (q0 - seg[si].pos0); }
+  __device__ __forceinline__ int nq() const { return min(BQ, seg_end(si) - q0); }
+  __device__ __forceinline__ int64_t lrow() const { return (si == 0 ? r0 : r1) + (q0 - seg_pos(si)); }
   __device__ __forceinline__ void next() {
     q0 += BQ;
     norm();
@@ -147,9 +161,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
+  constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ KvSmem<T, D> sm;
   __shared__ TablesFwd tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
+  LaneOffsets<D> lo;
+  if constexpr (kBf16) lo.init(lane);
   const int H = p.H, NB = p.NB;
   const float nb32 = NB * (1.0f / 32.0f);
   const float alpha = p.alpha;
@@ -219,19 +236,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
       const bool diag = key0 + BN - 1 > wave_qmin;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) {
-        const f32x16 s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
+        f32x16 s;
+        if constexpr (kBf16)
+          s = tile_mma_rows_o<D>(reinterpret_cast<const char*>(kt_), lo, blk, qop);
+        else
+          s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
         float cb[16];
         int bsel[16];
         block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
         float pv[16];
+        if (diag) {
+          const int lim_row = qpos - key0 - blk * 32;  // values with row > lim_row are masked
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = fmaf(s[i], alpha, cb[i]);
-          float a = x * fast_sigmoid(x);
-          if (diag && key0 + blk * 32 + acc_row(i, g) > qpos) a = 0.0f;
-          pv[i] = a;
+          for (int i = 0; i < 16; ++i) {
+            const float x = fmaf(s[i], alpha, cb[i]);
+            const float a = x * fast_sigmoid(x);
+            pv[i] = acc_row(i, g) > lim_row ? 0.0f : a;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = fmaf(s[i], alpha, cb[i]);
+            pv[i] = x * fast_sigmoid(x);
+          }
         }
-        tile_contract_block<T, D>(oacc, vt_, pv, blk, lane);
+        if constexpr (kBf16)
+          tile_contract_block_o<D>(oacc, reinterpret_cast<const char*>(vt_), lo, pv, blk);
+        else
+          tile_contract_block<T, D>(oacc, vt_, pv, blk, lane);
       }
       if (more && wave == 0) ts_tile_fill<BN, false>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane);
       wait_loads();
@@ -253,9 +285,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
+  constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
   __shared__ Tables tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
+  LaneOffsets<D> lo;
+  if constexpr (kBf16) lo.init(lane);
   const int H = p.H, NB = p.NB;
   const float nb32 = NB * (1.0f / 32.0f);
   const float alpha = p.alpha;
@@ -337,22 +372,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
       float dwb[kMaxEdges + 1] = {0.0f, 0.0f, 0.0f, 0.0f};  // bins b_lo + k
 #pragma unroll
       for (int blk = 0; blk < BQ / 32; ++blk) {
-        const f32x16 s = tile_mma_rows<T, D>(qt_, blk * 32 + r32, kop, g);
-        const f32x16 dp = tile_mma_rows<T, D>(dt_, blk * 32 + r32, vop, g);
+        f32x16 s, dp;
+        if constexpr (kBf16) {
+          s = tile_mma_rows_o<D>(reinterpret_cast<const char*>(qt_), lo, blk, kop);
+          dp = tile_mma_rows_o<D>(reinterpret_cast<const char*>(dt_), lo, blk, vop);
+        } else {
+          s = tile_mma_rows<T, D>(qt_, blk * 32 + r32, kop, g);
+          dp = tile_mma_rows<T, D>(dt_, blk * 32 + r32, vop, g);
+        }
         float cb[16];
         int bsel[16];
         block_bias<-1, BQ>(cb, bsel, mode, lb, tsk, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
         float pv[16], gv[16];
+        // query row qj is visible iff kpos <= q0 + qj and qj < nq
+        const int lo_row = kpos - q0 - blk * 32, hi_row = nq - blk * 32;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float x = fmaf(s[i], alpha, cb[i]);
           const float sg = fast_sigmoid(x);
           float a = x * sg;
           float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
-          const int qj = blk * 32 + acc_row(i, g);
-          if (needmask && (q0 + qj < kpos || qj >= nq)) {
-            a = 0.0f;
-            gg = 0.0f;
+          if (needmask) {
+            const int r = acc_row(i, g);
+            const bool vis = r >= lo_row && r < hi_row;
+            a = vis ? a : 0.0f;
+            gg = vis ? gg : 0.0f;
           }
           pv[i] = a;
           gv[i] = gg;
@@ -364,8 +408,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
               if (k <= mode) dwb[k] += bsel[i] == k ? gg : 0.0f;
           }
         }
-        tile_contract_block<T, D>(dvacc, dt_, pv, blk, lane);
-        tile_contract_block<T, D>(dkacc, qt_, gv, blk, lane);
+        if constexpr (kBf16) {
+          tile_contract_block_o<D>(dvacc, reinterpret_cast<const char*>(dt_), lo, pv, blk);
+          tile_contract_block_o<D>(dkacc, reinterpret_cast<const char*>(qt_), lo, gv, blk);
+        } else {
+          tile_contract_block<T, D>(dvacc, dt_, pv, blk, lane);
+          tile_contract_block<T, D>(dkacc, qt_, gv, blk, lane);
+        }
       }
       if (mode != kModeExact) {
 #pragma unroll
@@ -400,9 +449,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
+  constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ KvSmem<T, D> sm;
   __shared__ TablesFwd tb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
+  LaneOffsets<D> lo;
+  if constexpr (kBf16) lo.init(lane);
   const int H = p.H, NB = p.NB;
   const float nb32 = NB * (1.0f / 32.0f);
   const float alpha = p.alpha;
@@ -477,21 +529,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
       const bool diag = key0 + BN - 1 > wave_qmin;
 #pragma unroll
       for (int blk = 0; blk < BN / 32; ++blk) {
-        const f32x16 s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
-        const f32x16 dp = tile_mma_rows<T, D>(vt_, blk * 32 + r32, dop, g);
+        f32x16 s, dp;
+        if constexpr (kBf16) {
+          s = tile_mma_rows_o<D>(reinterpret_cast<const char*>(kt_), lo, blk, qop);
+          dp = tile_mma_rows_o<D>(reinterpret_cast<const char*>(vt_), lo, blk, dop);
+        } else {
+          s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
+          dp = tile_mma_rows<T, D>(vt_, blk * 32 + r32, dop, g);
+        }
         float cb[16];
         int bsel[16];
         block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
         float gv[16];
+        const int lim_row = qpos - key0 - blk * 32;  // values with row > lim_row are masked
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float x = fmaf(s[i], alpha, cb[i]);
           const float sg = fast_sigmoid(x);
-          float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
-          if (diag && key0 + blk * 32 + acc_row(i, g) > qpos) gg = 0.0f;
-          gv[i] = gg;
+          const float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
+          gv[i] = (diag && acc_row(i, g) > lim_row) ? 0.0f : gg;
         }
-        tile_contract_block<T, D>(dqacc, kt_, gv, blk, lane);
+        if constexpr (kBf16)
+          tile_contract_block_o<D>(dqacc, reinterpret_cast<const char*>(kt_), lo, gv, blk);
+        else
+          tile_contract_block<T, D>(dqacc, kt_, gv, blk, lane);
       }
       if (more && wave == 0) ts_tile_fill<BN, false>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane);
       wait_loads();

@@ -93,8 +93,8 @@ __device__ __forceinline__ void ts_tile_range(const TsTile<N>& t, int a, int b, 
 }
 
 struct LaneBias {
-  float c[kMaxEdges + 1];   // alpha * w[b_lo + k]
-  int32_t thr[kMaxEdges];   // element passes edge t iff (t32 <= thr[t]) != flip
+  float c0, c1, c2, c3;     // alpha * w[b_lo + k], k = 0..3
+  int32_t t0, t1, t2;       // element passes edge k iff (t32 <= t_k) != flip
   int32_t flip;
   int b_lo;
   int n;                    // edges crossed (0..kMaxEdges) or kModeExact
@@ -106,66 +106,44 @@ __device__ __forceinline__ int32_t clamp_i32(int64_t x) {
 
 // Per-lane bias plan.  tsr: the lane's own timestamp; [tmin, tmax]: range of
 // the other rows it sees (any == false: it sees none, everything is masked).
+// Scalar fields and one exit keep the plan in registers.
 template <int SIGMA>
 __device__ __forceinline__ LaneBias lane_bias(int64_t tsr, int64_t tmin, int64_t tmax, bool any, int64_t base,
                                               int wide, const float* __restrict__ wtab,
                                               const u32x2* __restrict__ ep, int nb, float nb32) {
-  LaneBias r;
-#pragma unroll
-  for (int t = 0; t <= kMaxEdges; ++t) r.c[t] = 0.0f;
-  r.flip = 0;
-#pragma unroll
-  for (int t = 0; t < kMaxEdges; ++t) r.thr[t] = INT32_MIN;  // never passed (flip == 0)
-  r.b_lo = 0;
-  r.n = 0;
-  if (!any) return r;
-  int64_t dmin, dmax;
-  if (SIGMA > 0) {
-    dmin = tsr - tmax;
-    dmax = tsr - tmin;
-  } else {
-    dmin = tmin - tsr;
-    dmax = tmax - tsr;
-  }
-  int dir;
-  int64_t mlo, mhi;
-  if (dmin >= 0) {
-    dir = 0;
-    mlo = dmin;
-    mhi = dmax;
-  } else if (dmax <= 0) {
-    dir = 1;
-    mlo = -dmax;
-    mhi = -dmin;
-  } else {
-    r.n = kModeExact;
-    return r;
-  }
+  const int64_t dmin = SIGMA > 0 ? tsr - tmax : tmin - tsr;
+  const int64_t dmax = SIGMA > 0 ? tsr - tmin : tmax - tsr;
+  const bool pos = dmin >= 0, neg = dmax <= 0;
+  const int dir = pos ? 0 : 1;
+  const int64_t mlo = pos ? dmin : -dmax;
+  const int64_t mhi = pos ? dmax : -dmin;
   const int blo = bucket_of(mlo, nb, nb32, ep);
   const int bhi = bucket_of(mhi, nb, nb32, ep);
-  r.b_lo = blo;
   const int n = bhi - blo;
-  if (n > kMaxEdges || (n > 0 && wide)) {
-    r.n = kModeExact;
-    return r;
-  }
-  r.n = n;
+  const bool exact = any && ((!pos && !neg) || n > kMaxEdges || (n > 0 && wide));
   // Element |Δ| >= E passes the edge.  With Δ = σ(tsr - tso):
   //   σ(tsr - tso) >= E  (dir 0) / -σ(tsr - tso) >= E  (dir 1)
   // reduces to tso <= tsr - E (flip 0) or tso >= tsr + E, i.e. !(tso <= tsr + E - 1) (flip 1).
-  const int flip = SIGMA > 0 ? dir : 1 - dir;
+  const int flip = (any && !exact) ? (SIGMA > 0 ? dir : 1 - dir) : 0;
+  const int nn = (any && !exact) ? n : 0;
+  const int32_t never = flip ? INT32_MAX : INT32_MIN;
+  const int b0 = any && !exact ? blo : 0;
+  auto thr = [&](int k) -> int32_t {
+    if (k >= nn) return never;
+    const int64_t E = (int64_t)ep[b0 + k + 1].x;
+    return clamp_i32((flip ? tsr + E - 1 : tsr - E) - base);
+  };
+  LaneBias r;
+  r.b_lo = b0;
+  r.n = exact ? kModeExact : nn;
   r.flip = flip;
-#pragma unroll
-  for (int t = 0; t <= kMaxEdges; ++t) r.c[t] = wtab[min(blo + t, nb - 1)];
-#pragma unroll
-  for (int t = 0; t < kMaxEdges; ++t) {
-    if (t < n) {
-      const int64_t E = (int64_t)ep[blo + t + 1].x;
-      r.thr[t] = clamp_i32((flip ? tsr + E - 1 : tsr - E) - base);
-    } else {
-      r.thr[t] = flip ? INT32_MAX : INT32_MIN;  // never passed
-    }
-  }
+  r.c0 = any ? wtab[b0] : 0.0f;
+  r.c1 = any ? wtab[min(b0 + 1, nb - 1)] : 0.0f;
+  r.c2 = any ? wtab[min(b0 + 2, nb - 1)] : 0.0f;
+  r.c3 = any ? wtab[min(b0 + 3, nb - 1)] : 0.0f;
+  r.t0 = thr(0);
+  r.t1 = thr(1);
+  r.t2 = thr(2);
   return r;
 }
 
@@ -176,14 +154,14 @@ __device__ __forceinline__ LaneBias lane_bias(int64_t tsr, int64_t tmin, int64_t
 // has |tsr - base| < 2^30 (fast32) and the tile is not wide, |Δ| < 2^31 is
 // formed from 32-bit offsets.
 template <int SIGMA, int N>
-__device__ __forceinline__ void block_bias(float* cb, int* bsel, int nw, const LaneBias& lb, int64_t tsr,
+__device__ __forceinline__ void block_bias(float* cb, int* bsel, int nw, const LaneBias lb, int64_t tsr,
                                            int32_t tsr_rel, bool fast32, const TsTile<N>& t, int blk, int g,
                                            const float* __restrict__ wtab, const u32x2* __restrict__ ep, int nb,
                                            float nb32) {
   if (nw == 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      cb[i] = lb.c[0];
+      cb[i] = lb.c0;
       bsel[i] = 0;
     }
   } else if (nw <= kMaxEdges) {
@@ -195,10 +173,10 @@ __device__ __forceinline__ void block_bias(float* cb, int* bsel, int nw, const L
       const int32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool p0 = (vv[u] <= lb.thr[0]) != fl;
-        const bool p1 = (vv[u] <= lb.thr[1]) != fl;
-        const bool p2 = (vv[u] <= lb.thr[2]) != fl;
-        cb[q4 * 4 + u] = p2 ? lb.c[3] : (p1 ? lb.c[2] : (p0 ? lb.c[1] : lb.c[0]));
+        const bool p0 = (vv[u] <= lb.t0) != fl;
+        const bool p1 = (vv[u] <= lb.t1) != fl;
+        const bool p2 = (vv[u] <= lb.t2) != fl;
+        cb[q4 * 4 + u] = p2 ? lb.c3 : (p1 ? lb.c2 : (p0 ? lb.c1 : lb.c0));
         bsel[q4 * 4 + u] = (int)p0 + (int)p1 + (int)p2;
       }
     }

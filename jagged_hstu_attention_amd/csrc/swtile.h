@@ -155,3 +155,63 @@ __device__ __forceinline__ void store_row_from_acc(T* __restrict__ dst, const f3
 }
 
 }  // namespace hstu
+
+namespace hstu {
+
+// Per-lane byte offsets of the LDS reads one lane makes into a bf16 tile,
+// computed once per work item (the swizzle is the same for rows 32 apart and,
+// for transpose reads, for rows 16 apart, so block and step offsets are
+// compile-time constants added to these).
+template <int D> struct LaneOffsets {
+  int row[D / 16];     // row reads: row r32, elements kk*16 + 8g
+  int tr[D / 32][2];   // transpose reads: rows rb + 8h, columns dblk*32 + cb
+  __device__ __forceinline__ void init(int lane) {
+    using S = SwTile<__bf16, D>;
+    const int r32 = lane & 31, g = lane >> 5, m = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = 2 * S::off(r32, kk * 16 + 8 * g);
+    const int rb = 4 * g + (m >> 2), cb = 16 * (q & 1) + 4 * (m & 3);
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) tr[dblk][h] = 2 * S::off(rb + 8 * h, dblk * 32 + cb);
+  }
+};
+
+// Same products as tile_mma_rows / tile_contract_block, for bf16 tiles, with
+// precomputed lane offsets (`base` is the tile's LDS byte address).
+template <int D>
+__device__ __forceinline__ f32x16 tile_mma_rows_o(const char* __restrict__ base, const LaneOffsets<D>& lo, int blk,
+                                                  const bf16x8* op) {
+  using M = Mma<__bf16>;
+  f32x16 acc = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    acc = M::mma(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + lo.row[kk] + blk * 32 * D * 2)),
+                 op[kk], acc);
+  return acc;
+}
+
+template <int D>
+__device__ __forceinline__ void tile_contract_block_o(f32x16* out, const char* __restrict__ base,
+                                                      const LaneOffsets<D>& lo, const float* vals, int blk) {
+  using M = Mma<__bf16>;
+  bf16x8 b[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[u][j] = (__bf16)vals[8 * u + j];
+#pragma unroll
+  for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const char* p0 = base + lo.tr[dblk][0] + (blk * 32 + 16 * u) * D * 2;
+      const char* p1 = base + lo.tr[dblk][1] + (blk * 32 + 16 * u) * D * 2;
+      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+      const short __attribute__((ext_vector_type(8))) a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      out[dblk] = M::mma(__builtin_bit_cast(bf16x8, a), b[u], out[dblk]);
+    }
+}
+
+}  // namespace hstu

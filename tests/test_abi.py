@@ -122,3 +122,15 @@ def test_reorder_validation():
     assert lib.hstu_cp_reorder(None, o, 8, g, 2, 10, 5, 2, 0, None, None) == 1
     # nothing to do: no launch, OK
     assert lib.hstu_cp_reorder(g, o, 8, g, 0, 0, 0, 2, 0, None, None) == 0
+
+
+def test_timing_api_without_launches():
+    import jagged_hstu_attention_amd as m
+    m.timing_reset()
+    m.timing_enable(True)
+    m.timing_enable(False)
+    for k in ("sched", "fwd", "bwd_kv", "bwd_q", "reorder"):
+        assert m.timing_read(k) == (0.0, 0)
+    lib = _lib.load()
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.hstu_timing_read(7, ctypes.byref(ms), ctypes.byref(n)) == 1
