@@ -20,6 +20,8 @@ Besides the JSON contract fields it reports:
                 forward.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+       python bench.py --counter-run          (the program profiled for HBM counters)
+       python bench.py --traffic-summary FETCH_CSV WRITE_CSV   (CPU: writes the counter summary)
 """
 
 from __future__ import annotations
@@ -151,6 +153,41 @@ def stored_traffic(kernel):
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
 
 
+COUNTER_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o <name> -- "
+               "python bench.py --counter-run")
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_kernel", "bwd_q": "bwd_q_kernel", "sched": "sched_kernel"}
+
+
+def traffic_summary(fetch_csv, write_csv, out_path):
+    """Per-launch HBM bytes of each kernel from two rocprofv3 --pmc runs of
+    `bench.py --counter-run` (FETCH_SIZE, then WRITE_SIZE; both in KiB per
+    dispatch).  Each counter is scaled by what it reads for the 256 MiB device
+    copy (the largest copyBuffer dispatch) of that same run: the copy moves
+    exactly 256 MiB each way."""
+    import csv
+    import statistics
+    copy_kib = (256 << 20) / 1024.0
+    out = {"source_sha256": source_digest(), "workload": "bf16, B=16 x length 3072, H=4, d=128, 128 buckets",
+           "commands": [COUNTER_CMD.format(counter=c) for c in ("FETCH_SIZE", "WRITE_SIZE")],
+           "calibration": {}, "kernels": {}}
+    for counter, path, key in (("FETCH_SIZE", fetch_csv, "fetch_bytes"), ("WRITE_SIZE", write_csv, "write_bytes")):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        scale = copy_kib / copy
+        out["calibration"][counter] = {"copy_counter_kib": copy, "copy_true_kib": copy_kib,
+                                       "scale": round(scale, 4)}
+        for k, sym in KERNEL_SYMBOLS.items():
+            vals = [float(r["Counter_Value"]) for r in rows if sym in r["Kernel_Name"]]
+            if vals:
+                ent = out["kernels"].setdefault(k, {})
+                ent[key] = int(statistics.mean(vals) * scale * 1024)
+                ent[counter.lower() + "_kib_raw_per_dispatch"] = [round(v, 1) for v in vals]
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def time_kernels(case, steps):
     """Per-kernel average milliseconds, from HIP events the library records on
     the launch stream around each kernel (one forward + one backward per call)."""
@@ -267,7 +304,15 @@ def main():
     ap.add_argument("--counter-run", action="store_true",
                     help="for rocprofv3 --pmc: a 256 MiB device copy (calibration), then 3 forward+backward "
                          "steps of the 3072-length workload; no timing")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: turn the two --pmc counter CSVs of --counter-run into "
+                         "profiles/traffic_len3072.json and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        t = traffic_summary(*args.traffic_summary, os.path.join(ROOT, "profiles", "traffic_len3072.json"))
+        print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk.endswith("bytes")}
+                          for k, v in t["kernels"].items()}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
