@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "attn.h"
+#include "bias.h"
 #include "hstu.h"
 
 namespace {
@@ -103,21 +104,42 @@ void compute_edges(int64_t nb, uint32_t* e) {
   e[nb] = 0xFFFFFFFFu;
 }
 
+// The kernels' exact-bucket table splits every octave [2^e, 2^(e+1)) into 32
+// sub-bins and assumes no sub-bin holds two edges.  Check it for this table.
+int64_t bucket_of_host(uint64_t m, const uint32_t* e, int64_t nb) {
+  int64_t c = 0;
+  for (int64_t k = 1; k < nb; ++k) c += m >= e[k] ? 1 : 0;
+  return c;
+}
+
+bool subbins_hold_one_edge(const uint32_t* e, int64_t nb) {
+  for (int oct = 5; oct < 32; ++oct)
+    for (uint64_t j = 0; j < 32; ++j) {
+      const uint64_t lo = (32 + j) << (oct - 5), hi = lo + (1ull << (oct - 5)) - 1;
+      if (bucket_of_host(hi, e, nb) - bucket_of_host(lo, e, nb) > 1) return false;
+    }
+  return true;  // octaves below 5: a sub-bin holds at most one integer
+}
+
 struct EdgeCache {
   std::mutex mu;
   int64_t nb = -1;
+  bool lut_ok = false;
   hstu::EdgeArg arg;
 };
 EdgeCache g_edges;
 
-void get_edges(int64_t nb, hstu::EdgeArg* out) {
+// Returns false when the exact-bucket table cannot represent these edges.
+bool get_edges(int64_t nb, hstu::EdgeArg* out) {
   std::lock_guard<std::mutex> lk(g_edges.mu);
   if (g_edges.nb != nb) {
     std::memset(&g_edges.arg, 0, sizeof(g_edges.arg));
     compute_edges(nb, g_edges.arg.e);
+    g_edges.lut_ok = subbins_hold_one_edge(g_edges.arg.e, nb);
     g_edges.nb = nb;
   }
   *out = g_edges.arg;
+  return g_edges.lut_ok;
 }
 
 // Cached compute-unit count per device.
@@ -139,7 +161,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ctr, edges, local_off, qitems, kitems, total;
+  size_t ctr, edges, lut, local_off, qitems, kitems, total;
   int64_t max_qtiles, max_ktiles;
 };
 
@@ -155,6 +177,8 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
   off = align_up(off + hstu::kCtrCount * sizeof(int));
   l.edges = off;
   off = align_up(off + (hstu::kMaxBuckets + 4) * sizeof(uint32_t));
+  l.lut = off;
+  off = align_up(off + hstu::kLutSize * sizeof(hstu::u32x2));
   l.local_off = off;
   off = align_up(off + (size_t)(p->num_seqs + 1) * sizeof(int64_t));
   l.qitems = off;
@@ -276,11 +300,14 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   sp.kitems = reinterpret_cast<hstu::Item*>(ws + l.kitems);
   sp.ctr = reinterpret_cast<int*>(ws + l.ctr);
   sp.edges_out = reinterpret_cast<uint32_t*>(ws + l.edges);
+  sp.lut_out = reinterpret_cast<hstu::u32x2*>(ws + l.lut);
   sp.dw = dw;
   sp.dw_count = (int)(p->num_heads * p->num_buckets);
   sp.NB = (int)p->num_buckets;
   hstu::EdgeArg edges;
-  get_edges(p->num_buckets, &edges);
+  if (!get_edges(p->num_buckets, &edges))
+    return fail(HSTU_EUNSUPPORTED, "bucket table for num_buckets %lld has two edges in one sub-bin",
+                (long long)p->num_buckets);
   const hipError_t e = timed(HSTU_KERNEL_SCHED, s, [&] { return hstu::launch_sched(sp, edges, s); });
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
   return HSTU_OK;
@@ -293,6 +320,7 @@ hstu::AttnParams attn_params(const hstu_problem_t* p, const Layout& l, char* ws)
   a.kitems = reinterpret_cast<const hstu::Item*>(ws + l.kitems);
   a.ctr = reinterpret_cast<int*>(ws + l.ctr);
   a.edges = reinterpret_cast<const uint32_t*>(ws + l.edges);
+  a.lut = reinterpret_cast<const hstu::u32x2*>(ws + l.lut);
   a.H = (int)p->num_heads;
   a.NB = (int)p->num_buckets;
   a.cp_size = (int)p->cp_size;

@@ -27,6 +27,7 @@ struct AttnParams {
   const Item* kitems;
   int* ctr;
   const uint32_t* edges;     // [NB+1]
+  const u32x2* lut;          // [1024] exact-bucket table
   int H;
   int NB;
   int cp_size;
@@ -60,6 +61,7 @@ struct SchedParams {
   Item* kitems;
   int* ctr;
   uint32_t* edges_out;
+  u32x2* lut_out;    // [1024] exact-bucket table
   float* dw;         // zero-filled when non-null
   int dw_count;
   int NB;

@@ -4,19 +4,27 @@
 //
 // The operation (Scaling Generative Recommendations with Context Parallelism on
 // HSTU, §2.1, HSTUAttention equation and timestamp-bias paragraph):
-//   s_ij = alpha * (q_i . k_j + w[h, bucket(ts_i - ts_j)]),  alpha = 1/sqrt(d)
-//   a_ij = SiLU(s_ij) * [pos_j <= pos_i]
+//   x_ij = alpha * (q_i . k_j + w[h, bucket(ts_i - ts_j)]),  alpha = 1/sqrt(d)
+//   a_ij = SiLU(x_ij) * [pos_j <= pos_i]
 //   O_i  = sum_j a_ij v_j
-// Backward: dP = dO Vᵀ, G = alpha * dP * SiLU'(s) * mask, dV = aᵀ dO,
+// Backward: dP = dO Vᵀ, G = alpha * dP * SiLU'(x) * mask, dV = aᵀ dO,
 // dK = Gᵀ Q, dQ = G K, dW[h, b] = sum of G over pairs in bucket b.
+//
+// Arithmetic per score: with y = -log2(e) * x (one fma from the raw dot
+// product and a pre-scaled bias table), sigma = 1 / (1 + 2^y) and a' = y sigma
+// = -log2(e) SiLU(x).  SiLU'(x) = sigma + x sigma (1 - sigma)
+// = sigma - ln2 * a' (1 - sigma).  The constant factors -ln 2 (of a') and
+// alpha (of G) are applied once to the accumulated outputs.
 //
 // Every lane owns one row for the whole item (a query in the forward and dQ
 // passes, a key in the dK/dV pass), so the timestamp of its row, its causal
-// limit and its bias plan (epilogue.h) are per-lane scalars.  The other side
+// limit and its bias plan (bias.h) are per-lane scalars.  The other side
 // streams through double-buffered, swizzled LDS tiles (swtile.h) filled with
-// direct-to-LDS loads one tile ahead; one barrier per tile.
+// direct-to-LDS loads one tile ahead; one barrier per tile.  Each tile is
+// processed by a branch-free body specialised for its bias mode and for
+// whether it needs the causal mask.
 #include "attn.h"
-#include "epilogue.h"
+#include "bias.h"
 #include "swtile.h"
 
 namespace hstu {
@@ -30,42 +38,92 @@ constexpr int BK = 128;        // keys per dK/dV item (32 per wave)
 constexpr int BQ = 64;         // query rows per step of the dK/dV loop
 static_assert(BQ == BN, "the dK/dV step tiles share the key-tile shape");
 
+constexpr float kNegLog2e = -1.4426950408889634f;
+constexpr float kNegLn2 = -0.6931471805599453f;
+
 // d(ts_weights) bins are kept in kDwCopies interleaved copies (lane l adds to
 // copy l % kDwCopies) so that lanes of one instruction that hit the same bucket
 // mostly hit different addresses; the copies are summed at flush time.
 constexpr int kDwCopies = 8;
 
-struct alignas(16) Tables {
-  float w[kMaxBuckets];                         // alpha * ts_weights[h, :]
-  u32x2 ep[kMaxBuckets];                        // bucket edge pairs (E[k], E[k+1])
-  float dw[kDwCopies][kMaxBuckets + 1];         // per-item d(ts_weights) bins (backward)
-  int item;
+// MFMA products against LDS tiles, per element type.
+template <typename T, int D> struct TileOps;
+
+template <int D> struct TileOps<__bf16, D> {
+  LaneOffsets<D> lo;
+  __device__ __forceinline__ void init(int lane) { lo.init(lane); }
+  __device__ __forceinline__ f32x16 rows(const __bf16* t, int blk, const bf16x8* op) const {
+    return tile_mma_rows_o<D>(reinterpret_cast<const char*>(t), lo, blk, op);
+  }
+  __device__ __forceinline__ void contract(f32x16* out, const __bf16* t, const float* vals, int blk) const {
+    tile_contract_block_o<D>(out, reinterpret_cast<const char*>(t), lo, vals, blk);
+  }
 };
 
-struct alignas(16) TablesFwd {
-  float w[kMaxBuckets];
-  u32x2 ep[kMaxBuckets];
-  int item;
+template <int D> struct TileOps<float, D> {
+  int lane;
+  __device__ __forceinline__ void init(int l) { lane = l; }
+  __device__ __forceinline__ f32x16 rows(const float* t, int blk, const float* op) const {
+    return tile_mma_rows<float, D>(t, blk * 32 + (lane & 31), op, lane >> 5);
+  }
+  __device__ __forceinline__ void contract(f32x16* out, const float* t, const float* vals, int blk) const {
+    tile_contract_block<float, D>(out, t, vals, blk, lane);
+  }
 };
 
-template <typename TB>
-__device__ __forceinline__ void load_edges(TB& t, const AttnParams& p, int tid) {
-  for (int i = tid; i < p.NB; i += kThreads) t.ep[i] = u32x2{p.edges[i], p.edges[i + 1]};
+template <typename T, int D> struct alignas(16) KvSmem {
+  T k[2][BN * D];
+  T v[2][BN * D];
+  TsTile<BN> ts[2];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void issue_kv(KvSmem<T, D>& sm, int buf, const T* Kh, const T* Vh, int64_t ld, int key0,
+                                         int nvalid, int tid) {
+  tile_load_async<T, D, BN, kThreads>(sm.k[buf], Kh + key0 * ld, ld, nvalid, tid);
+  tile_load_async<T, D, BN, kThreads>(sm.v[buf], Vh + key0 * ld, ld, nvalid, tid);
 }
 
-template <typename T, typename TB>
-__device__ __forceinline__ void load_wtab(TB& t, const AttnParams& p, int h, int tid) {
+// The exact-bucket table and edges (once per workgroup) ...
+__device__ __forceinline__ void load_bucket_tables(BiasLds& bl, const AttnParams& p, int tid) {
+  for (int i = tid; i < kLutSize; i += kThreads) bl.lut[i] = p.lut[i];
+  for (int i = tid; i < p.NB + kPad; i += kThreads)
+    bl.e[i] = i <= p.NB ? (int32_t)min(p.edges[i], 0x7FFFFFFFu) : 0x7FFFFFFF;
+}
+
+// ... and the head's scaled bias values (per item).
+template <typename T>
+__device__ __forceinline__ void load_bias_values(BiasLds& bl, const AttnParams& p, int h, int tid) {
   const T* W = static_cast<const T*>(p.w) + (int64_t)h * p.NB;
-  for (int i = tid; i < p.NB; i += kThreads) t.w[i] = p.alpha * to_f32<T>(W[i]);
+  const float s = kNegLog2e * p.alpha;
+  for (int i = tid; i < p.NB + kPad; i += kThreads) bl.c[i] = s * to_f32<T>(W[min(i, p.NB - 1)]);
 }
 
-template <typename TB>
-__device__ __forceinline__ int pop_item(TB& t, int* counter, int tid) {
+__device__ __forceinline__ int pop_item(int* slot, int* counter, int tid) {
   __syncthreads();
-  if (tid == 0) t.item = atomicAdd(counter, 1);
+  if (tid == 0) *slot = atomicAdd(counter, 1);
   __syncthreads();
-  return t.item;
+  return *slot;
 }
+
+// Lane timestamp relative to the item base, and whether every valid lane of
+// the wave is within 2^30 of it (then the 32-bit paths apply to tiles that are
+// not wide).
+struct LaneTs {
+  int32_t rel;
+  bool fast;
+};
+__device__ __forceinline__ LaneTs lane_ts(int64_t ts, bool valid, int64_t base) {
+  const int64_t d = ts - base;
+  const bool ok = !valid || (d > -(1ll << 30) && d < (1ll << 30));
+  LaneTs r;
+  r.fast = __ballot(!ok) == 0;
+  r.rel = valid && ok ? (int32_t)d : 0;
+  return r;
+}
+
+// y = -log2(e) x, sigma = 1 / (1 + 2^y).
+__device__ __forceinline__ float sigmoid_y(float y) { return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y)); }
 
 // Rank-local query segments of sequence b: (local row start, first position,
 // length).  cp_size == 1: one segment covering the sequence.
@@ -135,6 +193,16 @@ struct StepIter {
   }
 };
 
+// Scale an accumulator set and store it as one row.
+template <typename T, int D>
+__device__ __forceinline__ void store_scaled(T* dst, f32x16* acc, float s, int g) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[i][j] *= s;
+  store_row_from_acc<T, D>(dst, acc, g);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -144,46 +212,73 @@ struct StepIter {
 // belongs to its own query, and the output is Oᵀ = Vᵀ Pᵀ with P taken straight
 // from the Sᵀ accumulators (V read with transpose reads).
 // ---------------------------------------------------------------------------
-template <typename T, int D> struct alignas(16) KvSmem {
-  T k[2][BN * D];
-  T v[2][BN * D];
-  TsTile<BN> ts[2];
+namespace {
+
+struct FwdLane {
+  int32_t tsr;      // own timestamp relative to the item base (32-bit modes)
+  int64_t ts64;     // own timestamp
+  int lim;          // key rows > lim of the tile are masked (qpos - key0)
+  int g;
+  float beta;       // -log2(e) * alpha
+  int nb;
 };
 
-template <typename T, int D>
-__device__ __forceinline__ void issue_kv(KvSmem<T, D>& sm, int buf, const T* Kh, const T* Vh, int64_t ld, int key0,
-                                         int nvalid, int tid) {
-  tile_load_async<T, D, BN, kThreads>(sm.k[buf], Kh + key0 * ld, ld, nvalid, tid);
-  tile_load_async<T, D, BN, kThreads>(sm.v[buf], Vh + key0 * ld, ld, nvalid, tid);
+// a' = y sigma(y) for the 16 values of one block, y = beta s + cb.
+template <bool MASK>
+__device__ __forceinline__ void silu_block(float* pv, const f32x16& s, const float* cb, float beta, int lim, int g) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float y = fmaf(s[i], beta, cb[i]);
+    const float a = y * sigmoid_y(y);
+    pv[i] = (MASK && acc_row(i, g) > lim) ? 0.0f : a;
+  }
 }
+
+// One 64-key tile: per 32-key block, the score MFMAs, the block's bias (their
+// latency overlaps), SiLU and the P V MFMAs.
+template <typename T, int D, bool MASK>
+__device__ __forceinline__ void fwd_tile(f32x16* oacc, const T* kt, const T* vt, const TsTile<BN>& ts,
+                                         const TileOps<T, D>& ops, const typename Mma<T>::operand* qop, int mode,
+                                         const Plan& pl, const FwdLane& ln, const BiasLds& bl) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const f32x16 s = ops.rows(kt, blk, qop);
+    float cb[16];
+    block_bias_mode<+1, BN, false, MASK>(cb, nullptr, mode, pl, ln.tsr, ln.ts64, ts, blk, ln.g, bl, ln.nb);
+    float pv[16];
+    silu_block<MASK>(pv, s, cb, ln.beta, ln.lim - 32 * blk, ln.g);
+    ops.contract(oacc, vt, pv, blk);
+  }
+}
+
+}  // namespace
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ KvSmem<T, D> sm;
-  __shared__ TablesFwd tb;
+  __shared__ BiasLds bl;
+  __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
-  LaneOffsets<D> lo;
-  if constexpr (kBf16) lo.init(lane);
+  TileOps<T, D> ops;
+  ops.init(lane);
   const int H = p.H, NB = p.NB;
-  const float nb32 = NB * (1.0f / 32.0f);
-  const float alpha = p.alpha;
   const int64_t ld = (int64_t)H * D;
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
   T* O = static_cast<T*>(p.out);
-  load_edges(tb, p, tid);
+  load_bucket_tables(bl, p, tid);
   const int n_work = p.ctr[kCtrQTiles] * H;
 
   for (;;) {
-    const int w = pop_item(tb, p.ctr + kCtrQNext, tid);
+    const int w = pop_item(&item_slot, p.ctr + kCtrQNext, tid);
     if (w >= n_work) break;
     const int h = w % H;
     const Item it = p.qitems[w / H];
     const int64_t seq0 = p.offsets[it.b];
+    const int64_t base = p.ts[seq0];
     const int qi = wave * 32 + r32;
     const bool qvalid = qi < it.n;
     const int qpos = it.pos0 + qi;
@@ -195,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
       qop[kk] = op_t{};
       if (qvalid) qop[kk] = M::load(Q + qrow * ld + h * D + kk * M::kK + g * M::kEpl);
     }
-    load_wtab<T>(tb, p, h, tid);
+    load_bias_values<T>(bl, p, h, tid);
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
@@ -205,10 +300,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
     const int wave_qmin = it.pos0 + wave * 32;
     const T* Kh = K + seq0 * ld + h * D;
     const T* Vh = V + seq0 * ld + h * D;
+    const LaneTs lt = lane_ts(tsq, qvalid, base);
+    FwdLane ln;
+    ln.g = g;
+    ln.beta = kNegLog2e * p.alpha;
+    ln.nb = NB;
+    ln.ts64 = tsq;
+    ln.tsr = lt.rel;
     int64_t tsv = 0;
     issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid);
     if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
-    if (wave == 0) ts_tile_fill<BN, false>(sm.ts[0], tsv, min(BN, kv_len), lane);
+    if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, min(BN, kv_len), lane, base);
     wait_loads();
     __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
@@ -221,55 +323,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
         issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid);
         if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
       }
-      const T* kt_ = sm.k[cur];
-      const T* vt_ = sm.v[cur];
       const TsTile<BN>& ts = sm.ts[cur];
-
-      const int lim = min(nvalid - 1, qpos - key0);
-      const bool any = qvalid && lim >= 0;
-      int64_t tmin = 0, tmax = 0;
-      ts_tile_range<BN, false>(ts, 0, any ? lim : 0, &tmin, &tmax);
-      const LaneBias lb = lane_bias<+1>(tsq, tmin, tmax, any, ts.base, ts.wide, tb.w, tb.ep, NB, nb32);
-      const int mode = wave_mode(lb.n);
-      int32_t tsr_rel = 0;
-      const bool fast32 = mode == kModeExact && wave_fast32(tsq, ts.base, ts.wide, &tsr_rel);
-      const bool diag = key0 + BN - 1 > wave_qmin;
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk) {
-        f32x16 s;
-        if constexpr (kBf16)
-          s = tile_mma_rows_o<D>(reinterpret_cast<const char*>(kt_), lo, blk, qop);
-        else
-          s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
-        float cb[16];
-        int bsel[16];
-        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
-        float pv[16];
-        if (diag) {
-          const int lim_row = qpos - key0 - blk * 32;  // values with row > lim_row are masked
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = fmaf(s[i], alpha, cb[i]);
-            const float a = x * fast_sigmoid(x);
-            pv[i] = acc_row(i, g) > lim_row ? 0.0f : a;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = fmaf(s[i], alpha, cb[i]);
-            pv[i] = x * fast_sigmoid(x);
-          }
-        }
-        if constexpr (kBf16)
-          tile_contract_block_o<D>(oacc, reinterpret_cast<const char*>(vt_), lo, pv, blk);
-        else
-          tile_contract_block<T, D>(oacc, vt_, pv, blk, lane);
+      const int4 hdr = ts.hdr;
+      const bool fast = lt.fast && hdr.z == 0;
+      ln.lim = qpos - key0;
+      if (key0 + BN - 1 > wave_qmin || nvalid < BN || !fast) {
+        fwd_tile<T, D, true>(oacc, sm.k[cur], sm.v[cur], ts, ops, qop, fast ? kModeLut : kModeWide, Plan{}, ln, bl);
+      } else {
+        const Plan pl = make_plan<+1>(ln.tsr, qvalid, hdr.x, hdr.y, bl);
+        fwd_tile<T, D, false>(oacc, sm.k[cur], sm.v[cur], ts, ops, qop, wave_mode(pl.n), pl, ln, bl);
       }
-      if (more && wave == 0) ts_tile_fill<BN, false>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane);
+      if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
       wait_loads();
       __syncthreads();
     }
-    if (qvalid) store_row_from_acc<T, D>(O + qrow * ld + h * D, oacc, g);
+    if (qvalid) store_scaled<T, D>(O + qrow * ld + h * D, oacc, kNegLn2, g);
   }
 }
 
@@ -281,19 +349,92 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
 // transposed from the same tiles.  Query rows past the end of a step replicate
 // the last row; their P and G are masked to zero.
 // ---------------------------------------------------------------------------
+namespace {
+
+struct KvLane {
+  int32_t tsr;
+  int64_t ts64;
+  int lo_row;   // query rows r of the step are visible iff lo_row <= r < hi_row
+  int hi_row;
+  int g;
+  float beta;
+  int nb;
+  bool valid;
+};
+
+// d(ts_weights) sums of a plan-mode step: s0 = all G, s_k = G passing edge k.
+struct DwSums {
+  float s0, s1, s2, s3;
+};
+
+template <typename T, int D, bool MASK>
+__device__ __forceinline__ void kv_tile(f32x16* dkacc, f32x16* dvacc, DwSums& dws, float* dwl, const T* qt,
+                                        const T* dt, const TsTile<BQ>& ts, const TileOps<T, D>& ops,
+                                        const typename Mma<T>::operand* kop, const typename Mma<T>::operand* vop,
+                                        int mode, const Plan& pl, const KvLane& ln, const BiasLds& bl) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const f32x16 s = ops.rows(qt, blk, kop);
+    const f32x16 dp = ops.rows(dt, blk, vop);
+    float cb[16];
+    int key[16];
+    block_bias_mode<-1, BQ, true, MASK>(cb, key, mode, pl, ln.tsr, ln.ts64, ts, blk, ln.g, bl, ln.nb);
+    float pv[16], gv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float y = fmaf(s[i], ln.beta, cb[i]);
+      const float sg = sigmoid_y(y);
+      const float a = y * sg;
+      const float u = fmaf(-a, sg, a);  // a' (1 - sigma)
+      const float gg = dp[i] * fmaf(u, kNegLn2, sg);
+      bool vis = true;
+      if constexpr (MASK) {
+        const int r = acc_row(i, ln.g) + blk * 32;
+        vis = r >= ln.lo_row && r < ln.hi_row;
+      }
+      pv[i] = vis ? a : 0.0f;
+      gv[i] = vis ? gg : 0.0f;
+    }
+    ops.contract(dvacc, dt, pv, blk);
+    ops.contract(dkacc, qt, gv, blk);
+    // d(ts_weights): exact modes add per element, plan modes keep sums
+    if (MASK || mode >= kModeLut) {
+      if (ln.valid) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) atomicAdd(&dwl[key[i]], gv[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dws.s0 += gv[i];
+      if (mode != kModeConst) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dws.s1 += key[i] >= 1 ? gv[i] : 0.0f;
+        if (mode == kModeThr3) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            dws.s2 += key[i] >= 2 ? gv[i] : 0.0f;
+            dws.s3 += key[i] >= 3 ? gv[i] : 0.0f;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
-  __shared__ Tables tb;
+  __shared__ BiasLds bl;
+  __shared__ float dwbins[kDwCopies][kMaxBuckets + 1];
+  __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
-  LaneOffsets<D> lo;
-  if constexpr (kBf16) lo.init(lane);
+  TileOps<T, D> ops;
+  ops.init(lane);
   const int H = p.H, NB = p.NB;
-  const float nb32 = NB * (1.0f / 32.0f);
-  const float alpha = p.alpha;
   const int64_t ld = (int64_t)H * D;
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
@@ -301,15 +442,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
   const T* dO = static_cast<const T*>(p.dout);
   T* dK = static_cast<T*>(p.dk);
   T* dV = static_cast<T*>(p.dv);
-  load_edges(tb, p, tid);
+  load_bucket_tables(bl, p, tid);
   const int n_work = p.ctr[kCtrKTiles] * H;
+  float* dwl = dwbins[lane % kDwCopies];
 
   for (;;) {
-    const int w = pop_item(tb, p.ctr + kCtrKNext, tid);
+    const int w = pop_item(&item_slot, p.ctr + kCtrKNext, tid);
     if (w >= n_work) break;
     const int h = w % H;
     const Item it = p.kitems[w / H];
     const int64_t seq0 = p.offsets[it.b];
+    const int64_t base = p.ts[seq0];
     const int kj = wave * 32 + r32;
     const bool kvalid = kj < it.n;
     const int kpos = it.pos0 + kj;
@@ -325,9 +468,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
         vop[kk] = M::load(V + krow * ld + h * D + kk * M::kK + g * M::kEpl);
       }
     }
-    load_wtab<T>(tb, p, h, tid);
-    for (int i = tid; i < kDwCopies * (kMaxBuckets + 1); i += kThreads) (&tb.dw[0][0])[i] = 0.0f;
-    float* dwl = tb.dw[lane % kDwCopies];
+    load_bias_values<T>(bl, p, h, tid);
+    for (int i = tid; i < kDwCopies * (kMaxBuckets + 1); i += kThreads) (&dwbins[0][0])[i] = 0.0f;
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
@@ -335,6 +477,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
       dvacc[i] = f32x16{};
     }
     const int wave_kmax = it.pos0 + wave * 32 + 31;
+    const LaneTs lt = lane_ts(tsk, kvalid, base);
+    KvLane ln;
+    ln.g = g;
+    ln.beta = kNegLog2e * p.alpha;
+    ln.nb = NB;
+    ln.ts64 = tsk;
+    ln.tsr = lt.rel;
+    ln.valid = kvalid;
 
     int64_t tsv = 0;
     StepIter si;
@@ -343,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
     if (si.valid()) {
       issue_kv<T, D>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid);
       if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
-      if (wave == 0) ts_tile_fill<BQ, true>(sm.ts[0], tsv, si.nq(), lane);
+      if (wave == 0) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
     }
     wait_loads();
     __syncthreads();
@@ -356,86 +506,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
         issue_kv<T, D>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid);
         if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
       }
-      const T* qt_ = sm.k[cur];
-      const T* dt_ = sm.v[cur];
       const TsTile<BQ>& ts = sm.ts[cur];
-
-      const int first = max(0, kpos - q0);
-      const bool any = kvalid && first < nq;
-      int64_t tmin = 0, tmax = 0;
-      ts_tile_range<BQ, true>(ts, any ? first : BQ - 1, BQ - 1, &tmin, &tmax);
-      const LaneBias lb = lane_bias<-1>(tsk, tmin, tmax, any, ts.base, ts.wide, tb.w, tb.ep, NB, nb32);
-      const int mode = wave_mode(lb.n);
-      int32_t tsr_rel = 0;
-      const bool fast32 = mode == kModeExact && wave_fast32(tsk, ts.base, ts.wide, &tsr_rel);
-      const bool needmask = q0 < wave_kmax || nq < BQ;
-      float dwb[kMaxEdges + 1] = {0.0f, 0.0f, 0.0f, 0.0f};  // bins b_lo + k
-#pragma unroll
-      for (int blk = 0; blk < BQ / 32; ++blk) {
-        f32x16 s, dp;
-        if constexpr (kBf16) {
-          s = tile_mma_rows_o<D>(reinterpret_cast<const char*>(qt_), lo, blk, kop);
-          dp = tile_mma_rows_o<D>(reinterpret_cast<const char*>(dt_), lo, blk, vop);
-        } else {
-          s = tile_mma_rows<T, D>(qt_, blk * 32 + r32, kop, g);
-          dp = tile_mma_rows<T, D>(dt_, blk * 32 + r32, vop, g);
-        }
-        float cb[16];
-        int bsel[16];
-        block_bias<-1, BQ>(cb, bsel, mode, lb, tsk, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
-        float pv[16], gv[16];
-        // query row qj is visible iff kpos <= q0 + qj and qj < nq
-        const int lo_row = kpos - q0 - blk * 32, hi_row = nq - blk * 32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = fmaf(s[i], alpha, cb[i]);
-          const float sg = fast_sigmoid(x);
-          float a = x * sg;
-          float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
-          if (needmask) {
-            const int r = acc_row(i, g);
-            const bool vis = r >= lo_row && r < hi_row;
-            a = vis ? a : 0.0f;
-            gg = vis ? gg : 0.0f;
-          }
-          pv[i] = a;
-          gv[i] = gg;
-          if (mode == kModeExact) {
-            if (gg != 0.0f) atomicAdd(&dwl[bsel[i]], gg);
-          } else {
-#pragma unroll
-            for (int k = 0; k <= kMaxEdges; ++k)
-              if (k <= mode) dwb[k] += bsel[i] == k ? gg : 0.0f;
-          }
-        }
-        if constexpr (kBf16) {
-          tile_contract_block_o<D>(dvacc, reinterpret_cast<const char*>(dt_), lo, pv, blk);
-          tile_contract_block_o<D>(dkacc, reinterpret_cast<const char*>(qt_), lo, gv, blk);
-        } else {
-          tile_contract_block<T, D>(dvacc, dt_, pv, blk, lane);
-          tile_contract_block<T, D>(dkacc, qt_, gv, blk, lane);
+      const int4 hdr = ts.hdr;
+      const bool fast = lt.fast && hdr.z == 0;
+      ln.lo_row = kpos - q0;
+      ln.hi_row = nq;
+      DwSums dws{0.0f, 0.0f, 0.0f, 0.0f};
+      if (q0 < wave_kmax || nq < BQ || !fast) {
+        kv_tile<T, D, true>(dkacc, dvacc, dws, dwl, sm.k[cur], sm.v[cur], ts, ops, kop, vop,
+                            fast ? kModeLut : kModeWide, Plan{}, ln, bl);
+      } else {
+        const Plan pl = make_plan<-1>(ln.tsr, kvalid, hdr.x, hdr.y, bl);
+        const int mode = wave_mode(pl.n);
+        kv_tile<T, D, false>(dkacc, dvacc, dws, dwl, sm.k[cur], sm.v[cur], ts, ops, kop, vop, mode, pl, ln, bl);
+        if (mode < kModeLut && kvalid) {
+          // bins b_lo + k from the nested sums
+          const int b0 = pl.blo;
+          if (dws.s0 != dws.s1) atomicAdd(&dwl[b0], dws.s0 - dws.s1);
+          if (dws.s1 != dws.s2) atomicAdd(&dwl[b0 + 1], dws.s1 - dws.s2);
+          if (dws.s2 != dws.s3) atomicAdd(&dwl[b0 + 2], dws.s2 - dws.s3);
+          if (dws.s3 != 0.0f) atomicAdd(&dwl[b0 + 3], dws.s3);
         }
       }
-      if (mode != kModeExact) {
-#pragma unroll
-        for (int k = 0; k <= kMaxEdges; ++k)
-          if (dwb[k] != 0.0f) atomicAdd(&dwl[lb.b_lo + k], dwb[k]);
-      }
-      if (nx.valid() && wave == 0) ts_tile_fill<BQ, true>(sm.ts[cur ^ 1], tsv, nx.nq(), lane);
+      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cur ^ 1], tsv, nx.nq(), lane, base);
       wait_loads();
       __syncthreads();
       si = nx;
       cur ^= 1;
     }
     if (kvalid) {
-      store_row_from_acc<T, D>(dK + krow * ld + h * D, dkacc, g);
-      store_row_from_acc<T, D>(dV + krow * ld + h * D, dvacc, g);
+      store_scaled<T, D>(dK + krow * ld + h * D, dkacc, p.alpha, g);
+      store_scaled<T, D>(dV + krow * ld + h * D, dvacc, kNegLn2, g);
     }
     for (int i = tid; i < NB; i += kThreads) {
       float v = 0.0f;
 #pragma unroll
-      for (int c = 0; c < kDwCopies; ++c) v += tb.dw[c][i];
-      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, v);
+      for (int c = 0; c < kDwCopies; ++c) v += dwbins[c][i];
+      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, p.alpha * v);
     }
   }
 }
@@ -445,34 +552,62 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
 // forward; Sᵀ = K Qᵀ and dPᵀ = V dOᵀ are recomputed and dQᵀ += Kᵀ Gᵀ (K read
 // transposed from the same tile).
 // ---------------------------------------------------------------------------
+namespace {
+
+template <typename T, int D, bool MASK>
+__device__ __forceinline__ void q_tile(f32x16* dqacc, const T* kt, const T* vt, const TsTile<BN>& ts,
+                                       const TileOps<T, D>& ops, const typename Mma<T>::operand* qop,
+                                       const typename Mma<T>::operand* dop, int mode, const Plan& pl,
+                                       const FwdLane& ln, const BiasLds& bl) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const f32x16 s = ops.rows(kt, blk, qop);
+    const f32x16 dp = ops.rows(vt, blk, dop);
+    float cb[16];
+    block_bias_mode<+1, BN, false, MASK>(cb, nullptr, mode, pl, ln.tsr, ln.ts64, ts, blk, ln.g, bl, ln.nb);
+    float gv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float y = fmaf(s[i], ln.beta, cb[i]);
+      const float sg = sigmoid_y(y);
+      const float a = y * sg;
+      const float u = fmaf(-a, sg, a);
+      const float gg = dp[i] * fmaf(u, kNegLn2, sg);
+      gv[i] = (MASK && acc_row(i, ln.g) > ln.lim - 32 * blk) ? 0.0f : gg;
+    }
+    ops.contract(dqacc, kt, gv, blk);
+  }
+}
+
+}  // namespace
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
-  constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ KvSmem<T, D> sm;
-  __shared__ TablesFwd tb;
+  __shared__ BiasLds bl;
+  __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
-  LaneOffsets<D> lo;
-  if constexpr (kBf16) lo.init(lane);
+  TileOps<T, D> ops;
+  ops.init(lane);
   const int H = p.H, NB = p.NB;
-  const float nb32 = NB * (1.0f / 32.0f);
-  const float alpha = p.alpha;
   const int64_t ld = (int64_t)H * D;
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
   const T* dO = static_cast<const T*>(p.dout);
   T* dQ = static_cast<T*>(p.dq);
-  load_edges(tb, p, tid);
+  load_bucket_tables(bl, p, tid);
   const int n_work = p.ctr[kCtrQTiles] * H;
 
   for (;;) {
-    const int w = pop_item(tb, p.ctr + kCtrQNext2, tid);
+    const int w = pop_item(&item_slot, p.ctr + kCtrQNext2, tid);
     if (w >= n_work) break;
     const int h = w % H;
     const Item it = p.qitems[w / H];
     const int64_t seq0 = p.offsets[it.b];
+    const int64_t base = p.ts[seq0];
     const int qi = wave * 32 + r32;
     const bool qvalid = qi < it.n;
     const int qpos = it.pos0 + qi;
@@ -488,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
         dop[kk] = M::load(dO + qrow * ld + h * D + kk * M::kK + g * M::kEpl);
       }
     }
-    load_wtab<T>(tb, p, h, tid);
+    load_bias_values<T>(bl, p, h, tid);
     f32x16 dqacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
@@ -498,10 +633,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
     const int wave_qmin = it.pos0 + wave * 32;
     const T* Kh = K + seq0 * ld + h * D;
     const T* Vh = V + seq0 * ld + h * D;
+    const LaneTs lt = lane_ts(tsq, qvalid, base);
+    FwdLane ln;
+    ln.g = g;
+    ln.beta = kNegLog2e * p.alpha;
+    ln.nb = NB;
+    ln.ts64 = tsq;
+    ln.tsr = lt.rel;
     int64_t tsv = 0;
     issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid);
     if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
-    if (wave == 0) ts_tile_fill<BN, false>(sm.ts[0], tsv, min(BN, kv_len), lane);
+    if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, min(BN, kv_len), lane, base);
     wait_loads();
     __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
@@ -514,51 +656,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
         issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid);
         if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
       }
-      const T* kt_ = sm.k[cur];
-      const T* vt_ = sm.v[cur];
       const TsTile<BN>& ts = sm.ts[cur];
-
-      const int lim = min(nvalid - 1, qpos - key0);
-      const bool any = qvalid && lim >= 0;
-      int64_t tmin = 0, tmax = 0;
-      ts_tile_range<BN, false>(ts, 0, any ? lim : 0, &tmin, &tmax);
-      const LaneBias lb = lane_bias<+1>(tsq, tmin, tmax, any, ts.base, ts.wide, tb.w, tb.ep, NB, nb32);
-      const int mode = wave_mode(lb.n);
-      int32_t tsr_rel = 0;
-      const bool fast32 = mode == kModeExact && wave_fast32(tsq, ts.base, ts.wide, &tsr_rel);
-      const bool diag = key0 + BN - 1 > wave_qmin;
-#pragma unroll
-      for (int blk = 0; blk < BN / 32; ++blk) {
-        f32x16 s, dp;
-        if constexpr (kBf16) {
-          s = tile_mma_rows_o<D>(reinterpret_cast<const char*>(kt_), lo, blk, qop);
-          dp = tile_mma_rows_o<D>(reinterpret_cast<const char*>(vt_), lo, blk, dop);
-        } else {
-          s = tile_mma_rows<T, D>(kt_, blk * 32 + r32, qop, g);
-          dp = tile_mma_rows<T, D>(vt_, blk * 32 + r32, dop, g);
-        }
-        float cb[16];
-        int bsel[16];
-        block_bias<+1, BN>(cb, bsel, mode, lb, tsq, tsr_rel, fast32, ts, blk, g, tb.w, tb.ep, NB, nb32);
-        float gv[16];
-        const int lim_row = qpos - key0 - blk * 32;  // values with row > lim_row are masked
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = fmaf(s[i], alpha, cb[i]);
-          const float sg = fast_sigmoid(x);
-          const float gg = alpha * dp[i] * (sg * (1.0f + x * (1.0f - sg)));
-          gv[i] = (diag && acc_row(i, g) > lim_row) ? 0.0f : gg;
-        }
-        if constexpr (kBf16)
-          tile_contract_block_o<D>(dqacc, reinterpret_cast<const char*>(kt_), lo, gv, blk);
-        else
-          tile_contract_block<T, D>(dqacc, kt_, gv, blk, lane);
+      const int4 hdr = ts.hdr;
+      const bool fast = lt.fast && hdr.z == 0;
+      ln.lim = qpos - key0;
+      if (key0 + BN - 1 > wave_qmin || nvalid < BN || !fast) {
+        q_tile<T, D, true>(dqacc, sm.k[cur], sm.v[cur], ts, ops, qop, dop, fast ? kModeLut : kModeWide, Plan{}, ln,
+                           bl);
+      } else {
+        const Plan pl = make_plan<+1>(ln.tsr, qvalid, hdr.x, hdr.y, bl);
+        q_tile<T, D, false>(dqacc, sm.k[cur], sm.v[cur], ts, ops, qop, dop, wave_mode(pl.n), pl, ln, bl);
       }
-      if (more && wave == 0) ts_tile_fill<BN, false>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane);
+      if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
       wait_loads();
       __syncthreads();
     }
-    if (qvalid) store_row_from_acc<T, D>(dQ + qrow * ld + h * D, dqacc, g);
+    if (qvalid) store_scaled<T, D>(dQ + qrow * ld + h * D, dqacc, p.alpha, g);
   }
 }
 

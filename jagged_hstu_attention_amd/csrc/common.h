@@ -1,5 +1,5 @@
 // Device-side building blocks shared by the gfx950 kernels: MFMA operand
-// traits, the exact timestamp bucket, SiLU, and the work-item format.
+// traits, conversions and the work-item format.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -69,33 +69,6 @@ template <> struct Mma<float> {
 
 // Row (within its 32-row block) of accumulator value i held by lane group g.
 __device__ __forceinline__ int acc_row(int i, int g) { return ((i >> 2) << 3) + (g << 2) + (i & 3); }
-
-// ---------------------------------------------------------------------------
-// Exact timestamp bucket: #{k in [1, NB) : |delta| >= E_k}.  For integer |delta|
-// the count equals floor(NB/32 * log2|delta|) in exact arithmetic, so a float
-// estimate of that floor is within one of it (the estimate's error is far below
-// one bucket), and one comparison against each neighbouring integer edge fixes
-// it.  `ep[k]` is the LDS pair (E[k], E[k+1]) for k in [0, NB), with E[0] = 0
-// and E[NB] = 0xFFFFFFFF as sentinel.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int bucket_u32(uint32_t x, int nb, float nb_over_32, const u32x2* __restrict__ ep) {
-  int k = (int)floorf(__log2f(fmaxf((float)x, 1.0f)) * nb_over_32);
-  k = min(max(k, 0), nb - 1);
-  const u32x2 e = ep[k];
-  k += (int)(x >= e.y) - (int)(x < e.x);
-  return min(k, nb - 1);  // only x = 2^32 - 1 reaches the sentinel
-}
-
-__device__ __forceinline__ int bucket_of(int64_t delta, int nb, float nb_over_32, const u32x2* __restrict__ ep) {
-  const uint64_t mag = delta < 0 ? (uint64_t)(-delta) : (uint64_t)delta;
-  if (mag >> 32) return nb - 1;
-  return bucket_u32((uint32_t)mag, nb, nb_over_32, ep);
-}
-
-// SiLU and its derivative, fp32.  sigmoid via exp2 and a hardware reciprocal.
-__device__ __forceinline__ float fast_sigmoid(float s) {
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s));
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;

@@ -8,6 +8,7 @@
 // and resets the work counters.  Tiles lying entirely above the causal
 // diagonal are never emitted: a query tile's key range stops at its last row.
 #include "attn.h"
+#include "bias.h"
 
 namespace hstu {
 
@@ -81,6 +82,39 @@ __device__ int64_t block_scan(int64_t v, int64_t* buf, int64_t* total) {
 
 __device__ __forceinline__ int clampc(int64_t c, int hs) { return (int)(c < hs - 1 ? c : hs - 1); }
 
+// #{k in [1, nb) : E_k <= m}
+__device__ int bucket_search(uint64_t m, const EdgeArg& edges, int nb) {
+  int lo = 0, hi = nb - 1;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((uint64_t)edges.e[mid] <= m) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Entry idx = (z << 5) | j of the exact-bucket table: the integers m whose
+// leading-zero count is z and whose five bits after the leading one are j.
+// With b0 the bucket of the smallest such m, the entry is {E, b0} when an edge
+// E lies above it within the sub-bin, else {0, b0 - 1} (the compare always
+// adds one).  At most one edge lies in a sub-bin for NB <= 512 (checked on
+// the host).  Index patterns no integer produces hold {0, 0xFFFFFFFF}.
+__device__ u32x2 lut_entry(int idx, const EdgeArg& edges, int nb) {
+  const int e = 31 - (idx >> 5), j = idx & 31;
+  uint64_t lo, hi;
+  if (e >= 5) {
+    lo = (uint64_t)(32 + j) << (e - 5);
+    hi = lo + (1ull << (e - 5)) - 1;
+  } else {
+    const int step = 1 << (5 - e);
+    if (j % step) return u32x2{0u, 0xFFFFFFFFu};
+    lo = hi = (1ull << e) + (uint64_t)(j / step);
+  }
+  const int b0 = bucket_search(lo, edges, nb);
+  if (b0 + 1 < nb && (uint64_t)edges.e[b0 + 1] <= hi) return u32x2{edges.e[b0 + 1], (uint32_t)b0};
+  return u32x2{0u, (uint32_t)(b0 - 1)};
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams p, const EdgeArg edges) {
@@ -91,6 +125,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   const int hs = p.hist_size;
 
   for (int i = t; i <= p.NB; i += kSchedThreads) p.edges_out[i] = edges.e[i];
+  for (int i = t; i < kLutSize; i += kSchedThreads) p.lut_out[i] = lut_entry(i, edges, p.NB);
   if (p.dw)
     for (int i = t; i < p.dw_count; i += kSchedThreads) p.dw[i] = 0.0f;
   for (int i = t; i < hs; i += kSchedThreads) {

@@ -134,3 +134,63 @@ def test_timing_api_without_launches():
     lib = _lib.load()
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.hstu_timing_read(7, ctypes.byref(ms), ctypes.byref(n)) == 1
+
+
+def _lut_model(edges, nb):
+    """Host model of the kernels' exact-bucket table: entry (z << 5) | j covers
+    the integers with z leading zeros and sub-bin j; bucket = b + [m >= E]."""
+    e_arr = np.array(edges[1:nb], dtype=np.uint64)
+    table = []
+    for idx in range(1024):
+        e, j = 31 - (idx >> 5), idx & 31
+        if e >= 5:
+            lo = (32 + j) << (e - 5)
+            hi = lo + (1 << (e - 5)) - 1
+        else:
+            step = 1 << (5 - e)
+            if j % step:
+                table.append((0, 0xFFFFFFFF))
+                continue
+            lo = hi = (1 << e) + j // step
+        b0 = int(np.searchsorted(e_arr, lo, side="right"))
+        if b0 + 1 < nb and edges[b0 + 1] <= hi:
+            table.append((edges[b0 + 1], b0))
+        else:
+            table.append((0, (b0 - 1) & 0xFFFFFFFF))
+    return table
+
+
+def _lut_lookup(table, m):
+    m = max(int(m), 1)
+    z = 32 - m.bit_length()
+    t = (m << z) & 0xFFFFFFFF
+    E, b = table[(z << 5) | ((t >> 26) & 31)]
+    return ((b + (1 if m >= E else 0)) & 0xFFFFFFFF)
+
+
+@pytest.mark.parametrize("nb", [1, 2, 3, 31, 32, 33, 100, 128, 256, 300, 511, 512])
+def test_exact_bucket_table_model_matches_oracle(nb):
+    edges = hstu.bucket_edges(nb)
+    table = _lut_model(edges, nb)
+    rng = np.random.default_rng(nb)
+    vals = set(range(0, 300))
+    for k in range(1, nb):
+        E = edges[k]
+        vals.update(x for x in (E - 1, E, E + 1) if 0 <= x < 2 ** 32)
+    for p in range(33):
+        vals.update(x for x in ((1 << p) - 1, 1 << p, (1 << p) + 1) if 0 <= x < 2 ** 32)
+    vals.update(int(x) for x in rng.integers(0, 2 ** 32, size=2000, dtype=np.uint64))
+    vals = np.array(sorted(vals), dtype=np.int64)
+    want = oracle.bucketize(vals, nb)
+    got = np.array([_lut_lookup(table, v) for v in vals])
+    assert np.array_equal(got, want)
+
+
+def test_every_sub_bin_holds_at_most_one_edge():
+    for nb in range(1, 513):
+        e = np.array(hstu.bucket_edges(nb)[1:nb], dtype=np.int64)
+        for oct_ in range(5, 32):
+            lo = (32 + np.arange(32, dtype=np.int64)) << (oct_ - 5)
+            hi = lo + (1 << (oct_ - 5)) - 1
+            inside = np.searchsorted(e, hi, side="right") - np.searchsorted(e, lo, side="right")
+            assert inside.max() <= 1, (nb, oct_)
