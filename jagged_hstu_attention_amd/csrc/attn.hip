@@ -41,10 +41,12 @@ static_assert(BQ == BN, "the dK/dV step tiles share the key-tile shape");
 constexpr float kNegLog2e = -1.4426950408889634f;
 constexpr float kNegLn2 = -0.6931471805599453f;
 
-// d(ts_weights) bins are kept in kDwCopies interleaved copies (lane l adds to
-// copy l % kDwCopies) so that lanes of one instruction that hit the same bucket
-// mostly hit different addresses; the copies are summed at flush time.
-constexpr int kDwCopies = 8;
+// d(ts_weights) bins are kept in kDwCopies copies (lane l adds to copy
+// l % kDwCopies): neighbouring keys usually share a bucket, so lanes of one
+// atomic instruction would otherwise collide on one address.  The copies are
+// summed at flush time.
+template <typename T, int D>
+constexpr int kDwCopies = sizeof(T) == 2 ? 32 : 8;  // fp32, d = 128 has no LDS left for more
 
 // MFMA products against LDS tiles, per element type.
 template <typename T, int D> struct TileOps;
@@ -99,11 +101,14 @@ __device__ __forceinline__ void load_bias_values(BiasLds& bl, const AttnParams& 
   for (int i = tid; i < p.NB + kPad; i += kThreads) bl.c[i] = s * to_f32<T>(W[min(i, p.NB - 1)]);
 }
 
+// The item index is read back from LDS; readfirstlane marks it wave-uniform,
+// so everything derived from it (item fields, offsets, tile bases) lives in
+// scalar registers.
 __device__ __forceinline__ int pop_item(int* slot, int* counter, int tid) {
   __syncthreads();
   if (tid == 0) *slot = atomicAdd(counter, 1);
   __syncthreads();
-  return *slot;
+  return __builtin_amdgcn_readfirstlane(*slot);
 }
 
 // Lane timestamp relative to the item base, and whether every valid lane of
@@ -397,11 +402,13 @@ __device__ __forceinline__ void kv_tile(f32x16* dkacc, f32x16* dvacc, DwSums& dw
     }
     ops.contract(dvacc, dt, pv, blk);
     ops.contract(dkacc, qt, gv, blk);
-    // d(ts_weights): exact modes add per element, plan modes keep sums
+    // d(ts_weights): exact modes add per element (masked-out elements skip
+    // the atomic), plan modes keep sums
     if (MASK || mode >= kModeLut) {
       if (ln.valid) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) atomicAdd(&dwl[key[i]], gv[i]);
+        for (int i = 0; i < 16; ++i)
+          if (gv[i] != 0.0f) atomicAdd(&dwl[key[i]], gv[i]);
       }
     } else {
 #pragma unroll
@@ -421,6 +428,59 @@ __device__ __forceinline__ void kv_tile(f32x16* dkacc, f32x16* dvacc, DwSums& dw
   }
 }
 
+// Plan-mode step specialised for its mode (constant bias, one or up to three
+// thresholds): the whole step is one basic block in which the compiler can
+// interleave the MFMAs with the elementwise work; the d(ts_weights) sums are
+// kept for the thresholds the mode has.
+template <typename T, int D, int MODE>
+__device__ __forceinline__ void kv_tile_plan(f32x16* dkacc, f32x16* dvacc, DwSums& dws, const T* qt, const T* dt,
+                                             const TsTile<BQ>& ts, const TileOps<T, D>& ops,
+                                             const typename Mma<T>::operand* kop,
+                                             const typename Mma<T>::operand* vop, const float c0, const float c1,
+                                             const float c2, const float c3, const int32_t t1, const int32_t t2,
+                                             const int32_t t3, const int flip, const float beta) {
+  const int32_t* varr = flip ? ts.nu : ts.u;
+  const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const f32x16 s = ops.rows(qt, blk, kop);
+    const f32x16 dp = ops.rows(dt, blk, vop);
+    int32_t v[16];
+    if constexpr (MODE != kModeConst) block_rows_i32(v, varr, blk, g);
+    float pv[16], gv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float c = c0;
+      bool p1 = false, p2 = false, p3 = false;
+      if constexpr (MODE != kModeConst) {
+        p1 = v[i] <= t1;
+        c = p1 ? c1 : c;
+      }
+      if constexpr (MODE == kModeThr3) {
+        p2 = v[i] <= t2;
+        p3 = v[i] <= t3;
+        c = p2 ? c2 : c;
+        c = p3 ? c3 : c;
+      }
+      const float y = fmaf(s[i], beta, c);
+      const float sg = sigmoid_y(y);
+      const float a = y * sg;
+      const float u = fmaf(-a, sg, a);  // a' (1 - sigma)
+      const float gg = dp[i] * fmaf(u, kNegLn2, sg);
+      pv[i] = a;
+      gv[i] = gg;
+      dws.s0 += gg;
+      if constexpr (MODE != kModeConst) dws.s1 += p1 ? gg : 0.0f;
+      if constexpr (MODE == kModeThr3) {
+        dws.s2 += p2 ? gg : 0.0f;
+        dws.s3 += p3 ? gg : 0.0f;
+      }
+    }
+    ops.contract(dvacc, dt, pv, blk);
+    ops.contract(dkacc, qt, gv, blk);
+  }
+}
+
 }  // namespace
 
 template <typename T, int D>
@@ -429,7 +489,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
   using op_t = typename M::operand;
   __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
   __shared__ BiasLds bl;
-  __shared__ float dwbins[kDwCopies][kMaxBuckets + 1];
+  constexpr int kCopies = kDwCopies<T, D>;
+  __shared__ float dwbins[kCopies][kMaxBuckets + 1];
   __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
   TileOps<T, D> ops;
@@ -444,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
   T* dV = static_cast<T*>(p.dv);
   load_bucket_tables(bl, p, tid);
   const int n_work = p.ctr[kCtrKTiles] * H;
-  float* dwl = dwbins[lane % kDwCopies];
+  float* dwl = dwbins[lane % kCopies];
 
   for (;;) {
     const int w = pop_item(&item_slot, p.ctr + kCtrKNext, tid);
@@ -469,7 +530,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
       }
     }
     load_bias_values<T>(bl, p, h, tid);
-    for (int i = tid; i < kDwCopies * (kMaxBuckets + 1); i += kThreads) (&dwbins[0][0])[i] = 0.0f;
+    for (int i = tid; i < kCopies * (kMaxBuckets + 1); i += kThreads) (&dwbins[0][0])[i] = 0.0f;
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
@@ -518,7 +579,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
       } else {
         const Plan pl = make_plan<-1>(ln.tsr, kvalid, hdr.x, hdr.y, bl);
         const int mode = wave_mode(pl.n);
-        kv_tile<T, D, false>(dkacc, dvacc, dws, dwl, sm.k[cur], sm.v[cur], ts, ops, kop, vop, mode, pl, ln, bl);
+#define HSTU_KV_PLAN(M)                                                                                        \
+  kv_tile_plan<T, D, M>(dkacc, dvacc, dws, sm.k[cur], sm.v[cur], ts, ops, kop, vop, pl.c0, pl.c1, pl.c2, pl.c3, \
+                        pl.t1, pl.t2, pl.t3, pl.flip, ln.beta)
+        if (mode == kModeConst)
+          HSTU_KV_PLAN(kModeConst);
+        else if (mode == kModeThr1)
+          HSTU_KV_PLAN(kModeThr1);
+        else if (mode == kModeThr3)
+          HSTU_KV_PLAN(kModeThr3);
+        else
+          kv_tile<T, D, false>(dkacc, dvacc, dws, dwl, sm.k[cur], sm.v[cur], ts, ops, kop, vop, mode, pl, ln, bl);
+#undef HSTU_KV_PLAN
         if (mode < kModeLut && kvalid) {
           // bins b_lo + k from the nested sums
           const int b0 = pl.blo;
@@ -541,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
     for (int i = tid; i < NB; i += kThreads) {
       float v = 0.0f;
 #pragma unroll
-      for (int c = 0; c < kDwCopies; ++c) v += dwbins[c][i];
+      for (int c = 0; c < kCopies; ++c) v += dwbins[c][i];
       if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, p.alpha * v);
     }
   }

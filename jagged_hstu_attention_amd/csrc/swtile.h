@@ -43,13 +43,34 @@ template <typename T, int D> struct SwTile {
 
 // Issue the direct-to-LDS loads of ROWS rows (row r at src + r*ld) into `dst`.
 // The loads complete asynchronously (vmcnt); wait and barrier before reading.
+// A full tile (nvalid == ROWS) is addressed from the tile's first row (a
+// wave-uniform base) plus a 32-bit per-lane offset, which keeps the issue
+// nearly free of vector registers and instructions; a partial tile clamps
+// each row to the last valid one.
 template <typename T, int D, int ROWS, int NT>
 __device__ __forceinline__ void tile_load_async(T* __restrict__ dst, const T* __restrict__ src, int64_t ld,
                                                 int nvalid, int tid) {
   using S = SwTile<T, D>;
   constexpr int kInstr = ROWS * S::C / 64;
   static_assert(ROWS * S::C % 64 == 0, "whole wave instructions");
-  const int wave = tid >> 6, lane = tid & 63;
+  // The per-lane addresses are cheap to recompute; the empty asm keeps the
+  // compiler from hoisting them out of the tile loop, where they would occupy
+  // registers (or be spilled and reloaded) for the whole loop.
+  int t = tid;
+  asm volatile("" : "+v"(t));
+  const int wave = t >> 6, lane = t & 63;
+  if (nvalid >= ROWS) {
+    const char* base = reinterpret_cast<const char*>(src);
+#pragma unroll
+    for (int i = wave; i < kInstr; i += NT / 64) {
+      const int s = i * 64 + lane;
+      const int G = s >> 4;
+      const int lin = (G << 4) | ((s & 15) ^ S::f(G));
+      const uint32_t off = (uint32_t)((lin / S::C) * (int)ld + (lin % S::C) * S::kElems) * (uint32_t)sizeof(T);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const T*>(base + off), dst + i * 64 * S::kElems, 16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = wave; i < kInstr; i += NT / 64) {
     const int s = i * 64 + lane;
@@ -213,5 +234,9 @@ __device__ __forceinline__ void tile_contract_block_o(f32x16* out, const char* _
       out[dblk] = M::mma(__builtin_bit_cast(bf16x8, a), b[u], out[dblk]);
     }
 }
+
+}  // namespace hstu
+
+namespace hstu {
 
 }  // namespace hstu
