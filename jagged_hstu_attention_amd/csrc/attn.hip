@@ -79,26 +79,27 @@ template <typename T, int D> struct alignas(16) KvSmem {
   TsTile<BN> ts[2];
 };
 
-template <typename T, int D>
+template <typename T, int D, int NT = kThreads>
 __device__ __forceinline__ void issue_kv(KvSmem<T, D>& sm, int buf, const T* Kh, const T* Vh, int64_t ld, int key0,
                                          int nvalid, int tid) {
-  tile_load_async<T, D, BN, kThreads>(sm.k[buf], Kh + key0 * ld, ld, nvalid, tid);
-  tile_load_async<T, D, BN, kThreads>(sm.v[buf], Vh + key0 * ld, ld, nvalid, tid);
+  tile_load_async<T, D, BN, NT>(sm.k[buf], Kh + key0 * ld, ld, nvalid, tid);
+  tile_load_async<T, D, BN, NT>(sm.v[buf], Vh + key0 * ld, ld, nvalid, tid);
 }
 
 // The exact-bucket table and edges (once per workgroup) ...
+template <int NT = kThreads>
 __device__ __forceinline__ void load_bucket_tables(BiasLds& bl, const AttnParams& p, int tid) {
-  for (int i = tid; i < kLutSize; i += kThreads) bl.lut[i] = p.lut[i];
-  for (int i = tid; i < p.NB + kPad; i += kThreads)
+  for (int i = tid; i < kLutSize; i += NT) bl.lut[i] = p.lut[i];
+  for (int i = tid; i < p.NB + kPad; i += NT)
     bl.e[i] = i <= p.NB ? (int32_t)min(p.edges[i], 0x7FFFFFFFu) : 0x7FFFFFFF;
 }
 
 // ... and the head's scaled bias values (per item).
-template <typename T>
+template <typename T, int NT = kThreads>
 __device__ __forceinline__ void load_bias_values(BiasLds& bl, const AttnParams& p, int h, int tid) {
   const T* W = static_cast<const T*>(p.w) + (int64_t)h * p.NB;
   const float s = kNegLog2e * p.alpha;
-  for (int i = tid; i < p.NB + kPad; i += kThreads) bl.c[i] = s * to_f32<T>(W[min(i, p.NB - 1)]);
+  for (int i = tid; i < p.NB + kPad; i += NT) bl.c[i] = s * to_f32<T>(W[min(i, p.NB - 1)]);
 }
 
 // The item index is read back from LDS; readfirstlane marks it wave-uniform,
@@ -407,8 +408,7 @@ __device__ __forceinline__ void kv_tile(f32x16* dkacc, f32x16* dvacc, DwSums& dw
     if (MASK || mode >= kModeLut) {
       if (ln.valid) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (gv[i] != 0.0f) atomicAdd(&dwl[key[i]], gv[i]);
+        for (int i = 0; i < 16; ++i) atomicAdd(&dwl[key[i]], gv[i]);
       }
     } else {
 #pragma unroll
@@ -620,6 +620,259 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Backward, key-major pass for bf16 with d in {64, 128}: eight waves per item
+// of 128 keys.  Waves w and w + 4 share keys 32 (w % 4) .. + 31.  In every step
+// of 64 query rows, wave w computes S and dP only for the 32-row block
+// hf = w / 4, and the pair swaps the resulting P and G through LDS; each wave
+// then accumulates dV and dK over both blocks for its half hf of the head
+// dimension.  A wave so holds half the accumulators of the four-wave kernel
+// and fits in 256 registers: two waves share each SIMD and overlap their
+// MFMA and VALU work.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kPairThreads = 512;
+constexpr int kPairDwCopies = 16;
+
+// Transpose-read offsets of the d blocks in this wave's half.
+template <int D> struct HalfTrOffsets {
+  static constexpr int kBlocks = D / 64;  // 32-column d blocks per half
+  int tr[kBlocks][2];
+  __device__ __forceinline__ void init(int lane, int hf) {
+    using S = SwTile<__bf16, D>;
+    const int g = lane >> 5, m = lane & 15, q = lane >> 4;
+    const int rb = 4 * g + (m >> 2), cb = 16 * (q & 1) + 4 * (m & 3);
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) tr[j][h] = 2 * S::off(rb + 8 * h, (hf * kBlocks + j) * 32 + cb);
+  }
+};
+
+// out[j] += Xᵀ (d block j of the half) B over the 32 rows of block blk of a
+// bf16 tile; B is the pair of packed bf16x8 operands of the block.
+template <int D>
+__device__ __forceinline__ void contract_half(f32x16* out, const char* __restrict__ base, const HalfTrOffsets<D>& to,
+                                              const u32x4* b, int blk) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const char* p0 = base + to.tr[j][0] + (blk * 32 + 16 * u) * D * 2;
+      const char* p1 = base + to.tr[j][1] + (blk * 32 + 16 * u) * D * 2;
+      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+      const short __attribute__((ext_vector_type(8))) a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      out[j] = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b[u]), out[j]);
+    }
+}
+
+// SiLU / gradient of one block (16 values per lane), packed to bf16, with the
+// d(ts_weights) contributions: exact modes add per element (key = bucket),
+// plan modes sum per passed edge (key = edges passed) and add per step.
+template <int MODE>
+__device__ __forceinline__ void pair_elem(u32x4* own_p, u32x4* own_g, float* dwl, const f32x16& s, const f32x16& dp,
+                                          const float* cb, const int* key, float beta, bool masked, int lo_row,
+                                          int hi_row, int g, bool kvalid, int blo) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    float a2[2], g2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float y = fmaf(s[i + e], beta, cb[i + e]);
+      const float sg = sigmoid_y(y);
+      const float a = y * sg;
+      const float u = fmaf(-a, sg, a);  // a' (1 - sigma)
+      const float gg = dp[i + e] * fmaf(u, kNegLn2, sg);
+      const int r = acc_row(i + e, g);
+      const bool vis = !masked || (r >= lo_row && r < hi_row);
+      a2[e] = vis ? a : 0.0f;
+      g2[e] = vis ? gg : 0.0f;
+      if constexpr (MODE >= kModeLut) {
+        atomicAdd(&dwl[key[i + e]], kvalid ? g2[e] : 0.0f);
+      } else {
+        s0 += g2[e];
+        if constexpr (MODE != kModeConst) s1 += key[i + e] >= 1 ? g2[e] : 0.0f;
+        if constexpr (MODE == kModeThr3) {
+          s2 += key[i + e] >= 2 ? g2[e] : 0.0f;
+          s3 += key[i + e] >= 3 ? g2[e] : 0.0f;
+        }
+      }
+    }
+    own_p[i >> 3][(i & 7) >> 1] = pack_bf16x2(a2[0], a2[1]);
+    own_g[i >> 3][(i & 7) >> 1] = pack_bf16x2(g2[0], g2[1]);
+  }
+  if constexpr (MODE < kModeLut) {
+    if (kvalid) {
+      if (s0 != s1) atomicAdd(&dwl[blo], s0 - s1);
+      if (s1 != s2) atomicAdd(&dwl[blo + 1], s1 - s2);
+      if (s2 != s3) atomicAdd(&dwl[blo + 2], s2 - s3);
+      if (s3 != 0.0f) atomicAdd(&dwl[blo + 3], s3);
+    }
+  }
+}
+
+__device__ __forceinline__ void pack16(u32x4* dst, const float* v) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    dst[u] = u32x4{pack_bf16x2(v[8 * u], v[8 * u + 1]), pack_bf16x2(v[8 * u + 2], v[8 * u + 3]),
+                   pack_bf16x2(v[8 * u + 4], v[8 * u + 5]), pack_bf16x2(v[8 * u + 6], v[8 * u + 7])};
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const AttnParams p) {
+  using M = Mma<__bf16>;
+  using T = __bf16;
+  constexpr int NT = kPairThreads;
+  constexpr int KB = D / 64;
+  __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
+  __shared__ BiasLds bl;
+  __shared__ float dwbins[kPairDwCopies][kMaxBuckets + 1];
+  __shared__ u32x4 xch[8][4][64];  // per wave: P (2 operands) and G (2 operands), lane-contiguous
+  __shared__ int item_slot;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
+  const int kg = wave & 3, hf = wave >> 2;
+  LaneOffsets<D> lo;
+  lo.init(lane);
+  HalfTrOffsets<D> to;
+  to.init(lane, hf);
+  const int H = p.H, NB = p.NB;
+  const int64_t ld = (int64_t)H * D;
+  const T* Q = static_cast<const T*>(p.q);
+  const T* K = static_cast<const T*>(p.k);
+  const T* V = static_cast<const T*>(p.v);
+  const T* dO = static_cast<const T*>(p.dout);
+  T* dK = static_cast<T*>(p.dk);
+  T* dV = static_cast<T*>(p.dv);
+  load_bucket_tables<NT>(bl, p, tid);
+  const int n_work = p.ctr[kCtrKTiles] * H;
+  float* dwl = dwbins[lane % kPairDwCopies];
+
+  for (;;) {
+    const int w = pop_item(&item_slot, p.ctr + kCtrKNext, tid);
+    if (w >= n_work) break;
+    const int h = w % H;
+    const Item it = p.kitems[w / H];
+    const int64_t seq0 = p.offsets[it.b];
+    const int64_t base = p.ts[seq0];
+    const int kj = kg * 32 + r32;
+    const bool kvalid = kj < it.n;
+    const int kpos = it.pos0 + kj;
+    const int64_t krow = (int64_t)it.row0 + kj;
+    const int64_t tsk = kvalid ? p.ts[krow] : 0;
+    bf16x8 kop[D / 16], vop[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kop[kk] = bf16x8{};
+      vop[kk] = bf16x8{};
+      if (kvalid) {
+        kop[kk] = M::load(K + krow * ld + h * D + kk * 16 + g * 8);
+        vop[kk] = M::load(V + krow * ld + h * D + kk * 16 + g * 8);
+      }
+    }
+    load_bias_values<T, NT>(bl, p, h, tid);
+    for (int i = tid; i < kPairDwCopies * (kMaxBuckets + 1); i += NT) (&dwbins[0][0])[i] = 0.0f;
+    f32x16 dkacc[KB], dvacc[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      dkacc[i] = f32x16{};
+      dvacc[i] = f32x16{};
+    }
+    const int wave_kmax = it.pos0 + kg * 32 + 31;
+    const LaneTs lt = lane_ts(tsk, kvalid, base);
+    const float beta = kNegLog2e * p.alpha;
+
+    int64_t tsv = 0;
+    StepIter si;
+    si.init(p, it.b, it.pos0);
+    int cur = 0;
+    if (si.valid()) {
+      issue_kv<T, D, NT>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid);
+      if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
+      if (wave == 0) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
+    }
+    wait_loads();
+    __syncthreads();
+    while (si.valid()) {
+      const int q0 = si.q0;
+      const int nq = si.nq();
+      StepIter nx = si;
+      nx.next();
+      if (nx.valid()) {
+        issue_kv<T, D, NT>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid);
+        if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
+      }
+      const TsTile<BQ>& ts = sm.ts[cur];
+      const char* qb = reinterpret_cast<const char*>(sm.k[cur]);
+      const char* db = reinterpret_cast<const char*>(sm.v[cur]);
+      const int4 hdr = ts.hdr;
+      const bool fast = lt.fast && hdr.z == 0;
+      // rows r of this wave's block are visible iff lo_row <= r < hi_row
+      const int lo_row = kpos - q0 - 32 * hf, hi_row = nq - 32 * hf;
+      const bool masked = q0 + 32 * hf < wave_kmax || nq < BQ || !fast;
+
+      const f32x16 s = tile_mma_rows_o<D>(qb, lo, hf, kop);
+      const f32x16 dp = tile_mma_rows_o<D>(db, lo, hf, vop);
+      float cb[16];
+      int key[16];
+      // The plan is only used in unmasked steps, but computing it always keeps
+      // it out of a conditional assignment (which would put it in memory).
+      const int2 br = ts.blk[hf];  // the plan covers this wave's block only
+      const Plan pl = make_plan<-1>(lt.rel, kvalid, br.x, br.y, bl);
+      const int pmode = wave_mode(pl.n);
+      const int mode = masked ? (fast ? kModeLut : kModeWide) : pmode;
+      if (masked)
+        block_bias_mode<-1, BQ, true, true>(cb, key, mode, pl, lt.rel, tsk, ts, hf, g, bl, NB);
+      else
+        block_bias_mode<-1, BQ, true, false>(cb, key, mode, pl, lt.rel, tsk, ts, hf, g, bl, NB);
+      // SiLU, its gradient, P and G packed to bf16 and exchanged with the
+      // partner wave, and the d(ts_weights) contributions (per mode).
+      u32x4 own_p[2], own_g[2];
+      if (mode >= kModeLut)
+        pair_elem<kModeLut>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
+      else if (mode == kModeConst)
+        pair_elem<kModeConst>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
+      else if (mode == kModeThr1)
+        pair_elem<kModeThr1>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
+      else
+        pair_elem<kModeThr3>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
+      xch[wave][0][lane] = own_p[0];
+      xch[wave][1][lane] = own_p[1];
+      xch[wave][2][lane] = own_g[0];
+      xch[wave][3][lane] = own_g[1];
+      __syncthreads();
+      const int pw = wave ^ 4;
+      const u32x4 par_p[2] = {xch[pw][0][lane], xch[pw][1][lane]};
+      const u32x4 par_g[2] = {xch[pw][2][lane], xch[pw][3][lane]};
+      contract_half<D>(dvacc, db, to, own_p, hf);
+      contract_half<D>(dkacc, qb, to, own_g, hf);
+      contract_half<D>(dvacc, db, to, par_p, hf ^ 1);
+      contract_half<D>(dkacc, qb, to, par_g, hf ^ 1);
+      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cur ^ 1], tsv, nx.nq(), lane, base);
+      wait_loads();
+      __syncthreads();
+      si = nx;
+      cur ^= 1;
+    }
+    if (kvalid) {
+      const int64_t row = (int64_t)it.row0 + kj;
+      store_scaled<T, D / 2>(dK + row * ld + h * D + hf * (D / 2), dkacc, p.alpha, g);
+      store_scaled<T, D / 2>(dV + row * ld + h * D + hf * (D / 2), dvacc, kNegLn2, g);
+    }
+    __syncthreads();
+    for (int i = tid; i < NB; i += NT) {
+      float v = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kPairDwCopies; ++c) v += dwbins[c][i];
+      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, p.alpha * v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Backward, query-major pass: dQ.  Same item list and lane ownership as the
 // forward; Sᵀ = K Qᵀ and dPᵀ = V dOᵀ are recomputed and dQᵀ += Kᵀ Gᵀ (K read
 // transposed from the same tile).
@@ -752,9 +1005,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
 // ---------------------------------------------------------------------------
 namespace {
 template <typename K>
-int grid_for(K kernel, int max_items, int cus) {
+int grid_for(K kernel, int max_items, int cus, int threads = kThreads) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int g = cus * per_cu;
   return max(1, min(g, max_items));
@@ -766,8 +1019,13 @@ hipError_t launch_all(const AttnParams& p, int which, int max_items, int cus, hi
     auto k = fwd_kernel<T, D>;
     hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
   } else if (which == 1) {
-    auto k = bwd_kv_kernel<T, D>;
-    hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
+    if constexpr (sizeof(T) == 2 && D >= 64) {
+      auto k = bwd_kv_pair_kernel<D>;
+      hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus, kPairThreads)), dim3(kPairThreads), 0, s, p);
+    } else {
+      auto k = bwd_kv_kernel<T, D>;
+      hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
+    }
   } else {
     auto k = bwd_q_kernel<T, D>;
     hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);

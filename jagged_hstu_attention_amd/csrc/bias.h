@@ -59,12 +59,14 @@ __device__ __forceinline__ int lut_bucket64(int64_t d, int nb, const u32x2* __re
 // Timestamps of the tile's other rows, staged in LDS by one wave, relative to
 // the base of the work item (the first timestamp of its sequence).  Rows past
 // the last valid one repeat its timestamp.  u = ts - base and nu = ~u (for
-// compares whose direction is flipped); hdr = {min u, max u, wide, 0}.
+// compares whose direction is flipped); hdr = {min u, max u, wide, 0} over the
+// tile and blk[b] = {min u, max u} over its 32-row block b.
 template <int N> struct alignas(16) TsTile {
   int32_t u[N];
   int32_t nu[N];
   int64_t t64[N];
   int4 hdr;  // wide: some |ts - base| is 2^30 or more, only the 64-bit path is exact
+  int2 blk[N / 32];
 };
 
 // Filled by one wave: lane j holds the timestamp of row j; rows >= nvalid
@@ -79,14 +81,17 @@ __device__ __forceinline__ void ts_tile_fill(TsTile<N>& t, int64_t ts, int nvali
   const int32_t r32 = wide ? 0 : (int32_t)rel;
   int32_t mn = r32, mx = r32;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
+  for (int off = 16; off >= 1; off >>= 1) {
     mn = min(mn, __shfl_xor(mn, off));
     mx = max(mx, __shfl_xor(mx, off));
   }
+  // mn/mx now hold the range of this lane's 32-row half
   t.u[lane] = r32;
   t.nu[lane] = ~r32;
   t.t64[lane] = v;
-  if (lane == 0) t.hdr = int4{mn, mx, wide ? 1 : 0, 0};
+  if ((lane & 31) == 0) t.blk[lane >> 5] = int2{mn, mx};
+  const int32_t mn2 = min(mn, __shfl_xor(mn, 32)), mx2 = max(mx, __shfl_xor(mx, 32));
+  if (lane == 0) t.hdr = int4{mn2, mx2, wide ? 1 : 0, 0};
 }
 
 // Per-lane plan of an unmasked tile.

@@ -56,9 +56,9 @@ __device__ __forceinline__ void tile_load_async(T* __restrict__ dst, const T* __
   // The per-lane addresses are cheap to recompute; the empty asm keeps the
   // compiler from hoisting them out of the tile loop, where they would occupy
   // registers (or be spilled and reloaded) for the whole loop.
-  int t = tid;
-  asm volatile("" : "+v"(t));
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations stay scalar
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
   if (nvalid >= ROWS) {
     const char* base = reinterpret_cast<const char*>(src);
 #pragma unroll
