@@ -155,7 +155,9 @@ def stored_traffic(kernel):
 
 COUNTER_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o <name> -- "
                "python bench.py --counter-run")
-KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_kernel", "bwd_q": "bwd_q_kernel", "sched": "sched_kernel"}
+# Substrings of the kernel symbols (the dK/dV pass runs bwd_kv_pair_kernel for
+# bf16 with d >= 64, bwd_kv_kernel otherwise).
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_", "bwd_q": "bwd_q_kernel", "sched": "sched_kernel"}
 
 
 def traffic_summary(fetch_csv, write_csv, out_path):
@@ -356,7 +358,7 @@ def main():
     achieved = kfl[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(dom),
-                "kernel": {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_kernel", "bwd_q": "bwd_q_kernel"}[dom],
+                "kernel": {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_pair_kernel", "bwd_q": "bwd_q_kernel"}[dom],
                 "ms_per_launch": round(kms[dom], 4), "flop_per_launch": kfl[dom]}
 
     extra = {

@@ -248,12 +248,28 @@ __device__ __forceinline__ void fwd_tile(f32x16* oacc, const T* kt, const T* vt,
                                          const Plan& pl, const FwdLane& ln, const BiasLds& bl) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const f32x16 s = ops.rows(kt, blk, qop);
+    f32x16 s;
+    bf16x8 tv[D / 16];
+    if constexpr (sizeof(T) == 2) {
+      // all K operands of the block, then its MFMAs; the V operands of the
+      // P V product are read while the bias and SiLU are computed
+      bf16x8 ka[D / 16];
+      rows_load<D>(ka, reinterpret_cast<const char*>(kt), ops.lo, blk);
+      __builtin_amdgcn_sched_barrier(0);
+      s = rows_mma<D>(ka, qop);
+      tr_load<D>(tv, reinterpret_cast<const char*>(vt), ops.lo, blk);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      s = ops.rows(kt, blk, qop);
+    }
     float cb[16];
     block_bias_mode<+1, BN, false, MASK>(cb, nullptr, mode, pl, ln.tsr, ln.ts64, ts, blk, ln.g, bl, ln.nb);
     float pv[16];
     silu_block<MASK>(pv, s, cb, ln.beta, ln.lim - 32 * blk, ln.g);
-    ops.contract(oacc, vt, pv, blk);
+    if constexpr (sizeof(T) == 2)
+      tr_mma<D>(oacc, tv, pv);
+    else
+      ops.contract(oacc, vt, pv, blk);
   }
 }
 

@@ -240,3 +240,53 @@ __device__ __forceinline__ void tile_contract_block_o(f32x16* out, const char* _
 namespace hstu {
 
 }  // namespace hstu
+
+namespace hstu {
+
+// Split forms of tile_mma_rows_o / tile_contract_block_o: the LDS reads of a
+// product are issued as one group (operands held in registers), so its MFMAs
+// run back to back instead of each waiting for its own read.
+template <int D>
+__device__ __forceinline__ void rows_load(bf16x8* a, const char* __restrict__ base, const LaneOffsets<D>& lo, int blk) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    a[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + lo.row[kk] + blk * 32 * D * 2));
+}
+
+template <int D>
+__device__ __forceinline__ f32x16 rows_mma(const bf16x8* a, const bf16x8* op) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) acc = Mma<__bf16>::mma(a[kk], op[kk], acc);
+  return acc;
+}
+
+template <int D>
+__device__ __forceinline__ void tr_load(bf16x8* t, const char* __restrict__ base, const LaneOffsets<D>& lo, int blk) {
+#pragma unroll
+  for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const char* p0 = base + lo.tr[dblk][0] + (blk * 32 + 16 * u) * D * 2;
+      const char* p1 = base + lo.tr[dblk][1] + (blk * 32 + 16 * u) * D * 2;
+      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+      const short __attribute__((ext_vector_type(8))) a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      t[2 * dblk + u] = __builtin_bit_cast(bf16x8, a);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void tr_mma(f32x16* out, const bf16x8* t, const float* vals) {
+  bf16x8 b[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[u][j] = (__bf16)vals[8 * u + j];
+#pragma unroll
+  for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) out[dblk] = Mma<__bf16>::mma(t[2 * dblk + u], b[u], out[dblk]);
+}
+
+}  // namespace hstu
