@@ -126,7 +126,9 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
  * out_offsets (device, may be NULL): receives the int64 [C*B + 1] offsets of
  * the rank-major segments (segment r*B + b = rank r's rows of sequence b),
  * whichever the direction.  offsets: int64 [B+1] sequence offsets of the
- * sequence-major layout; total_rows = offsets[B]. */
+ * sequence-major layout; total_rows = offsets[B] < 2^42 (else
+ * HSTU_EUNSUPPORTED); every sequence length must be <= max_seq_len (it sizes
+ * the grid; a longer sequence is copied only in part). */
 int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes,
                     const int64_t* offsets, int64_t num_seqs, int64_t total_rows,
                     int64_t max_seq_len, int64_t cp_size, int inverse,

@@ -485,6 +485,7 @@ int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t*
                     void* stream) {
   if (num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)num_seqs);
   if (total_rows < 0) return fail(HSTU_EINVAL, "total_rows %lld < 0", (long long)total_rows);
+  if (total_rows >= (1ll << 42)) return fail(HSTU_EUNSUPPORTED, "total_rows %lld >= 2^42", (long long)total_rows);
   if (row_bytes < 1) return fail(HSTU_EINVAL, "row_bytes %lld < 1", (long long)row_bytes);
   if (cp_size < 1) return fail(HSTU_EINVAL, "cp_size %lld < 1", (long long)cp_size);
   if (cp_size > 1024) return fail(HSTU_EUNSUPPORTED, "cp_size %lld > 1024", (long long)cp_size);

@@ -20,7 +20,14 @@ namespace {
 constexpr int kReorderThreads = 256;
 constexpr int64_t kSliceBytes = 64 * 1024;
 
-__device__ __forceinline__ int64_t chunk_lo64(int64_t L, int64_t k, int64_t nch) { return k * L / nch; }
+// floor(k L / nch) for 0 <= k <= nch <= 2048 and L < 2^42: k L is an exact
+// double, the quotient is correctly rounded (error below 2^-11 for a quotient
+// under 2^42), and a non-integral quotient lies at least 1/nch >= 2^-11 below
+// the next integer, so the floor is exact.  A 64-bit integer division would
+// take a long software loop.
+__device__ __forceinline__ int64_t chunk_lo64(int64_t L, int64_t k, int64_t nch) {
+  return (int64_t)floor((double)(k * L) / (double)nch);
+}
 
 // Rows of sequence b (length L) held by ranks < r: floor(rL/2C) + L - floor((2C-r)L/2C).
 __device__ __forceinline__ int64_t rows_before_rank(int64_t L, int64_t r, int64_t nch) {
@@ -37,27 +44,26 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(const char* __
                                                                   int64_t rb, const int64_t* __restrict__ offsets,
                                                                   int64_t B, int64_t T, int64_t C, int inverse,
                                                                   int64_t* __restrict__ out_offsets) {
-  __shared__ int64_t red[kReorderThreads];
+  __shared__ int64_t start_s;
   const int64_t pair = blockIdx.x;
   const int64_t r = pair / B, b = pair % B;
   const int64_t nch = 2 * C;
   const int tid = threadIdx.x;
 
   // Start of segment (r, b) in the rank-major layout: all rows of ranks < r,
-  // plus rank r's rows of sequences < b.
-  int64_t part = 0;
-  for (int64_t bb = tid; bb < B; bb += kReorderThreads) {
-    const int64_t L = offsets[bb + 1] - offsets[bb];
-    part += rows_before_rank(L, r, nch);
-    if (bb < b) part += pair_rows(L, r, nch);
+  // plus rank r's rows of sequences < b (a short serial sum: B is the number
+  // of sequences, and the copy below dominates).
+  if (tid == 0) {
+    int64_t part = 0;
+    for (int64_t bb = 0; bb < B; ++bb) {
+      const int64_t Lb = offsets[bb + 1] - offsets[bb];
+      part += rows_before_rank(Lb, r, nch);
+      if (bb < b) part += pair_rows(Lb, r, nch);
+    }
+    start_s = part;
   }
-  red[tid] = part;
   __syncthreads();
-  for (int s = kReorderThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const int64_t start = red[0];
+  const int64_t start = start_s;
 
   const int64_t o0 = offsets[b];
   const int64_t L = offsets[b + 1] - o0;
@@ -78,7 +84,9 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(const char* __
   char* rank_base_out = out + start * rb;               // rank-major side (forward)
   const int64_t seg_a = (o0 + a0) * rb, seg_b = (o0 + b0) * rb;
 
-  constexpr int kU = 4;
+  // Each thread moves kU vectors per round; the data is streamed once, so the
+  // accesses are non-temporal.
+  constexpr int kU = 8;
   constexpr int64_t kStep = (int64_t)kReorderThreads * sizeof(V);
   for (int64_t x0 = lo + tid * (int64_t)sizeof(V); x0 < hi; x0 += kU * kStep) {
     V val[kU];
@@ -87,7 +95,8 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(const char* __
       const int64_t x = x0 + u * kStep;
       if (x < hi) {
         const int64_t seq_off = x < abytes ? seg_a + x : seg_b + (x - abytes);
-        val[u] = inverse ? *reinterpret_cast<const V*>(rank_base_in + x) : *reinterpret_cast<const V*>(in + seq_off);
+        const V* src = inverse ? reinterpret_cast<const V*>(rank_base_in + x) : reinterpret_cast<const V*>(in + seq_off);
+        val[u] = __builtin_nontemporal_load(src);
       }
     }
 #pragma unroll
@@ -95,10 +104,8 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(const char* __
       const int64_t x = x0 + u * kStep;
       if (x < hi) {
         const int64_t seq_off = x < abytes ? seg_a + x : seg_b + (x - abytes);
-        if (inverse)
-          *reinterpret_cast<V*>(out + seq_off) = val[u];
-        else
-          *reinterpret_cast<V*>(rank_base_out + x) = val[u];
+        V* dst = inverse ? reinterpret_cast<V*>(out + seq_off) : reinterpret_cast<V*>(rank_base_out + x);
+        __builtin_nontemporal_store(val[u], dst);
       }
     }
   }
@@ -121,10 +128,10 @@ hipError_t launch_reorder(const void* in, void* out, int64_t row_bytes, const in
   char* o = static_cast<char*>(out);
   const int inv = inverse ? 1 : 0;
   if ((align & 15) == 0)
-    hipLaunchKernelGGL(reorder_kernel<uint4>, grid, dim3(kReorderThreads), 0, s, i, o, row_bytes, offsets, B,
+    hipLaunchKernelGGL(reorder_kernel<u32x4>, grid, dim3(kReorderThreads), 0, s, i, o, row_bytes, offsets, B,
                        total_rows, (int64_t)cp_size, inv, out_offsets);
   else if ((align & 7) == 0)
-    hipLaunchKernelGGL(reorder_kernel<uint2>, grid, dim3(kReorderThreads), 0, s, i, o, row_bytes, offsets, B,
+    hipLaunchKernelGGL(reorder_kernel<u32x2>, grid, dim3(kReorderThreads), 0, s, i, o, row_bytes, offsets, B,
                        total_rows, (int64_t)cp_size, inv, out_offsets);
   else if ((align & 3) == 0)
     hipLaunchKernelGGL(reorder_kernel<uint32_t>, grid, dim3(kReorderThreads), 0, s, i, o, row_bytes, offsets, B,
