@@ -126,12 +126,15 @@ def kernel_flops(pairs, heads, dqk, dv):
 
 
 def source_digest():
-    """sha256 over the kernel sources (to tell whether stored counters are current)."""
+    """sha256 over the sources of the kernels the counter summary covers (to
+    tell whether stored counters are current); the reorder kernel is not one of
+    them."""
     import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "jagged_hstu_attention_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+    files = glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))
+    for f in sorted(f for f in files if os.path.basename(f) != "reorder.hip"):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())

@@ -81,9 +81,9 @@ template <typename T, int D> struct alignas(16) KvSmem {
 
 template <typename T, int D, int NT = kThreads>
 __device__ __forceinline__ void issue_kv(KvSmem<T, D>& sm, int buf, const T* Kh, const T* Vh, int64_t ld, int key0,
-                                         int nvalid, int tid) {
-  tile_load_async<T, D, BN, NT>(sm.k[buf], Kh + key0 * ld, ld, nvalid, tid);
-  tile_load_async<T, D, BN, NT>(sm.v[buf], Vh + key0 * ld, ld, nvalid, tid);
+                                         int nvalid, int tid, uint32_t lane_off) {
+  tile_load_async<T, D, BN, NT>(sm.k[buf], Kh + key0 * ld, ld, nvalid, tid, lane_off);
+  tile_load_async<T, D, BN, NT>(sm.v[buf], Vh + key0 * ld, ld, nvalid, tid, lane_off);
 }
 
 // The exact-bucket table and edges (once per workgroup) ...
@@ -156,6 +156,12 @@ __device__ __forceinline__ int q_segments(const AttnParams& p, int b, Seg* seg) 
   return 2;
 }
 
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Steps of BQ query rows, over the (at most two) segments, from position
 // `start` on.  Segments are held in scalar fields (selected by index) so that
 // the iterator stays in registers.
@@ -189,6 +195,19 @@ struct StepIter {
     si = 0;
     q0 = max(p0, start);
     norm();
+    // the fields derive from wave-uniform values; readfirstlane keeps them in
+    // scalar registers (as vector registers they could be spilled, and every
+    // scratch reload waits for all outstanding loads, the tile prefetch too)
+    r0 = uni64(r0);
+    r1 = uni64(r1);
+    p0 = __builtin_amdgcn_readfirstlane(p0);
+    p1 = __builtin_amdgcn_readfirstlane(p1);
+    e0 = __builtin_amdgcn_readfirstlane(e0);
+    e1 = __builtin_amdgcn_readfirstlane(e1);
+    nseg = __builtin_amdgcn_readfirstlane(nseg);
+    start = __builtin_amdgcn_readfirstlane(start);
+    si = __builtin_amdgcn_readfirstlane(si);
+    q0 = __builtin_amdgcn_readfirstlane(q0);
   }
   __device__ __forceinline__ bool valid() const { return si < nseg; }
   __device__ __forceinline__ int nq() const { return min(BQ, seg_end(si) - q0); }
@@ -287,6 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
   ops.init(lane);
   const int H = p.H, NB = p.NB;
   const int64_t ld = (int64_t)H * D;
+  const uint32_t lane_off = tile_lane_offset<T, D, kThreads>(tid, ld);
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
@@ -330,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
     ln.ts64 = tsq;
     ln.tsr = lt.rel;
     int64_t tsv = 0;
-    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid);
+    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid, lane_off);
     if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
     if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, min(BN, kv_len), lane, base);
     wait_loads();
@@ -342,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
       const bool more = kt + 1 < n_kt;
       if (more) {
         const int nk0 = key0 + BN, nnv = min(BN, kv_len - nk0);
-        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid);
+        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
         if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
       }
       const TsTile<BN>& ts = sm.ts[cur];
@@ -513,6 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
   ops.init(lane);
   const int H = p.H, NB = p.NB;
   const int64_t ld = (int64_t)H * D;
+  const uint32_t lane_off = tile_lane_offset<T, D, kThreads>(tid, ld);
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
@@ -568,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
     si.init(p, it.b, it.pos0);
     int cur = 0;
     if (si.valid()) {
-      issue_kv<T, D>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid);
+      issue_kv<T, D>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid, lane_off);
       if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
       if (wave == 0) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
     }
@@ -580,7 +601,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
       StepIter nx = si;
       nx.next();
       if (nx.valid()) {
-        issue_kv<T, D>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid);
+        issue_kv<T, D>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid, lane_off);
         if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
       }
       const TsTile<BQ>& ts = sm.ts[cur];
@@ -683,57 +704,113 @@ __device__ __forceinline__ void contract_half(f32x16* out, const char* __restric
     }
 }
 
-// SiLU / gradient of one block (16 values per lane), packed to bf16, with the
-// d(ts_weights) contributions: exact modes add per element (key = bucket),
-// plan modes sum per passed edge (key = edges passed) and add per step.
-template <int MODE>
-__device__ __forceinline__ void pair_elem(u32x4* own_p, u32x4* own_g, float* dwl, const f32x16& s, const f32x16& dp,
-                                          const float* cb, const int* key, float beta, bool masked, int lo_row,
-                                          int hi_row, int g, bool kvalid, int blo) {
-  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    float a2[2], g2[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float y = fmaf(s[i + e], beta, cb[i + e]);
-      const float sg = sigmoid_y(y);
-      const float a = y * sg;
-      const float u = fmaf(-a, sg, a);  // a' (1 - sigma)
-      const float gg = dp[i + e] * fmaf(u, kNegLn2, sg);
-      const int r = acc_row(i + e, g);
-      const bool vis = !masked || (r >= lo_row && r < hi_row);
-      a2[e] = vis ? a : 0.0f;
-      g2[e] = vis ? gg : 0.0f;
-      if constexpr (MODE >= kModeLut) {
-        atomicAdd(&dwl[key[i + e]], kvalid ? g2[e] : 0.0f);
-      } else {
-        s0 += g2[e];
-        if constexpr (MODE != kModeConst) s1 += key[i + e] >= 1 ? g2[e] : 0.0f;
-        if constexpr (MODE == kModeThr3) {
-          s2 += key[i + e] >= 2 ? g2[e] : 0.0f;
-          s3 += key[i + e] >= 3 ? g2[e] : 0.0f;
-        }
-      }
-    }
-    own_p[i >> 3][(i & 7) >> 1] = pack_bf16x2(a2[0], a2[1]);
-    own_g[i >> 3][(i & 7) >> 1] = pack_bf16x2(g2[0], g2[1]);
-  }
-  if constexpr (MODE < kModeLut) {
-    if (kvalid) {
-      if (s0 != s1) atomicAdd(&dwl[blo], s0 - s1);
-      if (s1 != s2) atomicAdd(&dwl[blo + 1], s1 - s2);
-      if (s2 != s3) atomicAdd(&dwl[blo + 2], s2 - s3);
-      if (s3 != 0.0f) atomicAdd(&dwl[blo + 3], s3);
-    }
-  }
-}
-
 __device__ __forceinline__ void pack16(u32x4* dst, const float* v) {
 #pragma unroll
   for (int u = 0; u < 2; ++u)
     dst[u] = u32x4{pack_bf16x2(v[8 * u], v[8 * u + 1]), pack_bf16x2(v[8 * u + 2], v[8 * u + 3]),
                    pack_bf16x2(v[8 * u + 4], v[8 * u + 5]), pack_bf16x2(v[8 * u + 6], v[8 * u + 7])};
+}
+
+// SiLU and its gradient for one element: P = a' (scaled SiLU) and G.
+__device__ __forceinline__ void silu_grad(float s, float dp, float beta, float c, float& a, float& gg) {
+  const float y = fmaf(s, beta, c);
+  const float sg = sigmoid_y(y);
+  a = y * sg;
+  const float u = fmaf(-a, sg, a);  // a' (1 - sigma)
+  gg = dp * fmaf(u, kNegLn2, sg);
+}
+
+// Elementwise part of an unmasked step under a plan mode (kModeConst, Thr1,
+// Thr3): each element's bias by compares of the other row's timestamp offset
+// (rows[], this lane's four-row runs) with the lane's thresholds, SiLU and its
+// gradient, P and G packed to bf16, and the d(ts_weights) contributions summed
+// per passed edge and added once per step.  An edge the tile does not cross is
+// never passed, so its sum is zero.
+template <int MODE>
+__device__ __forceinline__ void pair_plan(u32x4* own_p, u32x4* own_g, float* dwl, const f32x16& s, const f32x16& dp,
+                                          const int32_t* __restrict__ rows, float beta, float c0, float c1, float c2,
+                                          float c3, int32_t t1, int32_t t2, int32_t t3, int blo) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  float pa[16], pg[16];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    int4 v4 = {0, 0, 0, 0};
+    if constexpr (MODE != kModeConst) v4 = *reinterpret_cast<const int4*>(rows + q4 * 8);
+    const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * q4 + e;
+      float c = c0;
+      bool p1 = false, p2 = false, p3 = false;
+      if constexpr (MODE != kModeConst) {
+        p1 = vv[e] <= t1;
+        c = p1 ? c1 : c;
+      }
+      if constexpr (MODE == kModeThr3) {
+        p2 = vv[e] <= t2;
+        p3 = vv[e] <= t3;
+        c = p2 ? c2 : c;
+        c = p3 ? c3 : c;
+      }
+      silu_grad(s[i], dp[i], beta, c, pa[i], pg[i]);
+      s0 += pg[i];
+      if constexpr (MODE != kModeConst) s1 += p1 ? pg[i] : 0.0f;
+      if constexpr (MODE == kModeThr3) {
+        s2 += p2 ? pg[i] : 0.0f;
+        s3 += p3 ? pg[i] : 0.0f;
+      }
+    }
+  }
+  pack16(own_p, pa);
+  pack16(own_g, pg);
+  atomicAdd(&dwl[blo], s0 - s1);
+  if constexpr (MODE != kModeConst) atomicAdd(&dwl[blo + 1], s1 - s2);
+  if constexpr (MODE == kModeThr3) {
+    atomicAdd(&dwl[blo + 2], s2 - s3);
+    atomicAdd(&dwl[blo + 3], s3);
+  }
+}
+
+// Elementwise part with the exact bucket per element (32-bit offsets from the
+// table, or WIDE: 64-bit timestamps), the causal / row-count mask when MASKED
+// (row r of the block is visible iff lo_row <= r < hi_row), and a
+// d(ts_weights) contribution per element.  A key lane past the item's end
+// has dp = 0 (its V operand is zero), so its G and contributions vanish.
+template <bool WIDE, bool MASKED>
+__device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dwl, const f32x16& s, const f32x16& dp,
+                                           const TsTile<BQ>& ts, int blk, int g, float beta, int32_t tsr,
+                                           int64_t tsr64, const BiasLds& bl, int nb, int lo_row, int hi_row) {
+  float pa[16], pg[16];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int r0 = q4 * 8 + 4 * g;
+    int4 v4 = {0, 0, 0, 0};
+    if constexpr (!WIDE) v4 = *reinterpret_cast<const int4*>(ts.u + blk * 32 + r0);
+    const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * q4 + e;
+      int b;
+      if constexpr (WIDE) {
+        b = lut_bucket64(ts.t64[blk * 32 + r0 + e] - tsr64, nb, bl.lut);
+      } else {
+        const int32_t d = vv[e] - tsr;
+        b = lut_bucket((uint32_t)(d < 0 ? -d : d), bl.lut);
+      }
+      float a, gg;
+      silu_grad(s[i], dp[i], beta, bl.c[b], a, gg);
+      if constexpr (MASKED) {
+        const bool vis = r0 + e >= lo_row && r0 + e < hi_row;
+        a = vis ? a : 0.0f;
+        gg = vis ? gg : 0.0f;
+      }
+      pa[i] = a;
+      pg[i] = gg;
+      atomicAdd(&dwl[b], gg);
+    }
+  }
+  pack16(own_p, pa);
+  pack16(own_g, pg);
 }
 
 }  // namespace
@@ -746,7 +823,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const Attn
   constexpr int KB = D / 64;
   __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
   __shared__ BiasLds bl;
-  __shared__ float dwbins[kPairDwCopies][kMaxBuckets + 1];
+  __shared__ float dwbins[kPairDwCopies][kMaxBuckets + kPad];  // plan sums touch up to b_lo + 3
   __shared__ u32x4 xch[8][4][64];  // per wave: P (2 operands) and G (2 operands), lane-contiguous
   __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
@@ -757,6 +834,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const Attn
   to.init(lane, hf);
   const int H = p.H, NB = p.NB;
   const int64_t ld = (int64_t)H * D;
+  const uint32_t lane_off = tile_lane_offset<T, D, NT>(tid, ld);
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
@@ -790,7 +868,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const Attn
       }
     }
     load_bias_values<T, NT>(bl, p, h, tid);
-    for (int i = tid; i < kPairDwCopies * (kMaxBuckets + 1); i += NT) (&dwbins[0][0])[i] = 0.0f;
+    for (int i = tid; i < kPairDwCopies * (kMaxBuckets + kPad); i += NT) (&dwbins[0][0])[i] = 0.0f;
     f32x16 dkacc[KB], dvacc[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -806,7 +884,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const Attn
     si.init(p, it.b, it.pos0);
     int cur = 0;
     if (si.valid()) {
-      issue_kv<T, D, NT>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid);
+      issue_kv<T, D, NT>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid, lane_off);
       if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
       if (wave == 0) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
     }
@@ -818,7 +896,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const Attn
       StepIter nx = si;
       nx.next();
       if (nx.valid()) {
-        issue_kv<T, D, NT>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid);
+        issue_kv<T, D, NT>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid, lane_off);
         if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
       }
       const TsTile<BQ>& ts = sm.ts[cur];
@@ -832,29 +910,31 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const Attn
 
       const f32x16 s = tile_mma_rows_o<D>(qb, lo, hf, kop);
       const f32x16 dp = tile_mma_rows_o<D>(db, lo, hf, vop);
-      float cb[16];
-      int key[16];
-      // The plan is only used in unmasked steps, but computing it always keeps
-      // it out of a conditional assignment (which would put it in memory).
-      const int2 br = ts.blk[hf];  // the plan covers this wave's block only
-      const Plan pl = make_plan<-1>(lt.rel, kvalid, br.x, br.y, bl);
-      const int pmode = wave_mode(pl.n);
-      const int mode = masked ? (fast ? kModeLut : kModeWide) : pmode;
-      if (masked)
-        block_bias_mode<-1, BQ, true, true>(cb, key, mode, pl, lt.rel, tsk, ts, hf, g, bl, NB);
-      else
-        block_bias_mode<-1, BQ, true, false>(cb, key, mode, pl, lt.rel, tsk, ts, hf, g, bl, NB);
-      // SiLU, its gradient, P and G packed to bf16 and exchanged with the
-      // partner wave, and the d(ts_weights) contributions (per mode).
+      // SiLU, its gradient, P and G packed to bf16 (exchanged with the partner
+      // wave below), and the d(ts_weights) contributions, per bias mode.
       u32x4 own_p[2], own_g[2];
-      if (mode >= kModeLut)
-        pair_elem<kModeLut>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
-      else if (mode == kModeConst)
-        pair_elem<kModeConst>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
-      else if (mode == kModeThr1)
-        pair_elem<kModeThr1>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
-      else
-        pair_elem<kModeThr3>(own_p, own_g, dwl, s, dp, cb, key, beta, masked, lo_row, hi_row, g, kvalid, pl.blo);
+      if (masked) {
+        if (fast)
+          pair_exact<false, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
+        else
+          pair_exact<true, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
+      } else {
+        const int2 br = ts.blk[hf];  // the plan covers this wave's block only
+        const Plan pl = make_plan<-1>(lt.rel, kvalid, br.x, br.y, bl);
+        const int mode = wave_mode(pl.n);
+        const int32_t* rows = (pl.flip ? ts.nu : ts.u) + hf * 32 + 4 * g;
+#define HSTU_PLAN(M) \
+  pair_plan<M>(own_p, own_g, dwl, s, dp, rows, beta, pl.c0, pl.c1, pl.c2, pl.c3, pl.t1, pl.t2, pl.t3, pl.blo)
+        if (mode == kModeConst)
+          HSTU_PLAN(kModeConst);
+        else if (mode == kModeThr1)
+          HSTU_PLAN(kModeThr1);
+        else if (mode == kModeThr3)
+          HSTU_PLAN(kModeThr3);
+        else
+          pair_exact<false, false>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, 0, BQ);
+#undef HSTU_PLAN
+      }
       xch[wave][0][lane] = own_p[0];
       xch[wave][1][lane] = own_p[1];
       xch[wave][2][lane] = own_g[0];
@@ -934,6 +1014,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
   ops.init(lane);
   const int H = p.H, NB = p.NB;
   const int64_t ld = (int64_t)H * D;
+  const uint32_t lane_off = tile_lane_offset<T, D, kThreads>(tid, ld);
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
@@ -982,7 +1063,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
     ln.ts64 = tsq;
     ln.tsr = lt.rel;
     int64_t tsv = 0;
-    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid);
+    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid, lane_off);
     if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
     if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, min(BN, kv_len), lane, base);
     wait_loads();
@@ -994,7 +1075,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
       const bool more = kt + 1 < n_kt;
       if (more) {
         const int nk0 = key0 + BN, nnv = min(BN, kv_len - nk0);
-        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid);
+        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
         if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
       }
       const TsTile<BN>& ts = sm.ts[cur];

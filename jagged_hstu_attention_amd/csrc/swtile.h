@@ -41,44 +41,62 @@ template <typename T, int D> struct SwTile {
   }
 };
 
-// Issue the direct-to-LDS loads of ROWS rows (row r at src + r*ld) into `dst`.
-// The loads complete asynchronously (vmcnt); wait and barrier before reading.
-// A full tile (nvalid == ROWS) is addressed from the tile's first row (a
-// wave-uniform base) plus a 32-bit per-lane offset, which keeps the issue
-// nearly free of vector registers and instructions; a partial tile clamps
-// each row to the last valid one.
+// Byte offset, from a tile's first row in global memory, of the chunk that
+// lane `tid` loads in its wave's first direct-to-LDS instruction.  The wave's
+// later instructions (every NT/64-th) fill slots NT further on: rows NT/C
+// further down with the same chunk order (the swizzle repeats every 16 rows or
+// fewer), so one offset per lane serves them all, and all tiles with the same
+// row stride.
+template <typename T, int D, int NT>
+__device__ __forceinline__ uint32_t tile_lane_offset(int tid, int64_t ld) {
+  using S = SwTile<T, D>;
+  static_assert((NT / 16) % 16 == 0, "the swizzle must repeat between a wave's instructions");
+  const int G = tid >> 4;
+  const int lin = (G << 4) | ((tid & 15) ^ S::f(G));
+  return (uint32_t)((lin / S::C) * ld + (lin % S::C) * S::kElems) * (uint32_t)sizeof(T);
+}
+
+// Buffer resource for raw (unstructured) loads from `base`: no stride, the
+// whole 32-bit offset range valid, default gfx9 data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+}
+
+// Issue the direct-to-LDS loads of ROWS rows (row r at src + r*ld) into `dst`,
+// as buffer loads from a resource based at the tile's first row: the lane's
+// 32-bit offset is the only vector operand.  The loads complete asynchronously
+// (vmcnt); wait and barrier before reading.  A full tile (nvalid == ROWS) uses
+// the offset from tile_lane_offset plus a scalar row shift per instruction; a
+// partial tile clamps each row to the last valid one.  The caller must ensure
+// ROWS * ld * sizeof(T) < 2^32.
 template <typename T, int D, int ROWS, int NT>
 __device__ __forceinline__ void tile_load_async(T* __restrict__ dst, const T* __restrict__ src, int64_t ld,
-                                                int nvalid, int tid) {
+                                                int nvalid, int tid, uint32_t lane_off) {
   using S = SwTile<T, D>;
+  using LdsPtr = __attribute__((address_space(3))) void*;
   constexpr int kInstr = ROWS * S::C / 64;
-  static_assert(ROWS * S::C % 64 == 0, "whole wave instructions");
-  // The per-lane addresses are cheap to recompute; the empty asm keeps the
-  // compiler from hoisting them out of the tile loop, where they would occupy
-  // registers (or be spilled and reloaded) for the whole loop.
+  constexpr int kWaves = NT / 64;
+  static_assert(ROWS * S::C % 64 == 0 && kInstr % kWaves == 0, "whole wave instructions");
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations stay scalar
-  int lane = tid & 63;
-  asm volatile("" : "+v"(lane));
+  const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src);
   if (nvalid >= ROWS) {
-    const char* base = reinterpret_cast<const char*>(src);
 #pragma unroll
-    for (int i = wave; i < kInstr; i += NT / 64) {
-      const int s = i * 64 + lane;
-      const int G = s >> 4;
-      const int lin = (G << 4) | ((s & 15) ^ S::f(G));
-      const uint32_t off = (uint32_t)((lin / S::C) * (int)ld + (lin % S::C) * S::kElems) * (uint32_t)sizeof(T);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const T*>(base + off), dst + i * 64 * S::kElems, 16, 0, 0);
+    for (int k = 0; k < kInstr / kWaves; ++k) {
+      const uint32_t shift = (uint32_t)(k * (NT / S::C) * ld * (int64_t)sizeof(T));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(dst + (wave + k * kWaves) * 64 * S::kElems), 16,
+                                               lane_off, shift, 0, 0);
     }
     return;
   }
+  const int lane = tid & 63;
 #pragma unroll
-  for (int i = wave; i < kInstr; i += NT / 64) {
+  for (int i = wave; i < kInstr; i += kWaves) {
     const int s = i * 64 + lane;
     const int G = s >> 4;
     const int lin = (G << 4) | ((s & 15) ^ S::f(G));
     const int row = min(lin / S::C, nvalid - 1);
-    const T* g = src + row * ld + (lin % S::C) * S::kElems;
-    __builtin_amdgcn_global_load_lds(g, dst + i * 64 * S::kElems, 16, 0, 0);
+    const uint32_t off = (uint32_t)(row * ld + (lin % S::C) * S::kElems) * (uint32_t)sizeof(T);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(dst + i * 64 * S::kElems), 16, off, 0, 0, 0);
   }
 }
 
