@@ -361,7 +361,7 @@ def main():
     achieved = kfl[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(dom),
-                "kernel": {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_pair_kernel", "bwd_q": "bwd_q_kernel"}[dom],
+                "kernel": {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_half_kernel", "bwd_q": "bwd_q_kernel"}[dom],
                 "ms_per_launch": round(kms[dom], 4), "flop_per_launch": kfl[dom]}
 
     extra = {

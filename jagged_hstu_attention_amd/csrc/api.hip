@@ -171,7 +171,7 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
   Layout l{};
   const int64_t segs = p->cp_size == 1 ? 1 : 2;
   l.max_qtiles = cdiv(p->total_q, hstu::attn_q_tile_rows()) + segs * p->num_seqs;
-  l.max_ktiles = backward ? cdiv(p->total_kv, hstu::attn_bwd_key_tile()) + p->num_seqs : 0;
+  l.max_ktiles = backward ? cdiv(p->total_kv, hstu::attn_bwd_key_tile(p->dtype == HSTU_BF16, (int)p->d_qk)) + p->num_seqs : 0;
   size_t off = 0;
   l.ctr = off;
   off = align_up(off + hstu::kCtrCount * sizeof(int));
@@ -290,7 +290,7 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   sp.cp_rank = (int)p->cp_rank;
   sp.q_tile = hstu::attn_q_tile_rows();
   sp.q_cost_tile = hstu::attn_k_tile_keys();
-  sp.k_tile = backward ? hstu::attn_bwd_key_tile() : 0;
+  sp.k_tile = backward ? hstu::attn_bwd_key_tile(p->dtype == HSTU_BF16, (int)p->d_qk) : 0;
   sp.k_cost_tile = hstu::attn_bwd_q_step();
   // costs are at most ceil(max_seq_len / 64) + 2 tiles
   const int64_t max_cost = cdiv(p->max_seq_len, std::min(hstu::attn_k_tile_keys(), hstu::attn_bwd_q_step())) + 3;

@@ -41,7 +41,7 @@ hipError_t launch_attn(const AttnParams& p, bool bf16, int d, int which, int max
 
 int attn_q_tile_rows();   // query rows per forward / dQ item
 int attn_k_tile_keys();   // keys per tile in the forward / dQ loops
-int attn_bwd_key_tile();  // keys per dK/dV item
+int attn_bwd_key_tile(bool bf16, int d);  // keys per dK/dV item
 int attn_bwd_q_step();    // query rows per step of the dK/dV loop
 
 // Scheduler: builds the descending-cost tile lists, the rank-local offsets,
