@@ -70,9 +70,21 @@ template <> struct Mma<float> {
 // Row (within its 32-row block) of accumulator value i held by lane group g.
 __device__ __forceinline__ int acc_row(int i, int g) { return ((i >> 2) << 3) + (g << 2) + (i & 3); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest even) and packed, lo in the low half:
+// one v_cvt_pk_bf16_f32 (converting the halves separately and merging them
+// takes three instructions).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// Eight floats as one bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* v) {
+  const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T x);

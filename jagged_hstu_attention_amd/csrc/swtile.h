@@ -137,8 +137,7 @@ __device__ __forceinline__ void tile_contract_block(f32x16* out, const T* __rest
     bf16x8 b[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b[u][j] = (__bf16)vals[8 * u + j];
+      b[u] = to_bf16x8(vals + 8 * u);
     const int m = lane & 15, q = lane >> 4;
     const int rb = blk * 32 + 4 * g + (m >> 2);
     const int cb = 16 * (q & 1) + 4 * (m & 3);
@@ -238,8 +237,7 @@ __device__ __forceinline__ void tile_contract_block_o(f32x16* out, const char* _
   bf16x8 b[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[u][j] = (__bf16)vals[8 * u + j];
+    b[u] = to_bf16x8(vals + 8 * u);
 #pragma unroll
   for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
@@ -299,8 +297,7 @@ __device__ __forceinline__ void tr_mma(f32x16* out, const bf16x8* t, const float
   bf16x8 b[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[u][j] = (__bf16)vals[8 * u + j];
+    b[u] = to_bf16x8(vals + 8 * u);
 #pragma unroll
   for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
