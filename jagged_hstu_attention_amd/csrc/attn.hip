@@ -773,14 +773,17 @@ __device__ __forceinline__ void pair_plan(u32x4* own_p, u32x4* own_g, float* dwl
 
 // Elementwise part with the exact bucket per element (32-bit offsets from the
 // table, or WIDE: 64-bit timestamps), the causal / row-count mask when MASKED
-// (row r of the block is visible iff lo_row <= r < hi_row), and a
-// d(ts_weights) contribution per element.  A key lane past the item's end
-// has dp = 0 (its V operand is zero), so its G and contributions vanish.
+// (row r of the block is visible iff lo_row <= r < hi_row), and the
+// d(ts_weights) contributions summed per run of equal buckets.  A key lane
+// past the item's end has dp = 0 (its V operand is zero), so its G and
+// contributions vanish.
 template <bool WIDE, bool MASKED>
 __device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dwl, const f32x16& s, const f32x16& dp,
                                            const TsTile<BQ>& ts, int blk, int g, float beta, int32_t tsr,
                                            int64_t tsr64, const BiasLds& bl, int nb, int lo_row, int hi_row) {
   float pa[16], pg[16];
+  int cur = 0;        // bucket of the running d(ts_weights) sum
+  float run = 0.0f;   // the running sum
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int r0 = q4 * 8 + 4 * g;
@@ -803,12 +806,28 @@ __device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dw
         const bool vis = r0 + e >= lo_row && r0 + e < hi_row;
         a = vis ? a : 0.0f;
         gg = vis ? gg : 0.0f;
+        if (i > 0) b = vis ? b : cur;  // a masked element never ends a run
       }
       pa[i] = a;
       pg[i] = gg;
-      atomicAdd(&dwl[b], gg);
+      // d(ts_weights): a lane's rows come in order and their bucket changes
+      // rarely, so each lane keeps a running sum per bucket and adds it to
+      // the bins when the bucket changes (one atomic per element would make
+      // the lanes that share a bucket collide on one address)
+      if (i == 0) {
+        cur = b;
+        run = gg;
+      } else {
+        if (b != cur) {
+          atomicAdd(&dwl[cur], run);
+          cur = b;
+          run = 0.0f;
+        }
+        run += gg;
+      }
     }
   }
+  atomicAdd(&dwl[cur], run);
   pack16(own_p, pa);
   pack16(own_g, pg);
 }
