@@ -1005,7 +1005,7 @@ constexpr int kHalfDwCopies = 4;
 template <int D> struct alignas(16) HalfSmem {
   __bf16 q[BQ * D];
   __bf16 d[BQ * D];
-  TsTile<BQ> ts;
+  TsTile<BQ> ts[2];  // this step's and the next step's timestamps
 };
 
 }  // namespace
@@ -1086,16 +1086,20 @@ __global__ __launch_bounds__(kHalfThreads, 2) void bwd_kv_half_kernel(const Attn
       if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
     }
     wait_loads();
-    if (wave == 0 && si.valid()) ts_tile_fill<BQ>(sm.ts, tsv, si.nq(), lane, base);
+    if (wave == 0 && si.valid()) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
     __syncthreads();
     const char* qb = reinterpret_cast<const char*>(sm.q);
     const char* db = reinterpret_cast<const char*>(sm.d);
+    int cts = 0;
     while (si.valid()) {
       const int q0 = si.q0;
       const int nq = si.nq();
       StepIter nx = si;
       nx.next();
-      const TsTile<BQ>& ts = sm.ts;
+      // the next step's timestamps are loaded now and staged after the
+      // elementwise part, off the path between the tile barriers
+      if (nx.valid() && wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
+      const TsTile<BQ>& ts = sm.ts[cts];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       // rows r of this wave's block are visible iff lo_row <= r < hi_row
@@ -1131,6 +1135,7 @@ __global__ __launch_bounds__(kHalfThreads, 2) void bwd_kv_half_kernel(const Attn
       xch[wave][1][lane] = own_p[1];
       xch[wave][2][lane] = own_g[0];
       xch[wave][3][lane] = own_g[1];
+      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cts ^ 1], tsv, nx.nq(), lane, base);
       __syncthreads();
       const int pw = wave ^ 2;
       const u32x4 par_p[2] = {xch[pw][0][lane], xch[pw][1][lane]};
@@ -1144,12 +1149,11 @@ __global__ __launch_bounds__(kHalfThreads, 2) void bwd_kv_half_kernel(const Attn
       if (nx.valid()) {
         tile_load_async<T, D, BQ, NT>(sm.q, Qh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
         tile_load_async<T, D, BQ, NT>(sm.d, dOh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
-        if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
       }
       wait_loads();
-      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts, tsv, nx.nq(), lane, base);
       __syncthreads();
       si = nx;
+      cts ^= 1;
     }
     if (kvalid) {
       store_scaled<T, D / 2>(dK + krow * ld + h * D + hf * (D / 2), dkacc, p.alpha, g);
