@@ -260,11 +260,11 @@ __device__ __forceinline__ void silu_block(float* pv, const f32x16& s, const flo
 }
 
 // One 64-key tile: per 32-key block, the score MFMAs, the block's bias (their
-// latency overlaps), SiLU and the P V MFMAs.
-template <typename T, int D, bool MASK>
+// latency overlaps), SiLU and the P V MFMAs; `mid` runs between the blocks.
+template <typename T, int D, bool MASK, typename Mid>
 __device__ __forceinline__ void fwd_tile(f32x16* oacc, const T* kt, const T* vt, const TsTile<BN>& ts,
                                          const TileOps<T, D>& ops, const typename Mma<T>::operand* qop, int mode,
-                                         const Plan& pl, const FwdLane& ln, const BiasLds& bl) {
+                                         const Plan& pl, const FwdLane& ln, const BiasLds& bl, Mid&& mid) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     f32x16 s;
@@ -289,6 +289,7 @@ __device__ __forceinline__ void fwd_tile(f32x16* oacc, const T* kt, const T* vt,
       tr_mma<D>(oacc, tv, pv);
     else
       ops.contract(oacc, vt, pv, blk);
+    if (blk == 0) mid();
   }
 }
 
@@ -361,21 +362,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
       const int nvalid = min(BN, kv_len - key0);
       const bool more = kt + 1 < n_kt;
       if (more) {
+        // the timestamps first: they are staged half-way through the tile
+        // (below), where waiting for them leaves the tile loads in flight
         const int nk0 = key0 + BN, nnv = min(BN, kv_len - nk0);
-        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
         if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
       }
+      const auto stage = [&] {
+        if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
+      };
       const TsTile<BN>& ts = sm.ts[cur];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       ln.lim = qpos - key0;
       if (key0 + BN - 1 > wave_qmin || nvalid < BN || !fast) {
-        fwd_tile<T, D, true>(oacc, sm.k[cur], sm.v[cur], ts, ops, qop, fast ? kModeLut : kModeWide, Plan{}, ln, bl);
+        fwd_tile<T, D, true>(oacc, sm.k[cur], sm.v[cur], ts, ops, qop, fast ? kModeLut : kModeWide, Plan{}, ln, bl,
+                             stage);
       } else {
         const Plan pl = make_plan<+1>(ln.tsr, qvalid, hdr.x, hdr.y, bl);
-        fwd_tile<T, D, false>(oacc, sm.k[cur], sm.v[cur], ts, ops, qop, wave_mode(pl.n), pl, ln, bl);
+        fwd_tile<T, D, false>(oacc, sm.k[cur], sm.v[cur], ts, ops, qop, wave_mode(pl.n), pl, ln, bl, stage);
       }
-      if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
       wait_loads();
       __syncthreads();
     }
@@ -1593,11 +1600,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_pipe_kernel(const AttnPara
 // ---------------------------------------------------------------------------
 namespace {
 
-template <typename T, int D, bool MASK>
+template <typename T, int D, bool MASK, typename Mid>
 __device__ __forceinline__ void q_tile(f32x16* dqacc, const T* kt, const T* vt, const TsTile<BN>& ts,
                                        const TileOps<T, D>& ops, const typename Mma<T>::operand* qop,
                                        const typename Mma<T>::operand* dop, int mode, const Plan& pl,
-                                       const FwdLane& ln, const BiasLds& bl) {
+                                       const FwdLane& ln, const BiasLds& bl, Mid&& mid) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const f32x16 s = ops.rows(kt, blk, qop);
@@ -1615,6 +1622,7 @@ __device__ __forceinline__ void q_tile(f32x16* dqacc, const T* kt, const T* vt, 
       gv[i] = (MASK && acc_row(i, ln.g) > ln.lim - 32 * blk) ? 0.0f : gg;
     }
     ops.contract(dqacc, kt, gv, blk);
+    if (blk == 0) mid();
   }
 }
 
@@ -1692,22 +1700,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
       const int nvalid = min(BN, kv_len - key0);
       const bool more = kt + 1 < n_kt;
       if (more) {
+        // the timestamps first: they are staged half-way through the tile
+        // (below), where waiting for them leaves the tile loads in flight
         const int nk0 = key0 + BN, nnv = min(BN, kv_len - nk0);
-        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
         if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
       }
+      const auto stage = [&] {
+        if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
+      };
       const TsTile<BN>& ts = sm.ts[cur];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       ln.lim = qpos - key0;
       if (key0 + BN - 1 > wave_qmin || nvalid < BN || !fast) {
         q_tile<T, D, true>(dqacc, sm.k[cur], sm.v[cur], ts, ops, qop, dop, fast ? kModeLut : kModeWide, Plan{}, ln,
-                           bl);
+                           bl, stage);
       } else {
         const Plan pl = make_plan<+1>(ln.tsr, qvalid, hdr.x, hdr.y, bl);
-        q_tile<T, D, false>(dqacc, sm.k[cur], sm.v[cur], ts, ops, qop, dop, wave_mode(pl.n), pl, ln, bl);
+        q_tile<T, D, false>(dqacc, sm.k[cur], sm.v[cur], ts, ops, qop, dop, wave_mode(pl.n), pl, ln, bl, stage);
       }
-      if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
       wait_loads();
       __syncthreads();
     }
