@@ -158,7 +158,7 @@ def stored_traffic(kernel):
 
 COUNTER_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o <name> -- "
                "python bench.py --counter-run")
-# Substrings of the kernel symbols (the dK/dV pass runs bwd_kv_pair_kernel for
+# Substrings of the kernel symbols (the dK/dV pass runs bwd_kv_half_kernel for
 # bf16 with d >= 64, bwd_kv_kernel otherwise).
 KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_", "bwd_q": "bwd_q_kernel", "sched": "sched_kernel"}
 

@@ -664,19 +664,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Backward, key-major pass for bf16 with d in {64, 128}: eight waves per item
-// of 128 keys.  Waves w and w + 4 share keys 32 (w % 4) .. + 31.  In every step
-// of 64 query rows, wave w computes S and dP only for the 32-row block
-// hf = w / 4, and the pair swaps the resulting P and G through LDS; each wave
-// then accumulates dV and dK over both blocks for its half hf of the head
-// dimension.  A wave so holds half the accumulators of the four-wave kernel
-// and fits in 256 registers: two waves share each SIMD and overlap their
-// MFMA and VALU work.
+// Backward, key-major pass for bf16 with d in {64, 128}: items of 64 keys,
+// four waves per workgroup, two workgroups per CU.  Waves w and w ^ 2 share
+// keys 32 (w % 2) .. + 31.  In every step of 64 query rows, wave w computes S
+// and dP only for the 32-row block hf = w / 2, and the pair swaps the
+// resulting P and G through LDS; each wave then accumulates dV and dK over
+// both blocks for its half hf of the head dimension.  A wave so holds half
+// the accumulators a full-width wave would and fits in 256 registers.  The
+// query/dO tile is single-buffered (the workgroup fits in half the CU's LDS):
+// while one workgroup waits for its next tile, the other computes.
 // ---------------------------------------------------------------------------
 namespace {
-
-constexpr int kPairThreads = 512;
-constexpr int kPairDwCopies = 16;
 
 // Transpose-read offsets of the d blocks in this wave's half.
 template <int D> struct HalfTrOffsets {
@@ -838,172 +836,6 @@ __device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dw
   pack16(own_p, pa);
   pack16(own_g, pg);
 }
-
-}  // namespace
-
-template <int D>
-__global__ __launch_bounds__(kPairThreads, 1) void bwd_kv_pair_kernel(const AttnParams p) {
-  using M = Mma<__bf16>;
-  using T = __bf16;
-  constexpr int NT = kPairThreads;
-  constexpr int KB = D / 64;
-  __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
-  __shared__ BiasLds bl;
-  __shared__ float dwbins[kPairDwCopies][kMaxBuckets + kPad];  // plan sums touch up to b_lo + 3
-  __shared__ u32x4 xch[8][4][64];  // per wave: P (2 operands) and G (2 operands), lane-contiguous
-  __shared__ int item_slot;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
-  const int kg = wave & 3, hf = wave >> 2;
-  LaneOffsets<D> lo;
-  lo.init(lane);
-  HalfTrOffsets<D> to;
-  to.init(lane, hf);
-  const int H = p.H, NB = p.NB;
-  const int64_t ld = (int64_t)H * D;
-  const uint32_t lane_off = tile_lane_offset<T, D, NT>(tid, ld);
-  const T* Q = static_cast<const T*>(p.q);
-  const T* K = static_cast<const T*>(p.k);
-  const T* V = static_cast<const T*>(p.v);
-  const T* dO = static_cast<const T*>(p.dout);
-  T* dK = static_cast<T*>(p.dk);
-  T* dV = static_cast<T*>(p.dv);
-  load_bucket_tables<NT>(bl, p, tid);
-  const int n_work = p.ctr[kCtrKTiles] * H;
-  float* dwl = dwbins[lane % kPairDwCopies];
-
-  for (;;) {
-    const int w = pop_item(&item_slot, p.ctr + kCtrKNext, tid);
-    if (w >= n_work) break;
-    const int h = w % H;
-    const Item it = p.kitems[w / H];
-    const int64_t seq0 = p.offsets[it.b];
-    const int64_t base = p.ts[seq0];
-    const int kj = kg * 32 + r32;
-    const bool kvalid = kj < it.n;
-    const int kpos = it.pos0 + kj;
-    const int64_t krow = (int64_t)it.row0 + kj;
-    const int64_t tsk = kvalid ? p.ts[krow] : 0;
-    bf16x8 kop[D / 16], vop[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kop[kk] = bf16x8{};
-      vop[kk] = bf16x8{};
-      if (kvalid) {
-        kop[kk] = M::load(K + krow * ld + h * D + kk * 16 + g * 8);
-        vop[kk] = M::load(V + krow * ld + h * D + kk * 16 + g * 8);
-      }
-    }
-    load_bias_values<T, NT>(bl, p, h, tid);
-    for (int i = tid; i < kPairDwCopies * (kMaxBuckets + kPad); i += NT) (&dwbins[0][0])[i] = 0.0f;
-    f32x16 dkacc[KB], dvacc[KB];
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      dkacc[i] = f32x16{};
-      dvacc[i] = f32x16{};
-    }
-    const int wave_kmax = it.pos0 + kg * 32 + 31;
-    const LaneTs lt = lane_ts(tsk, kvalid, base);
-    const float beta = kNegLog2e * p.alpha;
-
-    int64_t tsv = 0;
-    StepIter si;
-    si.init(p, it.b, it.pos0);
-    int cur = 0;
-    if (si.valid()) {
-      issue_kv<T, D, NT>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid, lane_off);
-      if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
-      if (wave == 0) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
-    }
-    wait_loads();
-    __syncthreads();
-    while (si.valid()) {
-      const int q0 = si.q0;
-      const int nq = si.nq();
-      StepIter nx = si;
-      nx.next();
-      if (nx.valid()) {
-        issue_kv<T, D, NT>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid, lane_off);
-        if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
-      }
-      const TsTile<BQ>& ts = sm.ts[cur];
-      const char* qb = reinterpret_cast<const char*>(sm.k[cur]);
-      const char* db = reinterpret_cast<const char*>(sm.v[cur]);
-      const int4 hdr = ts.hdr;
-      const bool fast = lt.fast && hdr.z == 0;
-      // rows r of this wave's block are visible iff lo_row <= r < hi_row
-      const int lo_row = kpos - q0 - 32 * hf, hi_row = nq - 32 * hf;
-      const bool masked = q0 + 32 * hf < wave_kmax || nq < BQ || !fast;
-
-      const f32x16 s = tile_mma_rows_o<D>(qb, lo, hf, kop);
-      const f32x16 dp = tile_mma_rows_o<D>(db, lo, hf, vop);
-      // SiLU, its gradient, P and G packed to bf16 (exchanged with the partner
-      // wave below), and the d(ts_weights) contributions, per bias mode.
-      u32x4 own_p[2], own_g[2];
-      if (masked) {
-        if (fast)
-          pair_exact<false, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
-        else
-          pair_exact<true, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
-      } else {
-        const int2 br = ts.blk[hf];  // the plan covers this wave's block only
-        const Plan pl = make_plan<-1>(lt.rel, kvalid, br.x, br.y, bl);
-        const int mode = wave_mode(pl.n);
-        const int32_t* rows = (pl.flip ? ts.nu : ts.u) + hf * 32 + 4 * g;
-#define HSTU_PLAN(M) \
-  pair_plan<M>(own_p, own_g, dwl, s, dp, rows, beta, pl.c0, pl.c1, pl.c2, pl.c3, pl.t1, pl.t2, pl.t3, pl.blo)
-        if (mode == kModeConst)
-          HSTU_PLAN(kModeConst);
-        else if (mode == kModeThr1)
-          HSTU_PLAN(kModeThr1);
-        else if (mode == kModeThr3)
-          HSTU_PLAN(kModeThr3);
-        else
-          pair_exact<false, false>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, 0, BQ);
-#undef HSTU_PLAN
-      }
-      xch[wave][0][lane] = own_p[0];
-      xch[wave][1][lane] = own_p[1];
-      xch[wave][2][lane] = own_g[0];
-      xch[wave][3][lane] = own_g[1];
-      __syncthreads();
-      const int pw = wave ^ 4;
-      const u32x4 par_p[2] = {xch[pw][0][lane], xch[pw][1][lane]};
-      const u32x4 par_g[2] = {xch[pw][2][lane], xch[pw][3][lane]};
-      contract_half<D>(dvacc, db, to, own_p, hf);
-      contract_half<D>(dkacc, qb, to, own_g, hf);
-      contract_half<D>(dvacc, db, to, par_p, hf ^ 1);
-      contract_half<D>(dkacc, qb, to, par_g, hf ^ 1);
-      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cur ^ 1], tsv, nx.nq(), lane, base);
-      wait_loads();
-      __syncthreads();
-      si = nx;
-      cur ^= 1;
-    }
-    if (kvalid) {
-      const int64_t row = (int64_t)it.row0 + kj;
-      store_scaled<T, D / 2>(dK + row * ld + h * D + hf * (D / 2), dkacc, p.alpha, g);
-      store_scaled<T, D / 2>(dV + row * ld + h * D + hf * (D / 2), dvacc, kNegLn2, g);
-    }
-    __syncthreads();
-    for (int i = tid; i < NB; i += NT) {
-      float v = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kPairDwCopies; ++c) v += dwbins[c][i];
-      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, p.alpha * v);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Backward, key-major pass for bf16 with d in {64, 128}: the pair scheme of
-// bwd_kv_pair_kernel on items of 64 keys, four waves per workgroup and two
-// workgroups per CU.  Waves w and w ^ 2 share keys 32 (w % 2) .. + 31; wave w
-// computes S and dP for the 32-row block hf = w / 2 of each 64-row step and
-// accumulates dV, dK for its half hf of the head dimension.  The query/dO tile
-// is single-buffered (the workgroup fits in half the CU's LDS); while one
-// workgroup waits for its next tile, the other computes.
-// ---------------------------------------------------------------------------
-namespace {
 
 constexpr int kHalfThreads = 256;
 constexpr int kHalfKeys = 64;
@@ -1177,423 +1009,6 @@ __global__ __launch_bounds__(kHalfThreads, 2) void bwd_kv_half_kernel(const Attn
 }
 
 // ---------------------------------------------------------------------------
-// Backward, key-major pass for bf16 with d in {64, 128}, software-pipelined.
-// Four waves, one per SIMD with the whole register file; lane (r32, g) of
-// wave w owns key 32w + r32 and the full head dimension.  Iteration t holds
-// three mutually independent pieces of work, emitted as one interleaved
-// stream so that a single wave keeps its VALU, its MFMA pipe and the LDS busy
-// together:
-//   - the elementwise part of step t (on S and dP from iteration t - 1),
-//   - the contractions of step t - 1 (dVᵀ += dOᵀ P, dKᵀ += Qᵀ G; transposed
-//     reads of tile t - 1, P and G from iteration t - 1),
-//   - S = Q Kᵀ and dP = dO Vᵀ of step t + 1 (row reads of tile t + 1).
-// Query/dO tiles rotate through four buffers (t - 1 and t + 1 read, t idle,
-// t + 2 in flight); one barrier per iteration.  Each bias mode has its own
-// copy of the iteration, so the stream is one basic block.
-// ---------------------------------------------------------------------------
-namespace {
-
-constexpr int kPipeBufs = 4;
-constexpr int kPipeDwCopies = 4;
-// step kinds of the pipelined kernel: plan modes, exact bucket (unmasked),
-// masked with 32-bit or 64-bit timestamp offsets
-constexpr int kStepConst = kModeConst, kStepThr1 = kModeThr1, kStepThr3 = kModeThr3, kStepLut = kModeLut,
-              kStepMasked = 5, kStepMaskedWide = 6;
-
-template <int D> struct alignas(16) PipeSmem {
-  __bf16 q[kPipeBufs][BQ * D];
-  __bf16 d[kPipeBufs][BQ * D];
-  TsTile<BQ> ts[kPipeBufs];
-};
-
-// out[dblk] += Xᵀ B over the 32 rows of block blk of a bf16 tile, for every
-// 32-column d block; B is the pair of packed bf16x8 operands of the block.
-template <int D>
-__device__ __forceinline__ void contract_full(f32x16* out, const char* __restrict__ base, const LaneOffsets<D>& lo,
-                                              const u32x4* b, int blk) {
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const char* p0 = base + lo.tr[j][0] + (blk * 32 + 16 * u) * D * 2;
-      const char* p1 = base + lo.tr[j][1] + (blk * 32 + 16 * u) * D * 2;
-      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
-      const short __attribute__((ext_vector_type(8))) a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      out[j] = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b[u]), out[j]);
-    }
-}
-
-// Operands of the MFMAs of chunk c (block c / 4, run q4 = c % 4) of an
-// iteration.  Contraction m of the chunk: operand u = q4 / 2 of the block,
-// d block (q4 % 2) * D/64 + m / 2, into dV (m even) or dK (m odd): the A
-// operand is a transposed read of tile t - 1.  Product m: number q4 *
-// kPerChunk + m of its block's chain, S (even) or dP (odd), kk = number / 2:
-// a row read of tile t (block 1, chunks 0-3) or t + 1 (block 0, chunks 4-7).
-template <int D> struct ChunkOps {
-  static constexpr int kPerChunk = D / 32;
-  bf16x8 ca[kPerChunk];
-  bf16x8 pa[kPerChunk];
-};
-
-template <int D>
-__device__ __forceinline__ void load_chunk_ops(ChunkOps<D>& o, int c, const char* __restrict__ qprev,
-                                               const char* __restrict__ dprev, const char* __restrict__ qcur,
-                                               const char* __restrict__ dcur, const char* __restrict__ qnext,
-                                               const char* __restrict__ dnext, const LaneOffsets<D>& lo) {
-  constexpr int kPerChunk = ChunkOps<D>::kPerChunk;
-  const int blk = c >> 2, q4 = c & 3;
-#pragma unroll
-  for (int m = 0; m < kPerChunk; ++m) {
-    const int which = m & 1, u = q4 >> 1, dblk = (q4 & 1) * (D / 64) + (m >> 1);
-    const char* base = which ? qprev : dprev;
-    const char* p0 = base + lo.tr[dblk][0] + (blk * 32 + 16 * u) * D * 2;
-    const char* p1 = base + lo.tr[dblk][1] + (blk * 32 + 16 * u) * D * 2;
-    const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
-    const short __attribute__((ext_vector_type(8))) a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-    o.ca[m] = __builtin_bit_cast(bf16x8, a);
-    const int j = q4 * kPerChunk + m, pw = j & 1, kk = j >> 1;
-    const char* pb = blk == 0 ? (pw ? dcur : qcur) : (pw ? dnext : qnext);
-    const int pblk = blk == 0 ? 1 : 0;
-    o.pa[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pb + lo.row[kk] + pblk * 32 * D * 2));
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void chunk_mfmas(const ChunkOps<D>& o, int c, f32x16* dkacc, f32x16* dvacc, f32x16* s,
-                                            f32x16* dp, const u32x4 (*P)[2], const u32x4 (*G)[2],
-                                            const bf16x8* kop, const bf16x8* vop) {
-  using M = Mma<__bf16>;
-  constexpr int kPerChunk = ChunkOps<D>::kPerChunk;
-  const int blk = c >> 2, q4 = c & 3;
-#pragma unroll
-  for (int m = 0; m < kPerChunk; ++m) {
-    const int which = m & 1, u = q4 >> 1, dblk = (q4 & 1) * (D / 64) + (m >> 1);
-    const u32x4 b = which ? G[blk][u] : P[blk][u];
-    f32x16& acc = which ? dkacc[dblk] : dvacc[dblk];
-    acc = M::mma(o.ca[m], __builtin_bit_cast(bf16x8, b), acc);
-    const int j = q4 * kPerChunk + m, pw = j & 1, kk = j >> 1;
-    const int pblk = blk == 0 ? 1 : 0;
-    f32x16& pacc = pw ? dp[pblk] : s[pblk];
-    pacc = M::mma(o.pa[m], pw ? vop[kk] : kop[kk], kk == 0 ? f32x16{} : pacc);
-  }
-}
-
-// One pipelined iteration for step kind `kind` (wave-uniform), in eight
-// chunks of four rows per lane.  Chunks 0-3: the elementwise part of block 0
-// of step t, the products of block 1 of step t (tile t) and the contractions
-// of block 0 of step t - 1 (tile t - 1).  Chunks 4-7: the elementwise part of
-// block 1, the products of block 0 of step t + 1 (tile t + 1; block 0's
-// values of step t are consumed by then) and the contractions of block 1 of
-// step t - 1.  P and G of a block are replaced once its contractions are
-// issued.  On entry s, dp hold block 0 of step t and P, G step t - 1; on exit
-// s, dp hold block 0 of step t + 1 and P, G step t.  The mode-dependent parts
-// (the bias of a chunk's elements, the mask, the d(ts_weights) updates) are
-// short uniform branches around a common block in which the chunk's MFMAs
-// interleave with its SiLU arithmetic; one body for all kinds keeps the
-// loop-carried registers in place.  Plan kinds use the thresholds (rows: the
-// step's timestamp offsets, u or ~u, offset by 4g); exact kinds the table;
-// masked kinds the visibility window [lo_row, hi_row).
-template <int D>
-__device__ __forceinline__ void pipe_iter(int kind, f32x16* dkacc, f32x16* dvacc, f32x16* s, f32x16* dp,
-                                          u32x4 (*P)[2], u32x4 (*G)[2], const char* __restrict__ qprev,
-                                          const char* __restrict__ dprev, const char* __restrict__ qcur,
-                                          const char* __restrict__ dcur, const char* __restrict__ qnext,
-                                          const char* __restrict__ dnext, const LaneOffsets<D>& lo,
-                                          const bf16x8* kop, const bf16x8* vop, float* dwl, float beta, float c0,
-                                          float c1, float c2, float c3, int32_t t1, int32_t t2, int32_t t3, int blo,
-                                          const int32_t* __restrict__ rows, const TsTile<BQ>& ts, int g,
-                                          int32_t tsr, int64_t tsr64, const BiasLds& bl, int nb, int lo_row,
-                                          int hi_row) {
-  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-  uint32_t pp[4], gp[4];  // packed P / G of the current block, two chunks per u32x4
-  // operands are read one chunk ahead (the mode branches end the compiler's
-  // scheduling regions, so it cannot move the reads earlier itself)
-  ChunkOps<D> ops[2];
-  load_chunk_ops<D>(ops[0], 0, qprev, dprev, qcur, dcur, qnext, dnext, lo);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int blk = c >> 2, q4 = c & 3;
-    const int r0 = blk * 32 + q4 * 8 + 4 * g;
-    // bias of the chunk's four elements; key = edges passed (plan kinds) or
-    // bucket (exact kinds)
-    float cb[4];
-    int key[4];
-    if (kind == kStepConst) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        cb[e] = c0;
-        key[e] = 0;
-      }
-    } else if (kind <= kStepThr3) {
-      const int4 v4 = *reinterpret_cast<const int4*>(rows + blk * 32 + q4 * 8);
-      const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
-      if (kind == kStepThr1) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool p1 = vv[e] <= t1;
-          cb[e] = p1 ? c1 : c0;
-          key[e] = p1 ? 1 : 0;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool p1 = vv[e] <= t1, p2 = vv[e] <= t2, p3 = vv[e] <= t3;
-          cb[e] = p3 ? c3 : (p2 ? c2 : (p1 ? c1 : c0));
-          key[e] = (p1 ? 1 : 0) + (p2 ? 1 : 0) + (p3 ? 1 : 0);
-        }
-      }
-    } else if (kind != kStepMaskedWide) {
-      const int4 v4 = *reinterpret_cast<const int4*>(ts.u + r0);
-      const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int32_t d = vv[e] - tsr;
-        key[e] = lut_bucket((uint32_t)(d < 0 ? -d : d), bl.lut);
-        cb[e] = bl.c[key[e]];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[e] = lut_bucket64(ts.t64[r0 + e] - tsr64, nb, bl.lut);
-        cb[e] = bl.c[key[e]];
-      }
-    }
-    // common block: the next chunk's operand reads, this chunk's MFMAs and
-    // its SiLU / gradient arithmetic.  Chunks q4 = 0, 1 issue every
-    // contraction of operand u = 0 of the block and chunks 2, 3 those of
-    // u = 1, so each operand is dead by the time the chunk pair that rebuilds
-    // it ends.
-    if (c < 7) load_chunk_ops<D>(ops[(c + 1) & 1], c + 1, qprev, dprev, qcur, dcur, qnext, dnext, lo);
-    chunk_mfmas<D>(ops[c & 1], c, dkacc, dvacc, s, dp, P, G, kop, vop);
-    float a[4], gg[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) silu_grad(s[blk][4 * q4 + e], dp[blk][4 * q4 + e], beta, cb[e], a[e], gg[e]);
-    if (kind >= kStepMasked) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool vis = r0 + e >= lo_row && r0 + e < hi_row;
-        a[e] = vis ? a[e] : 0.0f;
-        gg[e] = vis ? gg[e] : 0.0f;
-      }
-    }
-    // d(ts_weights): plan kinds sum per passed edge, exact kinds add per element
-    if (kind == kStepConst) {
-      s0 += (gg[0] + gg[1]) + (gg[2] + gg[3]);
-    } else if (kind == kStepThr1) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s0 += gg[e];
-        s1 += key[e] >= 1 ? gg[e] : 0.0f;
-      }
-    } else if (kind == kStepThr3) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s0 += gg[e];
-        s1 += key[e] >= 1 ? gg[e] : 0.0f;
-        s2 += key[e] >= 2 ? gg[e] : 0.0f;
-        s3 += key[e] >= 3 ? gg[e] : 0.0f;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&dwl[key[e]], gg[e]);
-    }
-    const int h2 = (q4 & 1) * 2;
-    pp[h2] = pack_bf16x2(a[0], a[1]);
-    pp[h2 + 1] = pack_bf16x2(a[2], a[3]);
-    gp[h2] = pack_bf16x2(gg[0], gg[1]);
-    gp[h2 + 1] = pack_bf16x2(gg[2], gg[3]);
-    if (q4 & 1) {
-      // rows runs q4 - 1 and q4 form operand u = q4 / 2 of the block
-      const int u = q4 >> 1;
-      P[blk][u] = u32x4{pp[0], pp[1], pp[2], pp[3]};
-      G[blk][u] = u32x4{gp[0], gp[1], gp[2], gp[3]};
-    }
-  }
-  if (kind <= kStepThr3) {
-    atomicAdd(&dwl[blo], s0 - s1);
-    if (kind != kStepConst) atomicAdd(&dwl[blo + 1], s1 - s2);
-    if (kind == kStepThr3) {
-      atomicAdd(&dwl[blo + 2], s2 - s3);
-      atomicAdd(&dwl[blo + 3], s3);
-    }
-  }
-}
-
-}  // namespace
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_kv_pipe_kernel(const AttnParams p) {
-  using M = Mma<__bf16>;
-  using T = __bf16;
-  __shared__ PipeSmem<D> sm;
-  __shared__ BiasLds bl;
-  __shared__ float dwbins[kPipeDwCopies][kMaxBuckets + kPad];  // plan sums touch up to b_lo + 3
-  __shared__ int item_slot;
-  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  LaneOffsets<D> lo;
-  lo.init(lane);
-  const int H = p.H, NB = p.NB;
-  const int64_t ld = (int64_t)H * D;
-  const uint32_t lane_off = tile_lane_offset<T, D, kThreads>(tid, ld);
-  const T* Q = static_cast<const T*>(p.q);
-  const T* K = static_cast<const T*>(p.k);
-  const T* V = static_cast<const T*>(p.v);
-  const T* dO = static_cast<const T*>(p.dout);
-  T* dK = static_cast<T*>(p.dk);
-  T* dV = static_cast<T*>(p.dv);
-  load_bucket_tables(bl, p, tid);
-  const int n_work = p.ctr[kCtrKTiles] * H;
-  float* dwl = dwbins[lane % kPipeDwCopies];
-  const float beta = kNegLog2e * p.alpha;
-
-  for (;;) {
-    const int w = pop_item(&item_slot, p.ctr + kCtrKNext, tid);
-    if (w >= n_work) break;
-    const int h = w % H;
-    const Item it = p.kitems[w / H];
-    const int64_t seq0 = p.offsets[it.b];
-    const int64_t base = p.ts[seq0];
-    const int kj = wave * 32 + r32;
-    const bool kvalid = kj < it.n;
-    const int kpos = it.pos0 + kj;
-    const int64_t krow = (int64_t)it.row0 + kj;
-    const int64_t tsk = kvalid ? p.ts[krow] : 0;
-    bf16x8 kop[D / 16], vop[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kop[kk] = bf16x8{};
-      vop[kk] = bf16x8{};
-      if (kvalid) {
-        kop[kk] = M::load(K + krow * ld + h * D + kk * 16 + g * 8);
-        vop[kk] = M::load(V + krow * ld + h * D + kk * 16 + g * 8);
-      }
-    }
-    load_bias_values<T>(bl, p, h, tid);
-    for (int i = tid; i < kPipeDwCopies * (kMaxBuckets + kPad); i += kThreads) (&dwbins[0][0])[i] = 0.0f;
-    f32x16 dkacc[D / 32], dvacc[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      dkacc[i] = f32x16{};
-      dvacc[i] = f32x16{};
-    }
-    const int wave_kmax = it.pos0 + wave * 32 + 31;
-    const LaneTs lt = lane_ts(tsk, kvalid, base);
-    const T* Qh = Q + h * D;
-    const T* dOh = dO + h * D;
-
-    // Prologue: tiles 0 and 1 (when present) loaded and their timestamps
-    // staged, then S and dP of step 0.
-    StepIter si;
-    si.init(p, it.b, it.pos0);
-    StepIter nx = si;
-    if (nx.valid()) nx.next();
-    int64_t tsv0 = 0, tsv1 = 0;
-    if (si.valid()) {
-      tile_load_async<T, D, BQ, kThreads>(sm.q[0], Qh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
-      tile_load_async<T, D, BQ, kThreads>(sm.d[0], dOh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
-      if (wave == 0) tsv0 = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
-    }
-    if (nx.valid()) {
-      tile_load_async<T, D, BQ, kThreads>(sm.q[1], Qh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
-      tile_load_async<T, D, BQ, kThreads>(sm.d[1], dOh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
-      if (wave == 0) tsv1 = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
-    }
-    if (wave == 0 && si.valid()) ts_tile_fill<BQ>(sm.ts[0], tsv0, si.nq(), lane, base);
-    if (wave == 0 && nx.valid()) ts_tile_fill<BQ>(sm.ts[1], tsv1, nx.nq(), lane, base);
-    wait_loads();
-    __syncthreads();
-
-    f32x16 s[2], dp[2];
-    u32x4 P[2][2], G[2][2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x16{};
-      dp[blk] = f32x16{};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        P[blk][u] = u32x4{0u, 0u, 0u, 0u};
-        G[blk][u] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (si.valid()) {
-      s[0] = tile_mma_rows_o<D>(reinterpret_cast<const char*>(sm.q[0]), lo, 0, kop);
-      dp[0] = tile_mma_rows_o<D>(reinterpret_cast<const char*>(sm.d[0]), lo, 0, vop);
-    }
-    // Iteration t reads buffer t - 1 (contractions; at t = 0 buffer 0 with zero
-    // P and G, which adds nothing), buffer t and buffer t + 1 (products; past
-    // the last step they read a stale buffer and are discarded).
-    int t = 0;
-    while (si.valid()) {
-      const int q0 = si.q0;
-      const int nq = si.nq();
-      StepIter n2 = nx;
-      if (n2.valid()) n2.next();
-      const int cur = t & 3, nxt = (t + 1) & 3, nxt2 = (t + 2) & 3, prv = t == 0 ? 0 : (t + 3) & 3;
-      int64_t tsv = 0;
-      if (n2.valid()) {
-        tile_load_async<T, D, BQ, kThreads>(sm.q[nxt2], Qh + n2.lrow() * ld, ld, n2.nq(), tid, lane_off);
-        tile_load_async<T, D, BQ, kThreads>(sm.d[nxt2], dOh + n2.lrow() * ld, ld, n2.nq(), tid, lane_off);
-        if (wave == 0) tsv = p.ts[seq0 + n2.q0 + min(lane, n2.nq() - 1)];
-      }
-      const TsTile<BQ>& ts = sm.ts[cur];
-      const int4 hdr = ts.hdr;
-      const bool fast = lt.fast && hdr.z == 0;
-      const char* qprev = reinterpret_cast<const char*>(sm.q[prv]);
-      const char* dprev = reinterpret_cast<const char*>(sm.d[prv]);
-      const char* qcur = reinterpret_cast<const char*>(sm.q[cur]);
-      const char* dcur = reinterpret_cast<const char*>(sm.d[cur]);
-      const char* qnext = reinterpret_cast<const char*>(sm.q[nxt]);
-      const char* dnext = reinterpret_cast<const char*>(sm.d[nxt]);
-      int kind, lo_row = 0, hi_row = BQ;
-      Plan pl{};
-      const int32_t* rows = ts.u;
-      if (q0 < wave_kmax || nq < BQ || !fast) {
-        kind = fast ? kStepMasked : kStepMaskedWide;
-        lo_row = kpos - q0;
-        hi_row = nq;
-      } else {
-        pl = make_plan<-1>(lt.rel, kvalid, hdr.x, hdr.y, bl);
-        kind = wave_mode(pl.n);
-        rows = (pl.flip ? ts.nu : ts.u) + 4 * g;
-      }
-      pipe_iter<D>(kind, dkacc, dvacc, s, dp, P, G, qprev, dprev, qcur, dcur, qnext, dnext, lo, kop, vop, dwl, beta,
-                   pl.c0, pl.c1, pl.c2, pl.c3, pl.t1, pl.t2, pl.t3, pl.blo, rows, ts, g, lt.rel, tsk, bl, NB, lo_row,
-                   hi_row);
-      if (n2.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[nxt2], tsv, n2.nq(), lane, base);
-      wait_loads();
-      __syncthreads();
-      si = nx;
-      nx = n2;
-      ++t;
-    }
-    if (t > 0) {
-      // contractions of the last step (tile t - 1 is still resident)
-      const char* qb = reinterpret_cast<const char*>(sm.q[(t - 1) & 3]);
-      const char* db = reinterpret_cast<const char*>(sm.d[(t - 1) & 3]);
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        contract_full<D>(dvacc, db, lo, P[blk], blk);
-        contract_full<D>(dkacc, qb, lo, G[blk], blk);
-      }
-    }
-    if (kvalid) {
-      store_scaled<T, D>(dK + krow * ld + h * D, dkacc, p.alpha, g);
-      store_scaled<T, D>(dV + krow * ld + h * D, dvacc, kNegLn2, g);
-    }
-    __syncthreads();
-    for (int i = tid; i < NB; i += kThreads) {
-      float v = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kPipeDwCopies; ++c) v += dwbins[c][i];
-      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, p.alpha * v);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Backward, query-major pass: dQ.  Same item list and lane ownership as the
 // forward; Sᵀ = K Qᵀ and dPᵀ = V dOᵀ are recomputed and dQᵀ += Kᵀ Gᵀ (K read
 // transposed from the same tile).
@@ -1732,11 +1147,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
 // Launchers
 // ---------------------------------------------------------------------------
 namespace {
-// dK/dV kernel for bf16, d >= 64: 0 = eight-wave pair kernel (128 keys),
-// 1 = software-pipelined four-wave kernel (128 keys), 2 = four-wave pair
-// kernel on 64 keys, two workgroups per CU.
-constexpr int kBwdKvBf16 = 2;
-
 template <typename K>
 int grid_for(K kernel, int max_items, int cus, int threads = kThreads) {
   int per_cu = 0;
@@ -1752,15 +1162,9 @@ hipError_t launch_all(const AttnParams& p, int which, int max_items, int cus, hi
     auto k = fwd_kernel<T, D>;
     hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
   } else if (which == 1) {
-    if constexpr (sizeof(T) == 2 && D >= 64 && kBwdKvBf16 == 2) {
+    if constexpr (sizeof(T) == 2 && D >= 64) {
       auto k = bwd_kv_half_kernel<D>;
       hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus, kHalfThreads)), dim3(kHalfThreads), 0, s, p);
-    } else if constexpr (sizeof(T) == 2 && D >= 64 && kBwdKvBf16 == 1) {
-      auto k = bwd_kv_pipe_kernel<D>;
-      hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
-    } else if constexpr (sizeof(T) == 2 && D >= 64) {
-      auto k = bwd_kv_pair_kernel<D>;
-      hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus, kPairThreads)), dim3(kPairThreads), 0, s, p);
     } else {
       auto k = bwd_kv_kernel<T, D>;
       hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
@@ -1789,7 +1193,7 @@ hipError_t launch_attn(const AttnParams& p, bool bf16, int d, int which, int max
 
 int attn_q_tile_rows() { return BM; }
 int attn_k_tile_keys() { return BN; }
-int attn_bwd_key_tile(bool bf16, int d) { return bf16 && d >= 64 && kBwdKvBf16 == 2 ? kHalfKeys : BK; }
+int attn_bwd_key_tile(bool bf16, int d) { return bf16 && d >= 64 ? kHalfKeys : BK; }
 int attn_bwd_q_step() { return BQ; }
 
 }  // namespace hstu
