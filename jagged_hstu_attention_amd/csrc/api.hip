@@ -161,7 +161,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ctr, edges, lut, local_off, qitems, kitems, total;
+  size_t ctr, edges, lut, local_off, tile_off, qitems, kitems, total;
   int64_t max_qtiles, max_ktiles;
 };
 
@@ -181,6 +181,8 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
   off = align_up(off + hstu::kLutSize * sizeof(hstu::u32x2));
   l.local_off = off;
   off = align_up(off + (size_t)(p->num_seqs + 1) * sizeof(int64_t));
+  l.tile_off = off;
+  off = align_up(off + (size_t)2 * (p->num_seqs + 1) * sizeof(int));
   l.qitems = off;
   off = align_up(off + (size_t)l.max_qtiles * sizeof(hstu::Item));
   l.kitems = off;
@@ -296,6 +298,8 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   const int64_t max_cost = cdiv(p->max_seq_len, std::min(hstu::attn_k_tile_keys(), hstu::attn_bwd_q_step())) + 3;
   sp.hist_size = (int)std::min<int64_t>(hstu::kSchedHist, std::max<int64_t>(max_cost, 1));
   sp.local_off = reinterpret_cast<int64_t*>(ws + l.local_off);
+  sp.qtile_off = reinterpret_cast<int*>(ws + l.tile_off);
+  sp.ktile_off = sp.qtile_off + (p->num_seqs + 1);
   sp.qitems = reinterpret_cast<hstu::Item*>(ws + l.qitems);
   sp.kitems = reinterpret_cast<hstu::Item*>(ws + l.kitems);
   sp.ctr = reinterpret_cast<int*>(ws + l.ctr);

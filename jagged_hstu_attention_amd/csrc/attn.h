@@ -57,6 +57,8 @@ struct SchedParams {
   int k_cost_tile;   // query rows per step used in a key tile's cost
   int hist_size;     // cost histogram bins (costs are clamped to hist_size-1)
   int64_t* local_off;
+  int* qtile_off;    // [B+1] first query tile of each sequence in tile order
+  int* ktile_off;    // [B+1] first key tile of each sequence
   Item* qitems;
   Item* kitems;
   int* ctr;

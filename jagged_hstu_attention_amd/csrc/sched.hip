@@ -82,6 +82,53 @@ __device__ int64_t block_scan(int64_t v, int64_t* buf, int64_t* total) {
 
 __device__ __forceinline__ int clampc(int64_t c, int hs) { return (int)(c < hs - 1 ? c : hs - 1); }
 
+// Sequence owning flat tile j: the largest b with off[b] <= j.
+__device__ __forceinline__ int owner(const int* off, int64_t B, int j) {
+  int lo = 0, hi = (int)B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct QTile {
+  int b, pos0, n;
+  int64_t row0;
+};
+
+// Flat query tile j: tiles of q_tile rows over the sequence's segments.
+__device__ __forceinline__ QTile query_tile(const SchedParams& p, int j) {
+  const int b = owner(p.qtile_off, p.B, j);
+  const SegInfo s = seq_segments(p, b, p.local_off[b]);
+  int i = j - p.qtile_off[b];
+  const int n0 = (s.len[0] + p.q_tile - 1) / p.q_tile;
+  const int sg = i < n0 ? 0 : 1;
+  if (sg == 1) i -= n0;
+  const int r = i * p.q_tile;
+  return QTile{b, s.pos0[sg] + r, min(p.q_tile, s.len[sg] - r), s.lrow0[sg] + r};
+}
+
+struct KTile {
+  int b, k0, n;
+  int64_t cost;
+};
+
+// Flat key tile j: k_tile keys from k0; cost = query steps at or after k0.
+__device__ __forceinline__ KTile key_tile(const SchedParams& p, int j) {
+  const int b = owner(p.ktile_off, p.B, j);
+  const int L = (int)(p.offsets[b + 1] - p.offsets[b]);
+  const int k0 = (j - p.ktile_off[b]) * p.k_tile;
+  const SegInfo s = seq_segments(p, b, p.local_off[b]);
+  int64_t cost = 0;
+  for (int sg = 0; sg < s.n; ++sg) {
+    const int from = max(s.pos0[sg], k0), to = s.pos0[sg] + s.len[sg];
+    if (to > from) cost += (to - from + p.k_cost_tile - 1) / p.k_cost_tile;
+  }
+  return KTile{b, k0, min(p.k_tile, L - k0), cost};
+}
+
 // #{k in [1, nb) : E_k <= m}
 __device__ int bucket_search(uint64_t m, const EdgeArg& edges, int nb) {
   int lo = 0, hi = nb - 1;  // answer in [lo, hi]
@@ -146,28 +193,42 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   if (t == 0) p.local_off[p.B] = carry;
   __syncthreads();
 
-  // Pass 1: cost histograms.
-  for (int64_t b = t; b < p.B; b += kSchedThreads) {
-    const SegInfo s = seq_segments(p, (int)b, p.local_off[b]);
-    if (p.q_tile > 0) {
-      for (int sg = 0; sg < s.n; ++sg)
-        for (int r = 0; r < s.len[sg]; r += p.q_tile) {
-          const int end = s.pos0[sg] + min(p.q_tile, s.len[sg] - r) + r;
-          atomicAdd(&histq[clampc((end + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
-        }
+  // Tile counts per sequence, scanned: sequence b owns query tiles
+  // [qtile_off[b], qtile_off[b+1]) and key tiles [ktile_off[b], ktile_off[b+1])
+  // of the flat tile order, so that the passes below run one thread per tile.
+  int64_t qcarry = 0, kcarry = 0;
+  for (int64_t base = 0; base < p.B; base += kSchedThreads) {
+    const int64_t b = base + t;
+    int64_t nq = 0, nk = 0;
+    if (b < p.B) {
+      const SegInfo s = seq_segments(p, (int)b, p.local_off[b]);
+      if (p.q_tile > 0)
+        for (int sg = 0; sg < s.n; ++sg) nq += (s.len[sg] + p.q_tile - 1) / p.q_tile;
+      if (p.k_tile > 0) nk = (p.offsets[b + 1] - p.offsets[b] + p.k_tile - 1) / p.k_tile;
     }
-    if (p.k_tile > 0) {
-      const int L = (int)(p.offsets[b + 1] - p.offsets[b]);
-      for (int k0 = 0; k0 < L; k0 += p.k_tile) {
-        int64_t cost = 0;
-        for (int sg = 0; sg < s.n; ++sg) {
-          const int from = max(s.pos0[sg], k0), to = s.pos0[sg] + s.len[sg];
-          if (to > from) cost += (to - from + p.k_cost_tile - 1) / p.k_cost_tile;
-        }
-        atomicAdd(&histk[clampc(cost, hs)], 1);
-      }
+    int64_t qtot, ktot;
+    const int64_t qpre = block_scan(nq, scan, &qtot);
+    const int64_t kpre = block_scan(nk, scan, &ktot);
+    if (b < p.B) {
+      p.qtile_off[b] = (int)(qcarry + qpre);
+      p.ktile_off[b] = (int)(kcarry + kpre);
     }
+    qcarry += qtot;
+    kcarry += ktot;
   }
+  if (t == 0) {
+    p.qtile_off[p.B] = (int)qcarry;
+    p.ktile_off[p.B] = (int)kcarry;
+  }
+  __syncthreads();
+  const int nqt = (int)qcarry, nkt = (int)kcarry;
+
+  // Pass 1: cost histograms.
+  for (int j = t; j < nqt; j += kSchedThreads) {
+    const QTile q = query_tile(p, j);
+    atomicAdd(&histq[clampc((q.pos0 + q.n + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
+  }
+  for (int j = t; j < nkt; j += kSchedThreads) atomicAdd(&histk[clampc(key_tile(p, j).cost, hs)], 1);
   __syncthreads();
 
   // Descending exclusive scan: start[c] = number of tiles with cost > c.
@@ -189,30 +250,15 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   __syncthreads();
 
   // Pass 2: scatter.
-  for (int64_t b = t; b < p.B; b += kSchedThreads) {
-    const SegInfo s = seq_segments(p, (int)b, p.local_off[b]);
-    if (p.q_tile > 0) {
-      for (int sg = 0; sg < s.n; ++sg)
-        for (int r = 0; r < s.len[sg]; r += p.q_tile) {
-          const int n = min(p.q_tile, s.len[sg] - r);
-          const int pos0 = s.pos0[sg] + r;
-          const int slot = atomicAdd(&histq[clampc((pos0 + n + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
-          p.qitems[slot] = Item{(int)b, (int)(s.lrow0[sg] + r), pos0, n};
-        }
-    }
-    if (p.k_tile > 0) {
-      const int64_t o0 = p.offsets[b];
-      const int L = (int)(p.offsets[b + 1] - o0);
-      for (int k0 = 0; k0 < L; k0 += p.k_tile) {
-        int64_t cost = 0;
-        for (int sg = 0; sg < s.n; ++sg) {
-          const int from = max(s.pos0[sg], k0), to = s.pos0[sg] + s.len[sg];
-          if (to > from) cost += (to - from + p.k_cost_tile - 1) / p.k_cost_tile;
-        }
-        const int slot = atomicAdd(&histk[clampc(cost, hs)], 1);
-        p.kitems[slot] = Item{(int)b, (int)(o0 + k0), k0, min(p.k_tile, L - k0)};
-      }
-    }
+  for (int j = t; j < nqt; j += kSchedThreads) {
+    const QTile q = query_tile(p, j);
+    const int slot = atomicAdd(&histq[clampc((q.pos0 + q.n + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
+    p.qitems[slot] = Item{q.b, (int)q.row0, q.pos0, q.n};
+  }
+  for (int j = t; j < nkt; j += kSchedThreads) {
+    const KTile k = key_tile(p, j);
+    const int slot = atomicAdd(&histk[clampc(k.cost, hs)], 1);
+    p.kitems[slot] = Item{k.b, (int)(p.offsets[k.b] + k.k0), k.k0, k.n};
   }
   if (t == 0) {
     p.ctr[kCtrQNext] = 0;
