@@ -9,7 +9,9 @@ from .hstu_oracle import (  # noqa: F401
     attn_bwd_kv_rows,
     attn_bwd_q_rows,
     attn_fwd,
+    attn_fwd_cached,
     attn_fwd_rows,
+    attn_fwd_targets,
     bucket_edges,
     bucketize,
     causal_pairs,
@@ -24,4 +26,6 @@ from .hstu_oracle import (  # noqa: F401
     reorder_index,
     silu,
     silu_grad,
+    target_mask,
+    target_rows,
 )

@@ -403,3 +403,74 @@ def attn_bwd_kv_rows(dout, q, k, v, offsets, ts, w, num_buckets, rows):
             dv[n, h] = silu(s) @ dd
             dk[n, h] = g @ qq
     return dk, dv
+
+
+# --------------------------------------------------------------------------
+# 6. Target-aware attention for scoring candidates ([HSTU] App. H, M-FALCON)
+#
+# A sequence of n rows ends with m candidate rows after n - m history rows.
+# Candidates attend to the history and must not attend to one another (App. H,
+# batched inference), so one pass over history plus candidates gives each
+# candidate the result of its own pass over history plus itself.  Reading:
+# a candidate attends to itself (the pages do not say; the self term is what
+# its own causal pass over history plus itself would contain).  With cached
+# history K and V (App. H, caching) only the candidates' rows are queried.
+# --------------------------------------------------------------------------
+
+def target_mask(n: int, num_targets: int) -> np.ndarray:
+    """Visibility [n, n] of key j to query i: causal, and a key among the last
+    num_targets rows is visible only to itself."""
+    hist = n - num_targets
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return (j <= i) & ((j < hist) | (j == i))
+
+
+def attn_fwd_targets(q, k, v, offsets, num_targets, ts, w, num_buckets) -> np.ndarray:
+    """Forward over all rows with the target-aware mask; num_targets: [B]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    w = np.asarray(w, np.float64)
+    ts = np.asarray(ts, np.int64)
+    T, H, dqk = q.shape
+    alpha = 1.0 / math.sqrt(dqk)
+    out = np.zeros((T, H, v.shape[2]), dtype=np.float64)
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi <= lo:
+            continue
+        mask = target_mask(hi - lo, int(num_targets[b]))
+        for h in range(H):
+            s, _ = _seq_scores(q[lo:hi, h], k[lo:hi, h], ts[lo:hi], ts[lo:hi], w[h], num_buckets, alpha)
+            out[lo:hi, h] = np.where(mask, silu(s), 0.0) @ v[lo:hi, h]
+    return out
+
+
+def target_rows(offsets, num_targets) -> np.ndarray:
+    """Global rows of the candidates, sequence by sequence."""
+    rows = []
+    for b in range(len(offsets) - 1):
+        hi = int(offsets[b + 1])
+        rows.extend(range(hi - int(num_targets[b]), hi))
+    return np.asarray(rows, dtype=np.int64)
+
+
+def attn_fwd_cached(q_targets, k, v, offsets, num_targets, ts, w, num_buckets) -> np.ndarray:
+    """Candidates only, against cached history: q_targets [sum m_b, H, d_qk]
+    holds the candidate rows in sequence order; k, v, ts cover all rows.
+    Each candidate is its own pass over the history and itself."""
+    q_targets = np.asarray(q_targets, np.float64)
+    H, dqk = q_targets.shape[1], q_targets.shape[2]
+    alpha = 1.0 / math.sqrt(dqk)
+    rows = target_rows(offsets, num_targets)
+    out = np.zeros((len(rows), H, v.shape[2]), dtype=np.float64)
+    for n, i in enumerate(rows):
+        b, lo, hi = _row_seq(offsets, int(i))
+        hist = hi - int(num_targets[b])
+        keys = np.concatenate([np.arange(lo, hist), [i]])
+        for h in range(H):
+            s, _ = _seq_scores(q_targets[n:n + 1, h], np.asarray(k[keys, h], np.float64),
+                               ts[i:i + 1], np.asarray(ts)[keys], np.asarray(w[h], np.float64), num_buckets, alpha)
+            out[n, h] = silu(s)[0] @ np.asarray(v[keys, h], np.float64)
+    return out

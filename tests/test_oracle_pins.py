@@ -461,3 +461,115 @@ def test_planted_mistakes_are_caught(monkeypatch):
         assert _pins_fail(monkeypatch, attr, bad) > 0, attr
         monkeypatch.setattr(ho, "_seq_scores", orig_scores)
         monkeypatch.setattr(ho, "silu", orig_silu)
+
+
+# --------------------------------------------------------------------------
+# Target-aware attention for candidates ([HSTU] App. H, M-FALCON)
+# --------------------------------------------------------------------------
+
+T_LENGTHS = [9, 1, 6, 0, 12, 5]
+T_TARGETS = [3, 1, 0, 0, 12, 2]
+
+
+def brute_force_fwd_targets(q, k, v, offsets, num_targets, ts, w, nb):
+    """Per-pair loop; key j is visible to query i iff j <= i and j is a history
+    row or i itself."""
+    T, H, d = q.shape
+    alpha = 1.0 / math.sqrt(d)
+    out = np.zeros((T, H, v.shape[2]))
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        hist = hi - int(num_targets[b])
+        for h in range(H):
+            for i in range(lo, hi):
+                for j in range(lo, i + 1):
+                    if j >= hist and j != i:
+                        continue
+                    dot = sum(float(q[i, h, e]) * float(k[j, h, e]) for e in range(d))
+                    s = alpha * (dot + float(w[h, bucket_by_log(int(ts[i]) - int(ts[j]), nb)]))
+                    out[i, h] += (s / (1.0 + math.exp(-s))) * v[j, h]
+    return out
+
+
+def targets_wl(seed=5, nb=128, w_std=0.5):
+    return small(T_LENGTHS, nb=nb, H=2, d=4, dv=3, w_std=w_std, seed=seed)
+
+
+def test_targets_match_brute_force():
+    wl = targets_wl()
+    got = oracle.attn_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, T_TARGETS, wl.ts, wl.w.f64, 128)
+    want = brute_force_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, T_TARGETS, wl.ts, wl.w.f64, 128)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_each_candidate_equals_its_own_pass():
+    # App. H: one pass over history plus all candidates gives each candidate
+    # what its own causal pass over history plus that candidate gives.
+    wl = targets_wl(seed=6)
+    got = oracle.attn_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, T_TARGETS, wl.ts, wl.w.f64, 128)
+    for b in range(len(T_LENGTHS)):
+        lo, hi = int(wl.offsets[b]), int(wl.offsets[b + 1])
+        hist = hi - T_TARGETS[b]
+        for c in range(hist, hi):
+            rows = list(range(lo, hist)) + [c]
+            alone = oracle.attn_fwd(wl.q.f64[rows], wl.k.f64[rows], wl.v.f64[rows], [0, len(rows)],
+                                    wl.ts[rows], wl.w.f64, 128)
+            np.testing.assert_allclose(got[c], alone[-1], rtol=0, atol=1e-12)
+
+
+def test_targets_zero_is_causal_and_history_rows_are_causal():
+    wl = targets_wl(seed=7)
+    plain = fwd(wl)
+    none = oracle.attn_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, [0] * len(T_LENGTHS), wl.ts,
+                                   wl.w.f64, 128)
+    np.testing.assert_allclose(none, plain, rtol=0, atol=1e-12)
+    got = oracle.attn_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, T_TARGETS, wl.ts, wl.w.f64, 128)
+    cand = set(oracle.target_rows(wl.offsets, T_TARGETS).tolist())
+    hist_rows = [i for i in range(int(wl.offsets[-1])) if i not in cand]
+    np.testing.assert_allclose(got[hist_rows], plain[hist_rows], rtol=0, atol=1e-12)
+
+
+def test_all_candidates_closed_form():
+    # no history: each row sees only itself, O_i = silu(alpha (q_i.k_i + w[h, bucket 0])) v_i
+    wl = small([4, 7], nb=128, H=2, d=4, dv=3, w_std=0.5, seed=8)
+    got = oracle.attn_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, [4, 7], wl.ts, wl.w.f64, 128)
+    alpha = 0.5
+    s = alpha * (np.einsum("thd,thd->th", wl.q.f64, wl.k.f64) + wl.w.f64[:, 0][None, :])
+    np.testing.assert_allclose(got, (s / (1.0 + np.exp(-s)))[:, :, None] * wl.v.f64, rtol=0, atol=1e-12)
+
+
+def test_cached_candidates_equal_full_pass():
+    wl = targets_wl(seed=9)
+    full = oracle.attn_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, T_TARGETS, wl.ts, wl.w.f64, 128)
+    rows = oracle.target_rows(wl.offsets, T_TARGETS)
+    cached = oracle.attn_fwd_cached(wl.q.f64[rows], wl.k.f64, wl.v.f64, wl.offsets, T_TARGETS, wl.ts, wl.w.f64, 128)
+    np.testing.assert_allclose(cached, full[rows], rtol=0, atol=1e-12)
+
+
+def test_planted_target_mask_mistakes_are_caught(monkeypatch):
+    orig = ho.target_mask
+
+    def candidates_see_each_other(n, m):
+        return np.tril(np.ones((n, n), dtype=bool))
+
+    def no_self(n, m):
+        out = orig(n, m)
+        idx = np.arange(n - m, n)
+        out[idx, idx] = False
+        return out
+
+    def history_off_by_one(n, m):
+        return orig(n, min(m + 1, n))
+
+    pins = [test_targets_match_brute_force, test_each_candidate_equals_its_own_pass,
+            test_all_candidates_closed_form]
+    for bad in (candidates_see_each_other, no_self, history_off_by_one):
+        monkeypatch.setattr(ho, "target_mask", bad)
+        failures = 0
+        for fn in pins:
+            try:
+                fn()
+            except AssertionError:
+                failures += 1
+        monkeypatch.setattr(ho, "target_mask", orig)
+        assert failures > 0, bad.__name__
