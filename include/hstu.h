@@ -82,7 +82,8 @@ typedef struct {
 
 /* Bytes of workspace needed by hstu_jagged_attn_fwd (backward = 0) or
  * hstu_jagged_attn_bwd (backward = 1).  Returns 0 if the problem is invalid
- * (hstu_last_error() then says why). */
+ * (hstu_last_error() then says why).  For a forward, total_q may be smaller
+ * than total_kv with cp_size 1 (the candidates-only pass). */
 size_t hstu_workspace_size(const hstu_problem_t* p, int backward);
 
 /* Forward.  HSTUAttention equation (CP paper §2.1) on jagged inputs.
@@ -103,7 +104,33 @@ int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k,
                          void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Backward of the forward above for upstream gradient dout [total_q, H, d_v].
+/* Forward for scoring candidates (Actions Speak Louder than Words, App. H,
+ * M-FALCON: a micro-batch of candidates appended to a user's history attends
+ * to the history but not to other candidates, so one pass scores the whole
+ * micro-batch; with cached history K and V only the candidates are queried).
+ *   num_targets int64 [B] (device): the last num_targets[b] rows of sequence
+ *            b are candidates (values outside [0, its length] are clamped to
+ *            it).  Key j is visible to query i iff j <= i and (j is a history
+ *            row or j == i).
+ *   q_targets_only = 0: q and out cover all total_kv rows (total_q must equal
+ *            total_kv); history rows attend causally as in hstu_jagged_attn_fwd.
+ *   q_targets_only = 1: q and out hold only the candidate rows, sequence by
+ *            sequence (total_q = sum of num_targets: host metadata, like
+ *            max_seq_len); k, v and timestamps cover all rows (the cached
+ *            history and the candidates).
+ * Requires cp_size == 1 (else HSTU_EUNSUPPORTED).  Other arguments, the
+ * workspace (hstu_workspace_size(p, 0)) and the errors are as for
+ * hstu_jagged_attn_fwd.  Forward only. */
+int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q,
+                                 const void* k, const void* v,
+                                 const int64_t* offsets,
+                                 const int64_t* num_targets, int q_targets_only,
+                                 const int64_t* timestamps,
+                                 const void* ts_weights, void* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Backward of hstu_jagged_attn_fwd for upstream gradient dout [total_q, H, d_v].
  * Writes dq [total_q, H, d_qk], dk [total_kv, H, d_qk], dv [total_kv, H, d_v]
  * (all in the input dtype, accumulated in fp32) and d_ts_weights [H, NB] (fp32).
  * With cp_size > 1, dk, dv and d_ts_weights are this rank's partial sums (zero

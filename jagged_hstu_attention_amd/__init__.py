@@ -110,6 +110,25 @@ def jagged_attn_fwd(q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_si
     return out
 
 
+def jagged_attn_fwd_targets(q, k, v, offsets, num_targets, ts, ts_weights, max_seq_len: int, *,
+                            q_targets_only: bool = False, out=None, workspace=None):
+    """Forward with candidates: the last num_targets[b] rows of sequence b
+    attend to its history rows and to themselves only.  q_targets_only: q
+    holds just those candidate rows (k, v, ts cover all rows).  Returns out
+    [q.shape[0], H, d_v]."""
+    torch = _torch()
+    p = problem(q, k, v, offsets, ts_weights, max_seq_len)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    ws, ws_bytes = _workspace(p, False, q.device, workspace)
+    lib = _lib.load()
+    _lib.check(lib.hstu_jagged_attn_fwd_targets(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                                                _ptr(num_targets), 1 if q_targets_only else 0, _ptr(ts),
+                                                _ptr(ts_weights), _ptr(out), _ptr(ws), ws_bytes,
+                                                _stream(q.device)))
+    return out
+
+
 def jagged_attn_bwd(dout, q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1,
                     cp_rank: int = 0, dq=None, dk=None, dv=None, dw=None, workspace=None):
     """Backward; returns (dq, dk, dv, d_ts_weights) with d_ts_weights in fp32."""

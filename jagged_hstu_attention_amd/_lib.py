@@ -38,6 +38,7 @@ class Problem(ctypes.Structure):
 EXPORTS = [
     "hstu_workspace_size",
     "hstu_jagged_attn_fwd",
+    "hstu_jagged_attn_fwd_targets",
     "hstu_jagged_attn_bwd",
     "hstu_cp_reorder",
     "hstu_bucket_edges",
@@ -74,6 +75,9 @@ def load() -> ctypes.CDLL:
     lib.hstu_workspace_size.restype = ctypes.c_size_t
     lib.hstu_jagged_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.hstu_jagged_attn_fwd.restype = ctypes.c_int
+    lib.hstu_jagged_attn_fwd_targets.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                                 ctypes.c_size_t, vp]
+    lib.hstu_jagged_attn_fwd_targets.restype = ctypes.c_int
     lib.hstu_jagged_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.hstu_jagged_attn_bwd.restype = ctypes.c_int
     lib.hstu_cp_reorder.argtypes = [vp, vp, i64, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp]

@@ -193,7 +193,9 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
-int validate(const hstu_problem_t* p) {
+// q_subset: the query rows may be a subset of the key rows with cp_size 1
+// (the candidates-only forward).
+int validate(const hstu_problem_t* p, bool q_subset = false) {
   if (!p) return fail(HSTU_EINVAL, "problem is NULL");
   if (p->dtype != HSTU_BF16 && p->dtype != HSTU_FP32) return fail(HSTU_EINVAL, "dtype %d is not bf16 (0) or fp32 (1)", p->dtype);
   if (p->reserved != 0) return fail(HSTU_EINVAL, "reserved field must be 0");
@@ -210,7 +212,7 @@ int validate(const hstu_problem_t* p) {
     return fail(HSTU_EINVAL, "cp_rank %lld not in [0, %lld)", (long long)p->cp_rank, (long long)p->cp_size);
   if (p->cp_size > 1024) return fail(HSTU_EUNSUPPORTED, "cp_size %lld > 1024", (long long)p->cp_size);
   if (p->total_kv < 0 || p->total_q < 0) return fail(HSTU_EINVAL, "negative row count");
-  if (p->cp_size == 1 && p->total_q != p->total_kv)
+  if (p->cp_size == 1 && !q_subset && p->total_q != p->total_kv)
     return fail(HSTU_EINVAL, "total_q %lld != total_kv %lld with cp_size 1", (long long)p->total_q, (long long)p->total_kv);
   if (p->total_q > p->total_kv) return fail(HSTU_EINVAL, "total_q > total_kv");
   if (p->max_seq_len < 0) return fail(HSTU_EINVAL, "max_seq_len %lld < 0", (long long)p->max_seq_len);
@@ -284,9 +286,11 @@ void timing_resolve_locked() {
 
 
 int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, char* ws, float* dw,
-             hipStream_t s, bool backward) {
+             hipStream_t s, bool backward, const int64_t* num_targets = nullptr, int targets_only = 0) {
   hstu::SchedParams sp{};
   sp.offsets = offsets;
+  sp.num_targets = num_targets;
+  sp.targets_only = targets_only;
   sp.B = p->num_seqs;
   sp.cp_size = (int)p->cp_size;
   sp.cp_rank = (int)p->cp_rank;
@@ -380,15 +384,15 @@ int hstu_bucket_edges(int64_t num_buckets, uint32_t* edges_out) {
 }
 
 size_t hstu_workspace_size(const hstu_problem_t* p, int backward) {
-  if (validate(p) != HSTU_OK) return 0;
+  if (validate(p, backward == 0) != HSTU_OK) return 0;  // a forward may query a subset of rows
   return layout_for(p, backward != 0).total;
 }
 
-int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, const void* v,
-                         const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = validate(p);
-  if (rc != HSTU_OK) return rc;
+namespace {
+
+int fwd_impl(const hstu_problem_t* p, const void* q, const void* k, const void* v, const int64_t* offsets,
+             const int64_t* num_targets, int targets_only, const int64_t* timestamps, const void* ts_weights,
+             void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (p->total_q == 0 || p->num_seqs == 0) return HSTU_OK;
   CHECK_PTR(q, "q");
   CHECK_PTR(k, "k");
@@ -404,7 +408,7 @@ int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, 
     return fail(HSTU_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  rc = schedule(p, l, offsets, ws, nullptr, s, false);
+  int rc = schedule(p, l, offsets, ws, nullptr, s, false, num_targets, targets_only);
   if (rc != HSTU_OK) return rc;
   hstu::AttnParams a = attn_params(p, l, ws);
   a.q = q;
@@ -414,12 +418,42 @@ int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, 
   a.ts = timestamps;
   a.w = ts_weights;
   a.out = out;
+  a.num_targets = num_targets;
+  a.targets_only = targets_only;
   const int max_items = (int)(l.max_qtiles * p->num_heads);
   const hipError_t e = timed(HSTU_KERNEL_FWD, s, [&] {
     return hstu::launch_attn(a, p->dtype == HSTU_BF16, (int)p->d_qk, 0, max_items, cu_count(), s);
   });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return HSTU_OK;
+}
+
+}  // namespace
+
+int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+                         const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = validate(p);
+  if (rc != HSTU_OK) return rc;
+  return fwd_impl(p, q, k, v, offsets, nullptr, 0, timestamps, ts_weights, out, workspace, workspace_bytes, stream);
+}
+
+int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+                                 const int64_t* offsets, const int64_t* num_targets, int q_targets_only,
+                                 const int64_t* timestamps, const void* ts_weights, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const int rc = validate(p, q_targets_only == 1);
+  if (rc != HSTU_OK) return rc;
+  if (p->cp_size != 1) return fail(HSTU_EUNSUPPORTED, "candidates with cp_size %lld > 1", (long long)p->cp_size);
+  if (q_targets_only != 0 && q_targets_only != 1) return fail(HSTU_EINVAL, "q_targets_only %d is not 0 or 1", q_targets_only);
+  if (!q_targets_only && p->total_q != p->total_kv)
+    return fail(HSTU_EINVAL, "total_q %lld != total_kv %lld with q_targets_only 0", (long long)p->total_q,
+                (long long)p->total_kv);
+  if (p->total_q > p->total_kv)
+    return fail(HSTU_EINVAL, "total_q %lld > total_kv %lld", (long long)p->total_q, (long long)p->total_kv);
+  if (p->num_seqs > 0 && p->total_kv > 0) CHECK_PTR8(num_targets, "num_targets");
+  return fwd_impl(p, q, k, v, offsets, num_targets, q_targets_only, timestamps, ts_weights, out, workspace,
+                  workspace_bytes, stream);
 }
 
 int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* q, const void* k, const void* v,

@@ -28,6 +28,11 @@ struct AttnParams {
   int* ctr;
   const uint32_t* edges;     // [NB+1]
   const u32x2* lut;          // [1024] exact-bucket table
+  // Candidates (forward only): the last num_targets[b] rows of sequence b
+  // attend to the sequence's other rows and to themselves only; with
+  // targets_only the query rows are those candidates alone.  NULL: none.
+  const int64_t* num_targets;
+  int targets_only;
   int H;
   int NB;
   int cp_size;
@@ -57,6 +62,8 @@ struct SchedParams {
   int k_cost_tile;   // query rows per step used in a key tile's cost
   int hist_size;     // cost histogram bins (costs are clamped to hist_size-1)
   int64_t* local_off;
+  const int64_t* num_targets;  // as in AttnParams (NULL: none)
+  int targets_only;
   int* qtile_off;    // [B+1] first query tile of each sequence in tile order
   int* ktile_off;    // [B+1] first key tile of each sequence
   Item* qitems;

@@ -243,19 +243,23 @@ struct FwdLane {
   int32_t tsr;      // own timestamp relative to the item base (32-bit modes)
   int64_t ts64;     // own timestamp
   int lim;          // key rows > lim of the tile are masked (qpos - key0)
+  int hlim;         // key rows >= hlim other than lim are candidates, masked (history end - key0)
   int g;
   float beta;       // -log2(e) * alpha
   int nb;
 };
 
-// a' = y sigma(y) for the 16 values of one block, y = beta s + cb.
+// a' = y sigma(y) for the 16 values of one block, y = beta s + cb.  Masked:
+// key row r of the block is visible iff r <= lim and (r < hlim or r == lim).
 template <bool MASK>
-__device__ __forceinline__ void silu_block(float* pv, const f32x16& s, const float* cb, float beta, int lim, int g) {
+__device__ __forceinline__ void silu_block(float* pv, const f32x16& s, const float* cb, float beta, int lim, int hlim,
+                                           int g) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float y = fmaf(s[i], beta, cb[i]);
     const float a = y * sigmoid_y(y);
-    pv[i] = (MASK && acc_row(i, g) > lim) ? 0.0f : a;
+    const int r = acc_row(i, g);
+    pv[i] = (MASK && (r > lim || (r >= hlim && r != lim))) ? 0.0f : a;
   }
 }
 
@@ -284,7 +288,7 @@ __device__ __forceinline__ void fwd_tile(f32x16* oacc, const T* kt, const T* vt,
     float cb[16];
     block_bias_mode<+1, BN, false, MASK>(cb, nullptr, mode, pl, ln.tsr, ln.ts64, ts, blk, ln.g, bl, ln.nb);
     float pv[16];
-    silu_block<MASK>(pv, s, cb, ln.beta, ln.lim - 32 * blk, ln.g);
+    silu_block<MASK>(pv, s, cb, ln.beta, ln.lim - 32 * blk, ln.hlim - 32 * blk, ln.g);
     if constexpr (sizeof(T) == 2)
       tr_mma<D>(oacc, tv, pv);
     else
@@ -339,8 +343,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
 
     const int kv_len = it.pos0 + it.n;
-    const int n_kt = (kv_len + BN - 1) / BN;
     const int wave_qmin = it.pos0 + wave * 32;
+    // Key tiles visited: the causal prefix [0, ht) over the history rows,
+    // then, past the history, only the tiles [d0, last] that hold the item's
+    // own rows (a candidate sees no other candidate).  Without candidates
+    // hist is the sequence length and the walk is 0 .. last.
+    int hist = kv_len;
+    if (p.num_targets) {  // candidates clamped to [0, L], as the scheduler does
+      const int L = (int)(p.offsets[it.b + 1] - seq0);
+      hist = L - (int)min(max(p.num_targets[it.b], (int64_t)0), (int64_t)L);
+    }
+    const int ht = (min(kv_len, hist) + BN - 1) / BN, last = (kv_len - 1) / BN;
+    const int d0 = kv_len <= hist ? last + 1 : max(max(it.pos0, hist) / BN, ht);
     const T* Kh = K + seq0 * ld + h * D;
     const T* Vh = V + seq0 * ld + h * D;
     const LaneTs lt = lane_ts(tsq, qvalid, base);
@@ -351,32 +365,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
     ln.ts64 = tsq;
     ln.tsr = lt.rel;
     int64_t tsv = 0;
-    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid, lane_off);
-    if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
-    if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, min(BN, kv_len), lane, base);
+    int kt = ht > 0 ? 0 : d0;
+    {
+      const int nv0 = min(BN, kv_len - kt * BN);
+      issue_kv<T, D>(sm, 0, Kh, Vh, ld, kt * BN, nv0, tid, lane_off);
+      if (wave == 0) tsv = p.ts[seq0 + kt * BN + min(lane, nv0 - 1)];
+      if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, nv0, lane, base);
+    }
     wait_loads();
     __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int cur = kt & 1;
+    for (int par = 0; kt <= last; ++par) {
+      const int cur = par & 1;
       const int key0 = kt * BN;
       const int nvalid = min(BN, kv_len - key0);
-      const bool more = kt + 1 < n_kt;
+      const int nkt = kt + 1 < ht ? kt + 1 : max(kt + 1, d0);
+      const bool more = nkt <= last;
+      const int nk0 = nkt * BN, nnv = more ? min(BN, kv_len - nk0) : 0;
       if (more) {
         // the timestamps first: they are staged half-way through the tile
         // (below), where waiting for them leaves the tile loads in flight
-        const int nk0 = key0 + BN, nnv = min(BN, kv_len - nk0);
         if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
         __builtin_amdgcn_sched_barrier(0);
         issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
       }
       const auto stage = [&] {
-        if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
+        if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, nnv, lane, base);
       };
       const TsTile<BN>& ts = sm.ts[cur];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       ln.lim = qpos - key0;
-      if (key0 + BN - 1 > wave_qmin || nvalid < BN || !fast) {
+      ln.hlim = hist - key0;
+      if (key0 + BN - 1 > wave_qmin || nvalid < BN || !fast || key0 + BN > hist) {
         fwd_tile<T, D, true>(oacc, sm.k[cur], sm.v[cur], ts, ops, qop, fast ? kModeLut : kModeWide, Plan{}, ln, bl,
                              stage);
       } else {
@@ -385,6 +405,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
       }
       wait_loads();
       __syncthreads();
+      kt = nkt;
     }
     if (qvalid) store_scaled<T, D>(O + qrow * ld + h * D, oacc, kNegLn2, g);
   }

@@ -16,6 +16,13 @@ namespace {
 
 constexpr int kSchedThreads = 1024;
 
+// Candidates of sequence b (length L), clamped to [0, L]; none without a list.
+__device__ __forceinline__ int candidates(const int64_t* num_targets, int b, int L) {
+  if (!num_targets) return 0;
+  const int64_t m = num_targets[b];
+  return (int)(m < 0 ? 0 : (m > L ? L : m));
+}
+
 struct SegInfo {
   int n;
   int pos0[2];
@@ -29,6 +36,14 @@ __device__ __forceinline__ SegInfo seq_segments(const SchedParams& p, int b, int
   const int64_t o0 = p.offsets[b];
   const int L = (int)(p.offsets[b + 1] - o0);
   SegInfo s;
+  if (p.targets_only) {  // the query rows are the candidates, the last num_targets[b] positions
+    const int m = candidates(p.num_targets, b, L);
+    s.n = 1;
+    s.pos0[0] = L - m;
+    s.len[0] = m;
+    s.lrow0[0] = local0;
+    return s;
+  }
   if (p.cp_size == 1) {
     s.n = 1;
     s.pos0[0] = 0;
@@ -50,6 +65,7 @@ __device__ __forceinline__ SegInfo seq_segments(const SchedParams& p, int b, int
 
 __device__ __forceinline__ int local_len(const SchedParams& p, int b) {
   const int64_t L = p.offsets[b + 1] - p.offsets[b];
+  if (p.targets_only) return candidates(p.num_targets, b, (int)L);
   if (p.cp_size == 1) return (int)L;
   const int nch = 2 * p.cp_size;
   const int c0 = p.cp_rank, c1 = nch - 1 - p.cp_rank;
@@ -96,7 +112,19 @@ __device__ __forceinline__ int owner(const int* off, int64_t B, int j) {
 struct QTile {
   int b, pos0, n;
   int64_t row0;
+  int cost;  // key tiles the forward visits
 };
+
+// Key tiles of q_cost_tile keys visited by a query tile ending at position
+// end (exclusive) that starts at pos0, with hist history rows: the causal
+// prefix, but past the history only the tiles that hold the tile's own rows
+// (a candidate sees no other candidate).
+__device__ __forceinline__ int q_tile_cost(int pos0, int end, int hist, int ct) {
+  const int ht = (min(end, hist) + ct - 1) / ct;
+  if (end <= hist) return ht;
+  const int d0 = max(max(pos0, hist) / ct, ht), last = (end - 1) / ct;
+  return ht + (last >= d0 ? last - d0 + 1 : 0);
+}
 
 // Flat query tile j: tiles of q_tile rows over the sequence's segments.
 __device__ __forceinline__ QTile query_tile(const SchedParams& p, int j) {
@@ -107,7 +135,10 @@ __device__ __forceinline__ QTile query_tile(const SchedParams& p, int j) {
   const int sg = i < n0 ? 0 : 1;
   if (sg == 1) i -= n0;
   const int r = i * p.q_tile;
-  return QTile{b, s.pos0[sg] + r, min(p.q_tile, s.len[sg] - r), s.lrow0[sg] + r};
+  const int pos0 = s.pos0[sg] + r, n = min(p.q_tile, s.len[sg] - r);
+  const int L = (int)(p.offsets[b + 1] - p.offsets[b]);
+  const int hist = L - candidates(p.num_targets, b, L);
+  return QTile{b, pos0, n, s.lrow0[sg] + r, q_tile_cost(pos0, pos0 + n, hist, p.q_cost_tile)};
 }
 
 struct KTile {
@@ -225,8 +256,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
 
   // Pass 1: cost histograms.
   for (int j = t; j < nqt; j += kSchedThreads) {
-    const QTile q = query_tile(p, j);
-    atomicAdd(&histq[clampc((q.pos0 + q.n + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
+    atomicAdd(&histq[clampc(query_tile(p, j).cost, hs)], 1);
   }
   for (int j = t; j < nkt; j += kSchedThreads) atomicAdd(&histk[clampc(key_tile(p, j).cost, hs)], 1);
   __syncthreads();
@@ -252,7 +282,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   // Pass 2: scatter.
   for (int j = t; j < nqt; j += kSchedThreads) {
     const QTile q = query_tile(p, j);
-    const int slot = atomicAdd(&histq[clampc((q.pos0 + q.n + p.q_cost_tile - 1) / p.q_cost_tile, hs)], 1);
+    const int slot = atomicAdd(&histq[clampc(q.cost, hs)], 1);
     p.qitems[slot] = Item{q.b, (int)q.row0, q.pos0, q.n};
   }
   for (int j = t; j < nkt; j += kSchedThreads) {

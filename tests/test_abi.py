@@ -81,7 +81,7 @@ def test_workspace_size_valid_and_monotone():
 def test_validation_errors(kw, status):
     p = make_problem(**kw)
     lib = _lib.load()
-    assert lib.hstu_workspace_size(ctypes.byref(p), 0) == 0
+    assert lib.hstu_workspace_size(ctypes.byref(p), 1) == 0
     dummy = ctypes.c_void_p(16)
     rc = lib.hstu_jagged_attn_fwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
                                   1 << 30, None)
@@ -194,3 +194,25 @@ def test_every_sub_bin_holds_at_most_one_edge():
             hi = lo + (1 << (oct_ - 5)) - 1
             inside = np.searchsorted(e, hi, side="right") - np.searchsorted(e, lo, side="right")
             assert inside.max() <= 1, (nb, oct_)
+
+
+def test_candidates_forward_validation():
+    lib = _lib.load()
+    dummy = ctypes.c_void_p(16)
+
+    def call(p, num_targets=dummy, only=0):
+        return lib.hstu_jagged_attn_fwd_targets(ctypes.byref(p), dummy, dummy, dummy, dummy, num_targets, only,
+                                                dummy, dummy, dummy, dummy, 1 << 30, None)
+
+    # a forward may query a subset of the rows (the candidates-only pass)
+    assert lib.hstu_workspace_size(ctypes.byref(make_problem(total_q=10)), 0) > 0
+    assert call(make_problem(cp_size=2, cp_rank=0, total_q=150)) == 2
+    assert call(make_problem(), only=2) == 1
+    assert call(make_problem(total_q=10), only=0) == 1
+    assert call(make_problem(total_q=400), only=1) == 1
+    assert call(make_problem(), num_targets=None) == 1
+    assert call(make_problem(), num_targets=ctypes.c_void_p(20)) == 1
+    # the plain forward still requires all rows
+    p = make_problem(total_q=10)
+    assert lib.hstu_jagged_attn_fwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                    1 << 30, None) == 1
