@@ -16,8 +16,10 @@ Besides the JSON contract fields it reports:
   cpu_baseline  the float64 oracle on a bounded sample of the same workload;
   extra         the other workloads: the CP=8 rank-3 share at length 16384
                 (forward+backward), its chunk-pair reorder in GB/s, the skewed
-                power-law batch (forward+backward) and the uniform 256..1024
-                forward.
+                power-law batch (forward+backward), the uniform 256..1024
+                forward, and the candidates pass: 16 users with a 3072-row
+                history and a micro-batch of 1024 candidates each, candidates
+                only against cached history K/V (candidates/s and TFLOP/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --counter-run          (the program profiled for HBM counters)
@@ -231,6 +233,40 @@ def time_loop(fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def candidates_pass(m, steps, users=16, hist=3072, cands=1024):
+    """Candidates-only forward against cached history K/V: each user's 3072
+    history rows plus a micro-batch of 1024 candidates, H=4, d=128, bf16.
+    Counted work: each candidate attends to its history and itself,
+    2*(d_qk+d_v) FLOP per pair and head."""
+    import numpy as np
+    import torch
+    import synth
+    wl = synth.custom([hist + cands] * users, num_heads=4, d_qk=128, d_v=128, num_buckets=128, dtype="bf16",
+                      gap_mean=3600.0, seed=1006, w_std=0.02, with_dout=False)
+
+    def up(t):
+        return torch.from_numpy(t.raw.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+    k, v, w = up(wl.k), up(wl.v), up(wl.w)
+    offsets = torch.from_numpy(wl.offsets).cuda()
+    ts = torch.from_numpy(wl.ts).cuda()
+    rows = np.concatenate([np.arange(int(wl.offsets[b + 1]) - cands, int(wl.offsets[b + 1])) for b in range(users)])
+    q = up(wl.q)[torch.from_numpy(rows).cuda()].contiguous()
+    nt = torch.full((users,), cands, dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+    p = m.problem(q, k, v, offsets, w, wl.max_seq_len)
+    ws = torch.empty(m.workspace_size(p, False), dtype=torch.uint8, device="cuda")
+
+    def run():
+        m.jagged_attn_fwd_targets(q, k, v, offsets, nt, ts, w, wl.max_seq_len, q_targets_only=True, out=out,
+                                  workspace=ws)
+
+    t = time_loop(run, steps, 2)
+    fl = 2 * (128 + 128) * users * cands * (hist + 1) * 4
+    return {"fwd_ms": round(t, 4), "candidates_per_s": round(users * cands / t * 1e3, 1),
+            "tflops": round(fl / t / 1e9, 2)}
+
+
 def cpu_baseline(max_seconds=30.0):
     """The float64 oracle, as it stands, on a bounded sample of the 3072-length
     workload: whole sequences (all 4 heads, forward + backward), as many as fit
@@ -406,6 +442,9 @@ def main():
         t2f = time_loop(c2.fwd, args.steps, 2)
         extra["u256_1024_forward"] = {"fwd_ms": round(t2f, 4), "tflops": round(f2f / t2f / 1e9, 2)}
         del c2
+        torch.cuda.empty_cache()
+        log("candidates against cached history")
+        extra["candidates_b16_hist3072_m1024"] = candidates_pass(m, args.steps)
 
     cpu = None
     if not args.no_cpu:
