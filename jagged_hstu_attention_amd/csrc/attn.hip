@@ -685,15 +685,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Backward, key-major pass for bf16 with d in {64, 128}: items of 64 keys,
-// four waves per workgroup, two workgroups per CU.  Waves w and w ^ 2 share
-// keys 32 (w % 2) .. + 31.  In every step of 64 query rows, wave w computes S
-// and dP only for the 32-row block hf = w / 2, and the pair swaps the
-// resulting P and G through LDS; each wave then accumulates dV and dK over
-// both blocks for its half hf of the head dimension.  A wave so holds half
-// the accumulators a full-width wave would and fits in 256 registers.  The
-// query/dO tile is single-buffered (the workgroup fits in half the CU's LDS):
-// while one workgroup waits for its next tile, the other computes.
+// Backward, key-major pass for bf16 with d in {64, 128}: items of 128 keys,
+// eight waves per workgroup, one workgroup per CU (two waves per SIMD).
+// Waves w and w ^ 4 share keys 32 (w % 4) .. + 31.  In every step of 64 query
+// rows, wave w computes S and dP only for the 32-row block hf = w / 4, and the
+// pair swaps the resulting P and G through LDS; each wave then accumulates dV
+// and dK over both blocks for its half hf of the head dimension.  A wave so
+// holds half the accumulators a full-width wave would and fits in 256
+// registers.  The query/dO tiles are double-buffered: the next step's tiles
+// load during the whole current step.  A wave whose block lies entirely before
+// its first key (the diagonal steps) skips its products: its P and G are zero.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -858,20 +859,20 @@ __device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dw
   pack16(own_g, pg);
 }
 
-constexpr int kHalfThreads = 256;
-constexpr int kHalfKeys = 64;
+constexpr int kHalfThreads = 512;
+constexpr int kHalfKeys = 128;
 constexpr int kHalfDwCopies = 4;
 
 template <int D> struct alignas(16) HalfSmem {
-  __bf16 q[BQ * D];
-  __bf16 d[BQ * D];
-  TsTile<BQ> ts[2];  // this step's and the next step's timestamps
+  __bf16 q[2][BQ * D];  // this step's and the next step's tiles
+  __bf16 d[2][BQ * D];
+  TsTile<BQ> ts[2];
 };
 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(kHalfThreads, 2) void bwd_kv_half_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const AttnParams p) {
   using M = Mma<__bf16>;
   using T = __bf16;
   constexpr int NT = kHalfThreads;
@@ -879,11 +880,11 @@ __global__ __launch_bounds__(kHalfThreads, 2) void bwd_kv_half_kernel(const Attn
   __shared__ HalfSmem<D> sm;
   __shared__ BiasLds bl;
   __shared__ float dwbins[kHalfDwCopies][kMaxBuckets + kPad];  // plan sums touch up to b_lo + 3
-  __shared__ u32x4 xch[4][4][64];  // per wave: P (2 operands) and G (2 operands), lane-contiguous
+  __shared__ u32x4 xch[8][4][64];  // per wave: P (2 operands) and G (2 operands), lane-contiguous
   __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kg = wave & 1, hf = wave >> 1;
+  const int kg = wave & 3, hf = wave >> 2;
   LaneOffsets<D> lo;
   lo.init(lane);
   HalfTrOffsets<D> to;
@@ -941,79 +942,92 @@ __global__ __launch_bounds__(kHalfThreads, 2) void bwd_kv_half_kernel(const Attn
     si.init(p, it.b, it.pos0);
     int64_t tsv = 0;
     if (si.valid()) {
-      tile_load_async<T, D, BQ, NT>(sm.q, Qh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
-      tile_load_async<T, D, BQ, NT>(sm.d, dOh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
+      tile_load_async<T, D, BQ, NT>(sm.q[0], Qh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
+      tile_load_async<T, D, BQ, NT>(sm.d[0], dOh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
       if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
     }
     wait_loads();
     if (wave == 0 && si.valid()) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
     __syncthreads();
-    const char* qb = reinterpret_cast<const char*>(sm.q);
-    const char* db = reinterpret_cast<const char*>(sm.d);
-    int cts = 0;
+    const int key_lo = it.pos0 + kg * 32;  // first key of this wave
+    int cur = 0;
     while (si.valid()) {
       const int q0 = si.q0;
       const int nq = si.nq();
       StepIter nx = si;
       nx.next();
-      // the next step's timestamps are loaded now and staged after the
-      // elementwise part, off the path between the tile barriers
-      if (nx.valid() && wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
-      const TsTile<BQ>& ts = sm.ts[cts];
+      if (nx.valid()) {
+        // the next step's timestamps, then its tiles into the other buffers;
+        // the timestamps are staged after the elementwise part (waiting for
+        // them there leaves the tile loads in flight)
+        if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        tile_load_async<T, D, BQ, NT>(sm.q[cur ^ 1], Qh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
+        tile_load_async<T, D, BQ, NT>(sm.d[cur ^ 1], dOh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
+      }
+      const char* qb = reinterpret_cast<const char*>(sm.q[cur]);
+      const char* db = reinterpret_cast<const char*>(sm.d[cur]);
+      const TsTile<BQ>& ts = sm.ts[cur];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       // rows r of this wave's block are visible iff lo_row <= r < hi_row
       const int lo_row = kpos - q0 - 32 * hf, hi_row = nq - 32 * hf;
       const bool masked = q0 + 32 * hf < wave_kmax || nq < BQ || !fast;
+      // a block whose rows all precede the wave's keys (or lie past the step)
+      // contributes nothing; the partner's block likewise
+      const bool live = q0 + 32 * hf + 31 >= key_lo && 32 * hf < nq;
+      const bool par_live = q0 + 32 * (hf ^ 1) + 31 >= key_lo && 32 * (hf ^ 1) < nq;
 
-      const f32x16 s = tile_mma_rows_o<D>(qb, lo, hf, kop);
-      const f32x16 dp = tile_mma_rows_o<D>(db, lo, hf, vop);
-      u32x4 own_p[2], own_g[2];
-      if (masked) {
-        if (fast)
-          pair_exact<false, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
-        else
-          pair_exact<true, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
-      } else {
-        const int2 br = ts.blk[hf];  // the plan covers this wave's block only
-        const Plan pl = make_plan<-1>(lt.rel, kvalid, br.x, br.y, bl);
-        const int mode = wave_mode(pl.n);
-        const int32_t* rows = (pl.flip ? ts.nu : ts.u) + hf * 32 + 4 * g;
+      u32x4 own_p[2] = {}, own_g[2] = {};
+      if (live) {
+        const f32x16 s = tile_mma_rows_o<D>(qb, lo, hf, kop);
+        const f32x16 dp = tile_mma_rows_o<D>(db, lo, hf, vop);
+        if (masked) {
+          if (fast)
+            pair_exact<false, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
+          else
+            pair_exact<true, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
+        } else {
+          const int2 br = ts.blk[hf];  // the plan covers this wave's block only
+          const Plan pl = make_plan<-1>(lt.rel, kvalid, br.x, br.y, bl);
+          const int mode = wave_mode(pl.n);
+          const int32_t* rows = (pl.flip ? ts.nu : ts.u) + hf * 32 + 4 * g;
 #define HSTU_PLAN(M) \
   pair_plan<M>(own_p, own_g, dwl, s, dp, rows, beta, pl.c0, pl.c1, pl.c2, pl.c3, pl.t1, pl.t2, pl.t3, pl.blo)
-        if (mode == kModeConst)
-          HSTU_PLAN(kModeConst);
-        else if (mode == kModeThr1)
-          HSTU_PLAN(kModeThr1);
-        else if (mode == kModeThr3)
-          HSTU_PLAN(kModeThr3);
-        else
-          pair_exact<false, false>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, 0, BQ);
+          if (mode == kModeConst)
+            HSTU_PLAN(kModeConst);
+          else if (mode == kModeThr1)
+            HSTU_PLAN(kModeThr1);
+          else if (mode == kModeThr3)
+            HSTU_PLAN(kModeThr3);
+          else
+            pair_exact<false, false>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, 0, BQ);
 #undef HSTU_PLAN
+        }
+        xch[wave][0][lane] = own_p[0];
+        xch[wave][1][lane] = own_p[1];
+        xch[wave][2][lane] = own_g[0];
+        xch[wave][3][lane] = own_g[1];
       }
-      xch[wave][0][lane] = own_p[0];
-      xch[wave][1][lane] = own_p[1];
-      xch[wave][2][lane] = own_g[0];
-      xch[wave][3][lane] = own_g[1];
-      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cts ^ 1], tsv, nx.nq(), lane, base);
+      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cur ^ 1], tsv, nx.nq(), lane, base);
       __syncthreads();
-      const int pw = wave ^ 2;
-      const u32x4 par_p[2] = {xch[pw][0][lane], xch[pw][1][lane]};
-      const u32x4 par_g[2] = {xch[pw][2][lane], xch[pw][3][lane]};
-      contract_half<D>(dvacc, db, to, own_p, hf);
-      contract_half<D>(dkacc, qb, to, own_g, hf);
-      contract_half<D>(dvacc, db, to, par_p, hf ^ 1);
-      contract_half<D>(dkacc, qb, to, par_g, hf ^ 1);
-      // the tile (and the exchange slots) are free once every wave is here
-      __syncthreads();
-      if (nx.valid()) {
-        tile_load_async<T, D, BQ, NT>(sm.q, Qh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
-        tile_load_async<T, D, BQ, NT>(sm.d, dOh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
+      if (live) {
+        contract_half<D>(dvacc, db, to, own_p, hf);
+        contract_half<D>(dkacc, qb, to, own_g, hf);
       }
+      if (par_live) {
+        const int pw = wave ^ 4;
+        const u32x4 par_p[2] = {xch[pw][0][lane], xch[pw][1][lane]};
+        const u32x4 par_g[2] = {xch[pw][2][lane], xch[pw][3][lane]};
+        contract_half<D>(dvacc, db, to, par_p, hf ^ 1);
+        contract_half<D>(dkacc, qb, to, par_g, hf ^ 1);
+      }
+      // the next tiles have landed, and every wave is done with this step's
+      // tiles and exchange slots, once all waves are here
       wait_loads();
       __syncthreads();
       si = nx;
-      cts ^= 1;
+      cur ^= 1;
     }
     if (kvalid) {
       store_scaled<T, D / 2>(dK + krow * ld + h * D + hf * (D / 2), dkacc, p.alpha, g);
