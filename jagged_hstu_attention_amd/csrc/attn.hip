@@ -731,6 +731,50 @@ __device__ __forceinline__ void contract_half(f32x16* out, const char* __restric
     }
 }
 
+// Rows of block blk of bf16 tile a against rows of block bblk of bf16 tile b
+// (both operands read from LDS with the same lane offsets).
+template <int D>
+__device__ __forceinline__ f32x16 tile_mma_rows_oo(const char* __restrict__ a, const char* __restrict__ b,
+                                                   const LaneOffsets<D>& lo, int blk, int bblk) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    acc = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a + lo.row[kk] + blk * 32 * D * 2)),
+                           __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(b + lo.row[kk] + bblk * 32 * D * 2)),
+                           acc);
+  return acc;
+}
+
+// S = Q Kᵀ (K operands in registers) and dP = dO Vᵀ (V rows from LDS) for
+// block blk of the query/dO tiles, the LDS operands of slice kk + 1 read while
+// the MFMAs of slice kk run.
+template <int D>
+__device__ __forceinline__ void sdp_products(f32x16& s, f32x16& dp, const char* __restrict__ qb,
+                                             const char* __restrict__ db, const char* __restrict__ vb,
+                                             const LaneOffsets<D>& lo, int blk, int vblk, const bf16x8* kop) {
+  s = f32x16{};
+  dp = f32x16{};
+  const int qo = blk * 32 * D * 2, vo = vblk * 32 * D * 2;
+  u32x4 qa = *reinterpret_cast<const u32x4*>(qb + lo.row[0] + qo);
+  u32x4 da = *reinterpret_cast<const u32x4*>(db + lo.row[0] + qo);
+  u32x4 va = *reinterpret_cast<const u32x4*>(vb + lo.row[0] + vo);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 qn = qa, dn = da, vn = va;
+    if (kk + 1 < D / 16) {
+      qn = *reinterpret_cast<const u32x4*>(qb + lo.row[kk + 1] + qo);
+      dn = *reinterpret_cast<const u32x4*>(db + lo.row[kk + 1] + qo);
+      vn = *reinterpret_cast<const u32x4*>(vb + lo.row[kk + 1] + vo);
+    }
+    s = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, qa), kop[kk], s);
+    dp = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, da), __builtin_bit_cast(bf16x8, va), dp);
+    __builtin_amdgcn_sched_barrier(0);
+    qa = qn;
+    da = dn;
+    va = vn;
+  }
+}
+
 __device__ __forceinline__ void pack16(u32x4* dst, const float* v) {
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -866,6 +910,7 @@ constexpr int kHalfDwCopies = 4;
 template <int D> struct alignas(16) HalfSmem {
   __bf16 q[2][BQ * D];  // this step's and the next step's tiles
   __bf16 d[2][BQ * D];
+  __bf16 v[kHalfKeys * D];  // the item's V rows
   TsTile<BQ> ts[2];
 };
 
@@ -915,15 +960,12 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     const int kpos = it.pos0 + kj;
     const int64_t krow = (int64_t)it.row0 + kj;
     const int64_t tsk = kvalid ? p.ts[krow] : 0;
-    bf16x8 kop[D / 16], vop[D / 16];
+    // K operands in registers; the V rows are read from LDS in every step
+    bf16x8 kop[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       kop[kk] = bf16x8{};
-      vop[kk] = bf16x8{};
-      if (kvalid) {
-        kop[kk] = M::load(K + krow * ld + h * D + kk * 16 + g * 8);
-        vop[kk] = M::load(V + krow * ld + h * D + kk * 16 + g * 8);
-      }
+      if (kvalid) kop[kk] = M::load(K + krow * ld + h * D + kk * 16 + g * 8);
     }
     load_bias_values<T, NT>(bl, p, h, tid);
     for (int i = tid; i < kHalfDwCopies * (kMaxBuckets + kPad); i += NT) (&dwbins[0][0])[i] = 0.0f;
@@ -941,6 +983,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     StepIter si;
     si.init(p, it.b, it.pos0);
     int64_t tsv = 0;
+    tile_load_async<T, D, kHalfKeys, NT>(sm.v, V + (int64_t)it.row0 * ld + h * D, ld, it.n, tid, lane_off);
     if (si.valid()) {
       tile_load_async<T, D, BQ, NT>(sm.q[0], Qh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
       tile_load_async<T, D, BQ, NT>(sm.d[0], dOh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
@@ -949,6 +992,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     wait_loads();
     if (wave == 0 && si.valid()) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
     __syncthreads();
+    const char* vb = reinterpret_cast<const char*>(sm.v);
     const int key_lo = it.pos0 + kg * 32;  // first key of this wave
     int cur = 0;
     while (si.valid()) {
@@ -980,8 +1024,12 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
 
       u32x4 own_p[2] = {}, own_g[2] = {};
       if (live) {
-        const f32x16 s = tile_mma_rows_o<D>(qb, lo, hf, kop);
-        const f32x16 dp = tile_mma_rows_o<D>(db, lo, hf, vop);
+        f32x16 s, dp;
+        sdp_products<D>(s, dp, qb, db, vb, lo, hf, kg, kop);
+        // rows of the V tile past the item's end repeat its last row: a key
+        // lane past the end must have dP = 0 (so G and its d(ts_weights)
+        // contributions vanish)
+        if (!kvalid) dp = f32x16{};
         if (masked) {
           if (fast)
             pair_exact<false, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
