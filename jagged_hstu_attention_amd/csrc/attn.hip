@@ -57,6 +57,30 @@ template <int D> struct TileOps<__bf16, D> {
   __device__ __forceinline__ f32x16 rows(const __bf16* t, int blk, const bf16x8* op) const {
     return tile_mma_rows_o<D>(reinterpret_cast<const char*>(t), lo, blk, op);
   }
+  // rows(a, blk, opa) and rows(b, blk, opb) as one stream: the LDS operands
+  // of slice kk + 1 are read while the two MFMAs of slice kk run
+  __device__ __forceinline__ void rows2(f32x16& ra, f32x16& rb, const __bf16* a, const __bf16* b, int blk,
+                                        const bf16x8* opa, const bf16x8* opb) const {
+    const char* pa = reinterpret_cast<const char*>(a) + blk * 32 * D * 2;
+    const char* pb = reinterpret_cast<const char*>(b) + blk * 32 * D * 2;
+    ra = f32x16{};
+    rb = f32x16{};
+    u32x4 xa = *reinterpret_cast<const u32x4*>(pa + lo.row[0]);
+    u32x4 xb = *reinterpret_cast<const u32x4*>(pb + lo.row[0]);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 ya = xa, yb = xb;
+      if (kk + 1 < D / 16) {
+        ya = *reinterpret_cast<const u32x4*>(pa + lo.row[kk + 1]);
+        yb = *reinterpret_cast<const u32x4*>(pb + lo.row[kk + 1]);
+      }
+      ra = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, xa), opa[kk], ra);
+      rb = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, xb), opb[kk], rb);
+      __builtin_amdgcn_sched_barrier(0);
+      xa = ya;
+      xb = yb;
+    }
+  }
   __device__ __forceinline__ void contract(f32x16* out, const __bf16* t, const float* vals, int blk) const {
     tile_contract_block_o<D>(out, reinterpret_cast<const char*>(t), lo, vals, blk);
   }
@@ -1105,8 +1129,13 @@ __device__ __forceinline__ void q_tile(f32x16* dqacc, const T* kt, const T* vt, 
                                        const FwdLane& ln, const BiasLds& bl, Mid&& mid) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const f32x16 s = ops.rows(kt, blk, qop);
-    const f32x16 dp = ops.rows(vt, blk, dop);
+    f32x16 s, dp;
+    if constexpr (sizeof(T) == 2) {
+      ops.rows2(s, dp, kt, vt, blk, qop, dop);
+    } else {
+      s = ops.rows(kt, blk, qop);
+      dp = ops.rows(vt, blk, dop);
+    }
     float cb[16];
     block_bias_mode<+1, BN, false, MASK>(cb, nullptr, mode, pl, ln.tsr, ln.ts64, ts, blk, ln.g, bl, ln.nb);
     float gv[16];
