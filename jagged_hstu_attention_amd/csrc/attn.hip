@@ -527,7 +527,7 @@ __device__ __forceinline__ void kv_tile_plan(f32x16* dkacc, f32x16* dvacc, DwSum
                                              const typename Mma<T>::operand* vop, const float c0, const float c1,
                                              const float c2, const float c3, const int32_t t1, const int32_t t2,
                                              const int32_t t3, const int flip, const float beta) {
-  const int32_t* varr = flip ? ts.nu : ts.u;
+  const int32_t* varr = ts.un[flip ? 1 : 0];
   const int g = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
@@ -819,12 +819,13 @@ __device__ __forceinline__ void silu_grad(float s, float dp, float beta, float c
 // Thr3): each element's bias by compares of the other row's timestamp offset
 // (rows[], this lane's four-row runs) with the lane's thresholds, SiLU and its
 // gradient, P and G packed to bf16, and the d(ts_weights) contributions summed
-// per passed edge and added once per step.  An edge the tile does not cross is
-// never passed, so its sum is zero.
+// per passed edge into dw4 (bins b_lo .. b_lo + 3; the caller adds them to the
+// LDS bins).  An edge the tile does not cross is never passed, so its sum is
+// zero.
 template <int MODE>
-__device__ __forceinline__ void pair_plan(u32x4* own_p, u32x4* own_g, float* dwl, const f32x16& s, const f32x16& dp,
+__device__ __forceinline__ void pair_plan(u32x4* own_p, u32x4* own_g, float* dw4, const f32x16& s, const f32x16& dp,
                                           const int32_t* __restrict__ rows, float beta, float c0, float c1, float c2,
-                                          float c3, int32_t t1, int32_t t2, int32_t t3, int blo) {
+                                          float c3, int32_t t1, int32_t t2, int32_t t3) {
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
   float pa[16], pg[16];
 #pragma unroll
@@ -858,12 +859,12 @@ __device__ __forceinline__ void pair_plan(u32x4* own_p, u32x4* own_g, float* dwl
   }
   pack16(own_p, pa);
   pack16(own_g, pg);
-  atomicAdd(&dwl[blo], s0 - s1);
-  if constexpr (MODE != kModeConst) atomicAdd(&dwl[blo + 1], s1 - s2);
-  if constexpr (MODE == kModeThr3) {
-    atomicAdd(&dwl[blo + 2], s2 - s3);
-    atomicAdd(&dwl[blo + 3], s3);
-  }
+  // the contributions to bins b_lo .. b_lo + 3 (an edge the mode does not
+  // test contributes nothing)
+  dw4[0] = s0 - s1;
+  dw4[1] = s1 - s2;
+  dw4[2] = s2 - s3;
+  dw4[3] = s3;
 }
 
 // Elementwise part with the exact bucket per element (32-bit offsets from the
@@ -883,7 +884,7 @@ __device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dw
   for (int q4 = 0; q4 < 4; ++q4) {
     const int r0 = q4 * 8 + 4 * g;
     int4 v4 = {0, 0, 0, 0};
-    if constexpr (!WIDE) v4 = *reinterpret_cast<const int4*>(ts.u + blk * 32 + r0);
+    if constexpr (!WIDE) v4 = *reinterpret_cast<const int4*>(ts.un[0] + blk * 32 + r0);
     const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -960,7 +961,13 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
   to.init(lane, hf);
   const int H = p.H, NB = p.NB;
   const int64_t ld = (int64_t)H * D;
-  const uint32_t lane_off = tile_lane_offset<T, D, NT>(tid, ld);
+  // waves 4-7 load the query/dO tiles (their LDS bin updates are deferred past
+  // the load wait, see below); waves 0-3 never have a tile load in flight, so
+  // wave 0's timestamp staging waits only for its own timestamp load
+  constexpr int NL = NT / 2;
+  const bool loader = wave >= 4;
+  const uint32_t lane_off = tile_lane_offset<T, D, NL>(tid & (NL - 1), ld);
+  const uint32_t lane_off_all = tile_lane_offset<T, D, NT>(tid, ld);
   const T* Q = static_cast<const T*>(p.q);
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
@@ -1007,10 +1014,10 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     StepIter si;
     si.init(p, it.b, it.pos0);
     int64_t tsv = 0;
-    tile_load_async<T, D, kHalfKeys, NT>(sm.v, V + (int64_t)it.row0 * ld + h * D, ld, it.n, tid, lane_off);
+    tile_load_async<T, D, kHalfKeys, NT>(sm.v, V + (int64_t)it.row0 * ld + h * D, ld, it.n, tid, lane_off_all);
     if (si.valid()) {
-      tile_load_async<T, D, BQ, NT>(sm.q[0], Qh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
-      tile_load_async<T, D, BQ, NT>(sm.d[0], dOh + si.lrow() * ld, ld, si.nq(), tid, lane_off);
+      tile_load_async<T, D, BQ, NT>(sm.q[0], Qh + si.lrow() * ld, ld, si.nq(), tid, lane_off_all);
+      tile_load_async<T, D, BQ, NT>(sm.d[0], dOh + si.lrow() * ld, ld, si.nq(), tid, lane_off_all);
       if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
     }
     wait_loads();
@@ -1029,9 +1036,10 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         // the timestamps are staged after the elementwise part (waiting for
         // them there leaves the tile loads in flight)
         if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
-        __builtin_amdgcn_sched_barrier(0);
-        tile_load_async<T, D, BQ, NT>(sm.q[cur ^ 1], Qh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
-        tile_load_async<T, D, BQ, NT>(sm.d[cur ^ 1], dOh + nx.lrow() * ld, ld, nx.nq(), tid, lane_off);
+        if (loader) {
+          tile_load_async<T, D, BQ, NL>(sm.q[cur ^ 1], Qh + nx.lrow() * ld, ld, nx.nq(), tid - NL, lane_off);
+          tile_load_async<T, D, BQ, NL>(sm.d[cur ^ 1], dOh + nx.lrow() * ld, ld, nx.nq(), tid - NL, lane_off);
+        }
       }
       const char* qb = reinterpret_cast<const char*>(sm.q[cur]);
       const char* db = reinterpret_cast<const char*>(sm.d[cur]);
@@ -1047,6 +1055,8 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
       const bool par_live = q0 + 32 * (hf ^ 1) + 31 >= key_lo && 32 * (hf ^ 1) < nq;
 
       u32x4 own_p[2] = {}, own_g[2] = {};
+      float dw4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // plan steps: bins blo .. blo + 3, added after the load wait
+      int blo = 0;
       if (live) {
         f32x16 s, dp;
         sdp_products<D>(s, dp, qb, db, vb, lo, hf, kg, kop);
@@ -1063,9 +1073,9 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
           const int2 br = ts.blk[hf];  // the plan covers this wave's block only
           const Plan pl = make_plan<-1>(lt.rel, kvalid, br.x, br.y, bl);
           const int mode = wave_mode(pl.n);
-          const int32_t* rows = (pl.flip ? ts.nu : ts.u) + hf * 32 + 4 * g;
-#define HSTU_PLAN(M) \
-  pair_plan<M>(own_p, own_g, dwl, s, dp, rows, beta, pl.c0, pl.c1, pl.c2, pl.c3, pl.t1, pl.t2, pl.t3, pl.blo)
+          const int32_t* rows = ts.un[pl.flip ? 1 : 0] + hf * 32 + 4 * g;
+          blo = pl.blo;
+#define HSTU_PLAN(M) pair_plan<M>(own_p, own_g, dw4, s, dp, rows, beta, pl.c0, pl.c1, pl.c2, pl.c3, pl.t1, pl.t2, pl.t3)
           if (mode == kModeConst)
             HSTU_PLAN(kModeConst);
           else if (mode == kModeThr1)
@@ -1097,6 +1107,10 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
       // the next tiles have landed, and every wave is done with this step's
       // tiles and exchange slots, once all waves are here
       wait_loads();
+      if (dw4[0] != 0.0f) atomicAdd(&dwl[blo], dw4[0]);
+      if (dw4[1] != 0.0f) atomicAdd(&dwl[blo + 1], dw4[1]);
+      if (dw4[2] != 0.0f) atomicAdd(&dwl[blo + 2], dw4[2]);
+      if (dw4[3] != 0.0f) atomicAdd(&dwl[blo + 3], dw4[3]);
       __syncthreads();
       si = nx;
       cur ^= 1;

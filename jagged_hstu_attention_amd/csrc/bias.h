@@ -59,11 +59,11 @@ __device__ __forceinline__ int lut_bucket64(int64_t d, int nb, const u32x2* __re
 // Timestamps of the tile's other rows, staged in LDS by one wave, relative to
 // the base of the work item (the first timestamp of its sequence).  Rows past
 // the last valid one repeat its timestamp.  u = ts - base and nu = ~u (for
-// compares whose direction is flipped); hdr = {min u, max u, wide, 0} over the
-// tile and blk[b] = {min u, max u} over its 32-row block b.
+// compares whose direction is flipped), held as un[0] and un[1] so that a
+// flip selects by index; hdr = {min u, max u, wide, 0} over the tile and
+// blk[b] = {min u, max u} over its 32-row block b.
 template <int N> struct alignas(16) TsTile {
-  int32_t u[N];
-  int32_t nu[N];
+  int32_t un[2][N];
   int64_t t64[N];
   int4 hdr;  // wide: some |ts - base| is 2^30 or more, only the 64-bit path is exact
   int2 blk[N / 32];
@@ -86,8 +86,8 @@ __device__ __forceinline__ void ts_tile_fill(TsTile<N>& t, int64_t ts, int nvali
     mx = max(mx, __shfl_xor(mx, off));
   }
   // mn/mx now hold the range of this lane's 32-row half
-  t.u[lane] = r32;
-  t.nu[lane] = ~r32;
+  t.un[0][lane] = r32;
+  t.un[1][lane] = ~r32;
   t.t64[lane] = v;
   if ((lane & 31) == 0) t.blk[lane >> 5] = int2{mn, mx};
   const int32_t mn2 = min(mn, __shfl_xor(mn, 32)), mx2 = max(mx, __shfl_xor(mx, 32));
@@ -176,7 +176,7 @@ __device__ __forceinline__ void block_bias(float* cb, int* key, float c0, float 
       if constexpr (KEYS) key[i] = 0;
     }
   } else if constexpr (MODE == kModeThr1 || MODE == kModeThr3) {
-    block_rows_i32(v, flip ? t.nu : t.u, blk, g);
+    block_rows_i32(v, flip ? t.un[1] : t.un[0], blk, g);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool p1 = v[i] <= t1;
@@ -192,7 +192,7 @@ __device__ __forceinline__ void block_bias(float* cb, int* key, float c0, float 
       if constexpr (KEYS) key[i] = k;
     }
   } else if constexpr (MODE == kModeLut) {
-    block_rows_i32(v, t.u, blk, g);
+    block_rows_i32(v, t.un[0], blk, g);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int32_t d = SIGMA > 0 ? tsr - v[i] : v[i] - tsr;
