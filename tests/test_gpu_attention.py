@@ -179,6 +179,51 @@ def test_all_sequences_empty():
     assert float(dw.abs().max()) == 0.0
 
 
+def _wide_timestamp_workload(dtype, dim, seed):
+    # one sequence with ordinary gaps next to sequences whose timestamps span
+    # more than 2^32 (|ts - first| past 2^30 takes the 64-bit path; pairs with
+    # |dt| >= 2^32 fall in the last bucket)
+    lengths = [300, 129, 64, 1, 200]
+    wl = synth.custom(lengths, num_heads=2, d_qk=dim, d_v=dim, num_buckets=128, dtype=dtype,
+                      gap_mean=3.0e7, seed=seed, w_std=0.5)
+    small = synth.custom([lengths[0]], num_heads=2, d_qk=dim, d_v=dim, num_buckets=128, dtype=dtype,
+                         gap_mean=3600.0, seed=seed + 1)
+    wl.ts[: lengths[0]] = small.ts
+    spans = [int(wl.ts[wl.offsets[b + 1] - 1] - wl.ts[wl.offsets[b]]) for b in range(1, 5) if lengths[b] > 1]
+    assert max(spans) >= 2 ** 32, spans
+    return wl
+
+
+@pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+def test_wide_timestamp_spans(dtype, dim):
+    wl = _wide_timestamp_workload(dtype, dim, seed=40 + dim)
+    d = upload(wl)
+    assert_close(to_f64(run_fwd(wl, d)), oracle_fwd(wl), dtype, "out")
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    for name, got, r in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(to_f64(got), r, dtype, name)
+
+
+@pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("fp32", 32)])
+def test_unsorted_timestamps(dtype, dim):
+    # timestamps shuffled inside each sequence: dt takes both signs, and tiles
+    # whose rows lie on both sides of a lane's own timestamp use the exact
+    # per-element bucket
+    wl = synth.custom([257, 64, 130, 3], num_heads=2, d_qk=dim, d_v=dim, num_buckets=100, dtype=dtype,
+                      gap_mean=3600.0, seed=50 + dim, w_std=0.5)
+    rng = np.random.default_rng(7)
+    for b in range(wl.num_seqs):
+        lo, hi = int(wl.offsets[b]), int(wl.offsets[b + 1])
+        wl.ts[lo:hi] = rng.permutation(wl.ts[lo:hi])
+    d = upload(wl)
+    assert_close(to_f64(run_fwd(wl, d)), oracle_fwd(wl), dtype, "out")
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    for name, got, r in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(to_f64(got), r, dtype, name)
+
+
 def test_causality_on_gpu():
     import torch
     wl = synth.custom([400], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=16)
