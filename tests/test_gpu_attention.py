@@ -224,6 +224,20 @@ def test_unsorted_timestamps(dtype, dim):
         assert_close(to_f64(got), r, dtype, name)
 
 
+@pytest.mark.parametrize("dtype,dim,nb", [("bf16", 128, 1), ("bf16", 128, 2), ("bf16", 64, 512), ("fp32", 64, 512)])
+def test_bucket_count_extremes(dtype, dim, nb):
+    # NB = 1: every pair in one bucket; NB = 512: edges 2^(1/16) apart, many of
+    # them crossed inside a tile (gaps of about 2^20 spread dt over 2^20..2^29)
+    wl = synth.custom([200, 65, 1, 130], num_heads=2, d_qk=dim, d_v=dim, num_buckets=nb, dtype=dtype,
+                      gap_mean=float(1 << 20), seed=60 + nb, w_std=0.5)
+    d = upload(wl)
+    assert_close(to_f64(run_fwd(wl, d)), oracle_fwd(wl), dtype, "out")
+    dq, dk, dv, dw = run_bwd(wl, d)
+    rq, rk, rv, rw = oracle_bwd(wl)
+    for name, got, r in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(to_f64(got), r, dtype, name)
+
+
 def test_causality_on_gpu():
     import torch
     wl = synth.custom([400], num_heads=2, d_qk=128, d_v=128, dtype="bf16", seed=16)
