@@ -755,20 +755,6 @@ __device__ __forceinline__ void contract_half(f32x16* out, const char* __restric
     }
 }
 
-// Rows of block blk of bf16 tile a against rows of block bblk of bf16 tile b
-// (both operands read from LDS with the same lane offsets).
-template <int D>
-__device__ __forceinline__ f32x16 tile_mma_rows_oo(const char* __restrict__ a, const char* __restrict__ b,
-                                                   const LaneOffsets<D>& lo, int blk, int bblk) {
-  f32x16 acc = {};
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    acc = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a + lo.row[kk] + blk * 32 * D * 2)),
-                           __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(b + lo.row[kk] + bblk * 32 * D * 2)),
-                           acc);
-  return acc;
-}
-
 // S = Q Kᵀ (K operands in registers) and dP = dO Vᵀ (V rows from LDS) for
 // block blk of the query/dO tiles, the LDS operands of slice kk + 1 read while
 // the MFMAs of slice kk run.
