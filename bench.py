@@ -120,8 +120,10 @@ class Case:
 
 def kernel_flops(pairs, heads, dqk, dv):
     """Algorithmic FLOPs per launch of each attention kernel.  The dK/dV pass
-    computes S, dP, dV and dK; the dQ pass is credited with dQ only (its S and
-    dP are recomputation).  fwd + bwd_kv + bwd_q equals the counted total."""
+    computes S, dP, dV and dK; the dQ pass is credited with dQ only (with bf16
+    and d >= 64 it reads the score gradient the dK/dV pass stored; otherwise its
+    S and dP are recomputation).  fwd + bwd_kv + bwd_q equals the counted
+    total."""
     return {"fwd": 2 * (dqk + dv) * pairs * heads,
             "bwd_kv": 4 * (dqk + dv) * pairs * heads,
             "bwd_q": 2 * dqk * pairs * heads}
@@ -160,9 +162,10 @@ def stored_traffic(kernel):
 
 COUNTER_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o <name> -- "
                "python bench.py --counter-run")
-# Substrings of the kernel symbols (the dK/dV pass runs bwd_kv_half_kernel for
-# bf16 with d >= 64, bwd_kv_kernel otherwise).
-KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_", "bwd_q": "bwd_q_kernel", "sched": "sched_kernel"}
+# Substrings of the kernel symbols (for bf16 with d >= 64 the backward runs
+# bwd_kv_half_kernel and bwd_q_g_kernel, otherwise bwd_kv_kernel and
+# bwd_q_kernel).
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_", "bwd_q": "bwd_q_", "sched": "sched_kernel"}
 
 
 def traffic_summary(fetch_csv, write_csv, out_path):
@@ -397,7 +400,7 @@ def main():
     achieved = kfl[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(dom),
-                "kernel": {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_half_kernel", "bwd_q": "bwd_q_kernel"}[dom],
+                "kernel": {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_half_kernel", "bwd_q": "bwd_q_g_kernel"}[dom],
                 "ms_per_launch": round(kms[dom], 4), "flop_per_launch": kfl[dom]}
 
     extra = {

@@ -54,6 +54,15 @@ extern "C" {
 
 typedef enum { HSTU_BF16 = 0, HSTU_FP32 = 1 } hstu_dtype_t;
 
+/* Problem flags (hstu_problem_t.flags). */
+enum {
+  /* Backward keeps to the memory-efficient form of the HSTU paper's App. F.3
+   * (Actions Speak Louder than Words): nothing of the size of the attention
+   * matrix is stored; the query-major pass recomputes the score gradient
+   * instead of reading it from the workspace.  Smaller workspace, slower. */
+  HSTU_FLAG_RECOMPUTE_BWD = 1
+};
+
 typedef enum {
   HSTU_OK = 0,
   HSTU_EINVAL = 1,        /* bad argument (null pointer, bad size, bad rank) */
@@ -65,7 +74,7 @@ typedef enum {
 /* Problem description shared by the attention calls. */
 typedef struct {
   int32_t dtype;        /* hstu_dtype_t of q, k, v, out, dout, ts_weights, dq, dk, dv */
-  int32_t reserved;     /* must be 0 */
+  int32_t flags;        /* 0 or HSTU_FLAG_RECOMPUTE_BWD; other bits must be 0 */
   int64_t num_seqs;     /* B >= 0 */
   int64_t num_heads;    /* H >= 1 */
   int64_t d_qk;         /* Q/K head width; supported: 32, 64, 128 */
@@ -136,7 +145,17 @@ int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q,
  * With cp_size > 1, dk, dv and d_ts_weights are this rank's partial sums (zero
  * rows for keys no local query reaches); summing them over the C ranks gives
  * the gradients of the unsharded problem.  Nothing is normalised, so no
- * forward statistics are needed: the score tile is recomputed. */
+ * forward statistics are needed: the score tile is recomputed.  With bf16,
+ * d_qk >= 64 and cp_size == 1 the key-major pass also stores the score
+ * gradient G = dS (bf16, one 64-key x 128-query block per causal tile pair,
+ * H * sum_b n_b (n_b + 1) blocks of 16 KiB, n_b = ceil(L_b / 128)) in the
+ * workspace and the query-major pass computes dQ = G K from it (unless
+ * p->flags has HSTU_FLAG_RECOMPUTE_BWD);
+ * hstu_workspace_size(p, 1) then includes room for H (N + 1)
+ * (ceil(total_kv / 128) + B) blocks, N = ceil(max_seq_len / 128), unless
+ * that passes 16 GiB, in which case dQ recomputes G instead.  Here
+ * max_seq_len must bound every sequence length (blocks beyond the room are
+ * dropped, not written out of bounds). */
 int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* q,
                          const void* k, const void* v, const int64_t* offsets,
                          const int64_t* timestamps, const void* ts_weights,

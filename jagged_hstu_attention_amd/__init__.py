@@ -20,10 +20,11 @@ import math
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import HSTU_BF16, HSTU_FP32, HstuError, Problem  # noqa: F401
+from ._lib import HSTU_BF16, HSTU_FLAG_RECOMPUTE_BWD, HSTU_FP32, HstuError, Problem  # noqa: F401
 
 __all__ = [
-    "Problem", "HstuError", "problem", "workspace_size", "jagged_attn_fwd", "jagged_attn_bwd",
+    "Problem", "HstuError", "HSTU_FLAG_RECOMPUTE_BWD", "problem", "workspace_size", "jagged_attn_fwd",
+    "jagged_attn_fwd_targets", "jagged_attn_bwd",
     "cp_reorder", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
 ]
 
@@ -63,11 +64,13 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def problem(q, k, v, offsets, ts_weights, max_seq_len: int, *, cp_size: int = 1, cp_rank: int = 0) -> Problem:
-    """Fill the hstu_problem_t for these tensors (host metadata only)."""
+def problem(q, k, v, offsets, ts_weights, max_seq_len: int, *, cp_size: int = 1, cp_rank: int = 0,
+            recompute_bwd: bool = False) -> Problem:
+    """Fill the hstu_problem_t for these tensors (host metadata only).
+    recompute_bwd: the memory-efficient backward (no stored score gradient)."""
     p = Problem()
     p.dtype = _dtype_code(q)
-    p.reserved = 0
+    p.flags = HSTU_FLAG_RECOMPUTE_BWD if recompute_bwd else 0
     p.num_seqs = int(offsets.shape[0]) - 1
     p.num_heads = int(q.shape[1])
     p.d_qk = int(q.shape[2])
@@ -130,10 +133,14 @@ def jagged_attn_fwd_targets(q, k, v, offsets, num_targets, ts, ts_weights, max_s
 
 
 def jagged_attn_bwd(dout, q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1,
-                    cp_rank: int = 0, dq=None, dk=None, dv=None, dw=None, workspace=None):
-    """Backward; returns (dq, dk, dv, d_ts_weights) with d_ts_weights in fp32."""
+                    cp_rank: int = 0, dq=None, dk=None, dv=None, dw=None, workspace=None,
+                    recompute: bool = False):
+    """Backward; returns (dq, dk, dv, d_ts_weights) with d_ts_weights in fp32.
+    recompute: memory-efficient form (the dQ pass recomputes the score
+    gradient instead of reading it from the workspace)."""
     torch = _torch()
-    p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank)
+    p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank,
+                recompute_bwd=recompute)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

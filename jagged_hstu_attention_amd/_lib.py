@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libhstu.so")
 
 HSTU_BF16 = 0
 HSTU_FP32 = 1
+HSTU_FLAG_RECOMPUTE_BWD = 1
 
 STATUS = {0: "HSTU_OK", 1: "HSTU_EINVAL", 2: "HSTU_EUNSUPPORTED", 3: "HSTU_EWORKSPACE", 4: "HSTU_EHIP"}
 
@@ -21,7 +22,7 @@ STATUS = {0: "HSTU_OK", 1: "HSTU_EINVAL", 2: "HSTU_EUNSUPPORTED", 3: "HSTU_EWORK
 class Problem(ctypes.Structure):
     _fields_ = [
         ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("num_seqs", ctypes.c_int64),
         ("num_heads", ctypes.c_int64),
         ("d_qk", ctypes.c_int64),

@@ -161,11 +161,28 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ctr, edges, lut, local_off, tile_off, qitems, kitems, total;
-  int64_t max_qtiles, max_ktiles;
+  size_t ctr, edges, lut, local_off, tile_off, qitems, kitems, gblk_off, g, total;
+  int64_t max_qtiles, max_ktiles, g_blocks;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Stored score gradients (backward, bf16, d >= 64, cp_size 1): the dK/dV pass
+// writes G, the dQ pass reads it instead of recomputing it.  Blocks needed:
+// sum over sequences and heads of n(n+1), n = ceil(L / kGRows).  Bound from
+// host metadata (every L <= max_seq_len): n <= N = ceil(max_seq_len / kGRows)
+// and sum n <= ceil(T / kGRows) + B, so H (N + 1) (ceil(T / kGRows) + B).
+// 0 (recompute) when the path does not apply, the caller asks for the
+// memory-efficient backward, or the bound passes kGMaxBytes.
+constexpr int64_t kGMaxBytes = 16ll << 30;
+int64_t g_blocks_for(const hstu_problem_t* p) {
+  if (p->dtype != HSTU_BF16 || p->d_qk < 64 || p->cp_size != 1 || p->total_kv == 0 ||
+      (p->flags & HSTU_FLAG_RECOMPUTE_BWD))
+    return 0;
+  const int64_t n = cdiv(p->max_seq_len, hstu::kGRows);
+  const int64_t blocks = p->num_heads * (n + 1) * (cdiv(p->total_kv, hstu::kGRows) + p->num_seqs);
+  return blocks > kGMaxBytes / hstu::kGBlockBytes ? 0 : blocks;
+}
 
 Layout layout_for(const hstu_problem_t* p, bool backward) {
   Layout l{};
@@ -187,6 +204,11 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
   off = align_up(off + (size_t)l.max_qtiles * sizeof(hstu::Item));
   l.kitems = off;
   off = align_up(off + (size_t)l.max_ktiles * sizeof(hstu::Item));
+  l.g_blocks = backward ? g_blocks_for(p) : 0;
+  l.gblk_off = off;
+  off = align_up(off + (l.g_blocks ? (size_t)(p->num_seqs + 1) * sizeof(int64_t) : 0));
+  l.g = off;
+  off = align_up(off + (size_t)l.g_blocks * hstu::kGBlockBytes);
   l.total = off;
   return l;
 }
@@ -198,7 +220,7 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 int validate(const hstu_problem_t* p, bool q_subset = false) {
   if (!p) return fail(HSTU_EINVAL, "problem is NULL");
   if (p->dtype != HSTU_BF16 && p->dtype != HSTU_FP32) return fail(HSTU_EINVAL, "dtype %d is not bf16 (0) or fp32 (1)", p->dtype);
-  if (p->reserved != 0) return fail(HSTU_EINVAL, "reserved field must be 0");
+  if (p->flags & ~HSTU_FLAG_RECOMPUTE_BWD) return fail(HSTU_EINVAL, "unknown flags 0x%x", (unsigned)p->flags);
   if (p->num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)p->num_seqs);
   if (p->num_heads < 1) return fail(HSTU_EINVAL, "num_heads %lld < 1", (long long)p->num_heads);
   if (p->d_qk != 32 && p->d_qk != 64 && p->d_qk != 128)
@@ -311,6 +333,8 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   sp.lut_out = reinterpret_cast<hstu::u32x2*>(ws + l.lut);
   sp.dw = dw;
   sp.dw_count = (int)(p->num_heads * p->num_buckets);
+  sp.gblk_off = backward && l.g_blocks ? reinterpret_cast<int64_t*>(ws + l.gblk_off) : nullptr;
+  sp.g_heads = (int)p->num_heads;
   sp.NB = (int)p->num_buckets;
   hstu::EdgeArg edges;
   if (!get_edges(p->num_buckets, &edges))
@@ -329,6 +353,11 @@ hstu::AttnParams attn_params(const hstu_problem_t* p, const Layout& l, char* ws)
   a.ctr = reinterpret_cast<int*>(ws + l.ctr);
   a.edges = reinterpret_cast<const uint32_t*>(ws + l.edges);
   a.lut = reinterpret_cast<const hstu::u32x2*>(ws + l.lut);
+  if (l.g_blocks) {
+    a.g = reinterpret_cast<uint16_t*>(ws + l.g);
+    a.gblk_off = reinterpret_cast<const int64_t*>(ws + l.gblk_off);
+    a.g_blocks = l.g_blocks;
+  }
   a.H = (int)p->num_heads;
   a.NB = (int)p->num_buckets;
   a.cp_size = (int)p->cp_size;

@@ -33,12 +33,26 @@ struct AttnParams {
   // targets_only the query rows are those candidates alone.  NULL: none.
   const int64_t* num_targets;
   int targets_only;
+  // Stored score gradients (backward, bf16, d >= 64, cp_size 1; NULL: the dQ
+  // pass recomputes them).  G of sequence b, head h is kept in blocks of
+  // kGKeys keys x kGRows query rows, block (query tile i, key tile t) at
+  // index gblk_off[b] + h n(n+1) + i(i+1) + t with n = ceil(L_b / kGRows)
+  // (query tile i sees key tiles 0 .. 2i+1), each block a row-major
+  // [kGKeys][kGRows] bf16 tile (key rows, query columns).  Indices >= g_blocks
+  // are never touched.
+  uint16_t* g;
+  const int64_t* gblk_off;  // [B+1]
+  int64_t g_blocks;
   int H;
   int NB;
   int cp_size;
   int cp_rank;
   float alpha;
 };
+
+constexpr int kGKeys = 64;    // key rows of a stored-G block
+constexpr int kGRows = 128;   // query rows (columns) of a stored-G block
+constexpr int kGBlockBytes = kGKeys * kGRows * 2;
 
 // which: 0 forward, 1 dK/dV/dW pass, 2 dQ pass.  max_items bounds the number
 // of (tile, head) work items (the grid never exceeds it).
@@ -66,6 +80,8 @@ struct SchedParams {
   int targets_only;
   int* qtile_off;    // [B+1] first query tile of each sequence in tile order
   int* ktile_off;    // [B+1] first key tile of each sequence
+  int64_t* gblk_off; // [B+1] first stored-G block of each sequence (NULL: none)
+  int g_heads;       // heads of the stored-G blocks
   Item* qitems;
   Item* kitems;
   int* ctr;

@@ -918,6 +918,13 @@ constexpr int kHalfThreads = 512;
 constexpr int kHalfKeys = 128;
 constexpr int kHalfDwCopies = 4;
 
+// Workgroup barrier for LDS data only: it waits for this wave's LDS accesses
+// and not for its global memory operations (a __syncthreads waits for all of
+// them, the stored score gradients among them).  A wave whose direct-to-LDS
+// loads must be visible waits for them itself first.  The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int D> struct alignas(16) HalfSmem {
   __bf16 q[2][BQ * D];  // this step's and the next step's tiles
   __bf16 d[2][BQ * D];
@@ -936,7 +943,10 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
   __shared__ HalfSmem<D> sm;
   __shared__ BiasLds bl;
   __shared__ float dwbins[kHalfDwCopies][kMaxBuckets + kPad];  // plan sums touch up to b_lo + 3
-  __shared__ u32x4 xch[8][4][64];  // per wave: P (2 operands) and G (2 operands), lane-contiguous
+  // per wave: P (2 operands) and G (2 operands), lane-contiguous; each slot
+  // padded by 8 entries so that the stored-G gathering reads (below) hit
+  // distinct LDS banks
+  __shared__ u32x4 xch[8][4][64 + 8];
   __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -996,6 +1006,14 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     const LaneTs lt = lane_ts(tsk, kvalid, base);
     const T* Qh = Q + h * D;
     const T* dOh = dO + h * D;
+    // stored G: this item's blocks start at gbase (query tile 0); the wave's
+    // key tile and first row within it
+    int64_t gbase = 0;
+    if (p.g) {
+      const int64_t nt = (p.offsets[it.b + 1] - seq0 + kGRows - 1) / kGRows;
+      gbase = p.gblk_off[it.b] + h * nt * (nt + 1);
+    }
+    const int gkt = (it.pos0 + 32 * kg) / kGKeys, gk0 = (32 * kg) % kGKeys;
 
     StepIter si;
     si.init(p, it.b, it.pos0);
@@ -1090,14 +1108,46 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         contract_half<D>(dvacc, db, to, par_p, hf ^ 1);
         contract_half<D>(dkacc, qb, to, par_g, hf ^ 1);
       }
+      if (p.g && wave < 4) {
+        // stored G, written after the products (the loading waves wait for
+        // their tile loads here): this wave's 32 keys over the step's 64 rows,
+        // its own block (rows 0-31) and its partner's (rows 32-63; zero where a
+        // block is not live), into the block of (query tile q0 / kGRows, its
+        // key tile).  Re-gathered from the exchange slots so that each lane
+        // stores one 16-byte chunk (8 rows of one key) and each key's 64 rows
+        // are one 128-byte line: chunk c of key r holds rows 8c .. 8c+7, whose
+        // halves sit with lanes (r, g = 0) and (r, g = 1) as run c % 4 of
+        // their values.  Written once and read once: streamed past the caches.
+        const int gi = q0 / kGRows;
+        const int64_t gidx = gbase + (int64_t)gi * (gi + 1) + gkt;
+        if (gidx < p.g_blocks) {
+          char* gb = reinterpret_cast<char*>(p.g) + gidx * kGBlockBytes;
+          const int c = lane >> 3, j = c & 3;
+          const bool ok = c < 4 ? live : par_live;
+          const char* x = reinterpret_cast<const char*>(&xch[c < 4 ? wave : wave ^ 4][2 + (j >> 1)][0]) + 8 * (j & 1);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int r = 8 * k + (lane & 7);  // key within the wave's 32
+            u32x2 lo = {0u, 0u}, hi = {0u, 0u};
+            if (ok) {
+              lo = *reinterpret_cast<const u32x2*>(x + 16 * r);
+              hi = *reinterpret_cast<const u32x2*>(x + 16 * (r + 32));
+            }
+            const int row = gk0 + r, col = q0 % kGRows + 8 * c;
+            __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
+                                        reinterpret_cast<u32x4*>(gb + (row * kGRows + col) * 2));
+          }
+        }
+      }
       // the next tiles have landed, and every wave is done with this step's
-      // tiles and exchange slots, once all waves are here
-      wait_loads();
+      // tiles and exchange slots, once all waves are here (the loading waves
+      // wait for their tile loads; the stored-G writes stay in flight)
+      if (loader) wait_loads();
       if (dw4[0] != 0.0f) atomicAdd(&dwl[blo], dw4[0]);
       if (dw4[1] != 0.0f) atomicAdd(&dwl[blo + 1], dw4[1]);
       if (dw4[2] != 0.0f) atomicAdd(&dwl[blo + 2], dw4[2]);
       if (dw4[3] != 0.0f) atomicAdd(&dwl[blo + 3], dw4[3]);
-      __syncthreads();
+      lds_barrier();
       si = nx;
       cur ^= 1;
     }
@@ -1258,6 +1308,122 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Backward, query-major pass from stored score gradients (bf16, d >= 64,
+// cp_size 1): dQᵀ += Kᵀ Gᵀ with G read from the blocks the dK/dV pass wrote,
+// so S, dP, the bias and the SiLU gradient are not recomputed.  Same items as
+// the forward (query tiles of 128 rows, one per kGRows block column); per key
+// tile, the K tile and the G block (row-major) are loaded into swizzled LDS
+// tiles (double-buffered) and
+// both operands are taken with transpose reads: Kᵀ (d x keys) from the K tile
+// and Gᵀ (keys x the wave's 32 rows) from the G tile, in the same key order.
+// Masked pairs and rows past a sequence's end hold zero G.
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int D> struct alignas(16) QgSmem {
+  __bf16 k[2][BN * D];
+  __bf16 g[2][kGKeys * kGRows];
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_q_g_kernel(const AttnParams p) {
+  using T = __bf16;
+  using Ptr = __attribute__((address_space(3))) s16x4*;
+  static_assert(BN == kGKeys && BM == kGRows, "one stored-G block per key tile of a query tile");
+  __shared__ QgSmem<D> sm;
+  __shared__ int item_slot;
+  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  LaneOffsets<D> lk;       // transpose reads of the K tile
+  lk.init(lane);
+  // transpose reads of the G tile: this wave's column block (its 32 rows)
+  int gtr[2];
+  {
+    using S = SwTile<__bf16, kGRows>;
+    const int m = lane & 15, qq = lane >> 4;
+    const int rb = 4 * g + (m >> 2), cb = 16 * (qq & 1) + 4 * (m & 3);
+    gtr[0] = 2 * S::off(rb, wave * 32 + cb);
+    gtr[1] = 2 * S::off(rb + 8, wave * 32 + cb);
+  }
+  const int H = p.H;
+  const int64_t ld = (int64_t)H * D;
+  const uint32_t lane_off = tile_lane_offset<T, D, kThreads>(tid, ld);
+  const uint32_t g_lane_off = tile_lane_offset<T, kGRows, kThreads>(tid, kGRows);
+  const T* K = static_cast<const T*>(p.k);
+  T* dQ = static_cast<T*>(p.dq);
+  const T* G = reinterpret_cast<const T*>(p.g);
+  const int n_work = p.ctr[kCtrQTiles] * H;
+
+  for (;;) {
+    const int w = pop_item(&item_slot, p.ctr + kCtrQNext2, tid);
+    if (w >= n_work) break;
+    const int h = w % H;
+    const Item it = p.qitems[w / H];
+    const int64_t seq0 = p.offsets[it.b];
+    const int qi = wave * 32 + r32;
+    const bool qvalid = qi < it.n;
+    const int64_t qrow = (int64_t)it.row0 + qi;
+    const int64_t nt = (p.offsets[it.b + 1] - seq0 + kGRows - 1) / kGRows;
+    const int gi = it.pos0 / kGRows;
+    const int64_t gbase = p.gblk_off[it.b] + h * nt * (nt + 1) + (int64_t)gi * (gi + 1);
+    const int kv_len = it.pos0 + it.n;
+    const int n_kt = (kv_len + BN - 1) / BN;
+    const T* Kh = K + seq0 * ld + h * D;
+    f32x16 dqacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
+    // a block outside the allocation (a length past max_seq_len) is never read
+    const auto g_ok = [&](int kt) { return gbase + kt < p.g_blocks; };
+    tile_load_async<T, D, BN, kThreads>(sm.k[0], Kh, ld, min(BN, kv_len), tid, lane_off);
+    if (g_ok(0))
+      tile_load_async<T, kGRows, kGKeys, kThreads, 2>(sm.g[0], G + gbase * (kGKeys * kGRows), kGRows, kGKeys, tid,
+                                                   g_lane_off);
+    wait_loads();
+    __syncthreads();
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < n_kt) {
+        tile_load_async<T, D, BN, kThreads>(sm.k[cur ^ 1], Kh + (int64_t)(kt + 1) * BN * ld, ld,
+                                            min(BN, kv_len - (kt + 1) * BN), tid, lane_off);
+        if (g_ok(kt + 1))
+          tile_load_async<T, kGRows, kGKeys, kThreads, 2>(sm.g[cur ^ 1], G + (gbase + kt + 1) * (kGKeys * kGRows),
+                                                       kGRows, kGKeys, tid, g_lane_off);
+      }
+      if (g_ok(kt)) {
+        const char* kb = reinterpret_cast<const char*>(sm.k[cur]);
+        const char* gb = reinterpret_cast<const char*>(sm.g[cur]);
+        // the G operands of the tile (this wave's 32 rows), then the products
+        bf16x8 bg[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int blk = n >> 1, u = n & 1;
+          const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Ptr)(gb + gtr[0] + (blk * 32 + 16 * u) * kGRows * 2));
+          const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Ptr)(gb + gtr[1] + (blk * 32 + 16 * u) * kGRows * 2));
+          const short __attribute__((ext_vector_type(8))) b = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          bg[n] = __builtin_bit_cast(bf16x8, b);
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int blk = n >> 1, u = n & 1;
+#pragma unroll
+          for (int dblk = 0; dblk < D / 32; ++dblk) {
+            const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Ptr)(kb + lk.tr[dblk][0] + (blk * 32 + 16 * u) * D * 2));
+            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Ptr)(kb + lk.tr[dblk][1] + (blk * 32 + 16 * u) * D * 2));
+            const short __attribute__((ext_vector_type(8))) a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            dqacc[dblk] = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, a), bg[n], dqacc[dblk]);
+          }
+        }
+      }
+      wait_loads();
+      __syncthreads();
+    }
+    if (qvalid) store_scaled<T, D>(dQ + qrow * ld + h * D, dqacc, p.alpha, g);
+  }
+}
+
 namespace {
 template <typename K>
 int grid_for(K kernel, int max_items, int cus, int threads = kThreads) {
@@ -1282,6 +1448,13 @@ hipError_t launch_all(const AttnParams& p, int which, int max_items, int cus, hi
       hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
     }
   } else {
+    if constexpr (sizeof(T) == 2 && D >= 64) {
+      if (p.g) {
+        auto k = bwd_q_g_kernel<D>;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
+        return hipGetLastError();
+      }
+    }
     auto k = bwd_q_kernel<T, D>;
     hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
   }

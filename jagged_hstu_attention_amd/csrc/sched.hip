@@ -227,29 +227,39 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   // Tile counts per sequence, scanned: sequence b owns query tiles
   // [qtile_off[b], qtile_off[b+1]) and key tiles [ktile_off[b], ktile_off[b+1])
   // of the flat tile order, so that the passes below run one thread per tile.
-  int64_t qcarry = 0, kcarry = 0;
+  int64_t qcarry = 0, kcarry = 0, gcarry = 0;
   for (int64_t base = 0; base < p.B; base += kSchedThreads) {
     const int64_t b = base + t;
-    int64_t nq = 0, nk = 0;
+    int64_t nq = 0, nk = 0, ng = 0;
     if (b < p.B) {
       const SegInfo s = seq_segments(p, (int)b, p.local_off[b]);
       if (p.q_tile > 0)
         for (int sg = 0; sg < s.n; ++sg) nq += (s.len[sg] + p.q_tile - 1) / p.q_tile;
-      if (p.k_tile > 0) nk = (p.offsets[b + 1] - p.offsets[b] + p.k_tile - 1) / p.k_tile;
+      const int64_t L = p.offsets[b + 1] - p.offsets[b];
+      if (p.k_tile > 0) nk = (L + p.k_tile - 1) / p.k_tile;
+      if (p.gblk_off) {  // stored-G blocks: n(n+1) per head, n = query tiles of kGRows rows
+        const int64_t n = (L + kGRows - 1) / kGRows;
+        ng = (int64_t)p.g_heads * n * (n + 1);
+      }
     }
-    int64_t qtot, ktot;
+    // key tiles and stored-G blocks share one scan: both totals stay below
+    // 2^31 (the stored-G path is only taken for at most 2^20 blocks)
+    int64_t qtot, kgtot;
     const int64_t qpre = block_scan(nq, scan, &qtot);
-    const int64_t kpre = block_scan(nk, scan, &ktot);
+    const int64_t kgpre = block_scan(nk | (ng << 32), scan, &kgtot);
     if (b < p.B) {
       p.qtile_off[b] = (int)(qcarry + qpre);
-      p.ktile_off[b] = (int)(kcarry + kpre);
+      p.ktile_off[b] = (int)(kcarry + (kgpre & 0xFFFFFFFF));
+      if (p.gblk_off) p.gblk_off[b] = gcarry + (kgpre >> 32);
     }
     qcarry += qtot;
-    kcarry += ktot;
+    kcarry += kgtot & 0xFFFFFFFF;
+    gcarry += kgtot >> 32;
   }
   if (t == 0) {
     p.qtile_off[p.B] = (int)qcarry;
     p.ktile_off[p.B] = (int)kcarry;
+    if (p.gblk_off) p.gblk_off[p.B] = gcarry;
   }
   __syncthreads();
   const int nqt = (int)qcarry, nkt = (int)kcarry;

@@ -68,8 +68,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
 // (vmcnt); wait and barrier before reading.  A full tile (nvalid == ROWS) uses
 // the offset from tile_lane_offset plus a scalar row shift per instruction; a
 // partial tile clamps each row to the last valid one.  The caller must ensure
-// ROWS * ld * sizeof(T) < 2^32.
-template <typename T, int D, int ROWS, int NT>
+// ROWS * ld * sizeof(T) < 2^32.  AUX is the loads' cache policy (0: default;
+// 2: non-temporal, for data read once).
+template <typename T, int D, int ROWS, int NT, int AUX = 0>
 __device__ __forceinline__ void tile_load_async(T* __restrict__ dst, const T* __restrict__ src, int64_t ld,
                                                 int nvalid, int tid, uint32_t lane_off) {
   using S = SwTile<T, D>;
@@ -84,7 +85,7 @@ __device__ __forceinline__ void tile_load_async(T* __restrict__ dst, const T* __
     for (int k = 0; k < kInstr / kWaves; ++k) {
       const uint32_t shift = (uint32_t)(k * (NT / S::C) * ld * (int64_t)sizeof(T));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(dst + (wave + k * kWaves) * 64 * S::kElems), 16,
-                                               lane_off, shift, 0, 0);
+                                               lane_off, shift, 0, AUX);
     }
     return;
   }
@@ -96,7 +97,7 @@ __device__ __forceinline__ void tile_load_async(T* __restrict__ dst, const T* __
     const int lin = (G << 4) | ((s & 15) ^ S::f(G));
     const int row = min(lin / S::C, nvalid - 1);
     const uint32_t off = (uint32_t)(row * ld + (lin % S::C) * S::kElems) * (uint32_t)sizeof(T);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(dst + i * 64 * S::kElems), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(dst + i * 64 * S::kElems), 16, off, 0, 0, AUX);
   }
 }
 

@@ -54,7 +54,7 @@ def test_edge_table_rejects_bad_sizes():
 
 def make_problem(**kw):
     p = hstu.Problem()
-    base = dict(dtype=0, reserved=0, num_seqs=4, num_heads=2, d_qk=64, d_v=64, num_buckets=128,
+    base = dict(dtype=0, flags=0, num_seqs=4, num_heads=2, d_qk=64, d_v=64, num_buckets=128,
                 max_seq_len=100, total_kv=300, total_q=300, cp_size=1, cp_rank=0)
     base.update(kw)
     for k, v in base.items():
@@ -71,8 +71,31 @@ def test_workspace_size_valid_and_monotone():
     assert small % 256 == 0
 
 
+@pytest.mark.parametrize("kw,stored", [
+    (dict(), True), (dict(d_qk=128, d_v=128, max_seq_len=300, num_seqs=1), True),
+    (dict(dtype=1), False), (dict(d_qk=32, d_v=32), False), (dict(cp_size=2, total_q=150), False),
+])
+def test_backward_workspace_holds_score_gradient_blocks(kw, stored):
+    # bf16, d >= 64, one CP rank: the backward workspace holds the stored score
+    # gradient, 16 KiB blocks of 64 keys x 128 query rows, bounded by
+    # H (N + 1) (ceil(T / 128) + B) with N = ceil(max_seq_len / 128), plus the
+    # per-sequence block offsets (int64 [B + 1], 256-byte aligned); the
+    # memory-efficient flag drops both.  Otherwise the flag changes nothing.
+    p = make_problem(**kw)
+    lean = make_problem(flags=hstu.HSTU_FLAG_RECOMPUTE_BWD, **kw)
+    full, small = hstu.workspace_size(p, True), hstu.workspace_size(lean, True)
+    assert hstu.workspace_size(p, False) == hstu.workspace_size(lean, False)
+    if not stored:
+        assert full == small
+        return
+    n = -(-p.max_seq_len // 128)
+    blocks = p.num_heads * (n + 1) * (-(-p.total_kv // 128) + p.num_seqs)
+    offsets = -(-(p.num_seqs + 1) * 8 // 256) * 256
+    assert full - small == blocks * 64 * 128 * 2 + offsets
+
+
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=5), 1), (dict(reserved=1), 1), (dict(num_seqs=-1), 1), (dict(num_heads=0), 1),
+    (dict(dtype=5), 1), (dict(flags=2), 1), (dict(flags=-1), 1), (dict(num_seqs=-1), 1), (dict(num_heads=0), 1),
     (dict(d_qk=48, d_v=48), 2), (dict(d_v=32), 2), (dict(num_buckets=0), 1), (dict(num_buckets=1000), 2),
     (dict(cp_size=0), 1), (dict(cp_size=2, cp_rank=2), 1), (dict(cp_rank=-1), 1),
     (dict(total_q=10), 1), (dict(max_seq_len=400), 1), (dict(max_seq_len=0), 1),
