@@ -1123,19 +1123,24 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         if (gidx < p.g_blocks) {
           char* gb = reinterpret_cast<char*>(p.g) + gidx * kGBlockBytes;
           const int c = lane >> 3, j = c & 3;
-          const bool ok = c < 4 ? live : par_live;
+          // all ones where this lane's block is live (masks rather than a
+          // select, which the compiler turns into branches)
+          const uint32_t keep = c < 4 ? (live ? ~0u : 0u) : (par_live ? ~0u : 0u);
           const char* x = reinterpret_cast<const char*>(&xch[c < 4 ? wave : wave ^ 4][2 + (j >> 1)][0]) + 8 * (j & 1);
+          // the eight reads issued together (in bounds whether or not the
+          // block is live), then the four stores
+          u32x2 lo[4], hi[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int r = 8 * k + (lane & 7);  // key within the wave's 32
-            u32x2 lo = {0u, 0u}, hi = {0u, 0u};
-            if (ok) {
-              lo = *reinterpret_cast<const u32x2*>(x + 16 * r);
-              hi = *reinterpret_cast<const u32x2*>(x + 16 * (r + 32));
-            }
-            const int row = gk0 + r, col = q0 % kGRows + 8 * c;
-            __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
-                                        reinterpret_cast<u32x4*>(gb + (row * kGRows + col) * 2));
+            lo[k] = *reinterpret_cast<const u32x2*>(x + 16 * r);
+            hi[k] = *reinterpret_cast<const u32x2*>(x + 16 * (r + 32));
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int row = gk0 + 8 * k + (lane & 7), col = q0 % kGRows + 8 * c;
+            const u32x4 v = u32x4{lo[k][0], lo[k][1], hi[k][0], hi[k][1]} & keep;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(gb + (row * kGRows + col) * 2));
           }
         }
       }
@@ -1306,9 +1311,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// Launchers
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
 // Backward, query-major pass from stored score gradients (bf16, d >= 64,
 // cp_size 1): dQᵀ += Kᵀ Gᵀ with G read from the blocks the dK/dV pass wrote,
 // so S, dP, the bias and the SiLU gradient are not recomputed.  Same items as
@@ -1424,6 +1426,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_g_kernel(const AttnParams p
   }
 }
 
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
 namespace {
 template <typename K>
 int grid_for(K kernel, int max_items, int cus, int threads = kThreads) {
