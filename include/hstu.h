@@ -201,7 +201,8 @@ typedef enum {
   HSTU_KERNEL_BWD_KV = 2,   /* backward, key-major pass: dK, dV, d(ts_weights) */
   HSTU_KERNEL_BWD_Q = 3,    /* backward, query-major pass: dQ */
   HSTU_KERNEL_REORDER = 4,  /* chunk-pair reorder */
-  HSTU_KERNEL_COUNT = 5
+  HSTU_KERNEL_REDUCE = 5,   /* sum of the parts of split query tiles (forward or dQ) */
+  HSTU_KERNEL_COUNT = 6
 } hstu_kernel_t;
 int hstu_timing_enable(int on);
 int hstu_timing_reset(void);

@@ -50,7 +50,7 @@ EXPORTS = [
     "hstu_timing_read",
 ]
 
-KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4}
+KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4, "reduce": 5}
 
 _lib = None
 

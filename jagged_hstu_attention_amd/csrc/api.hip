@@ -161,11 +161,27 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ctr, edges, lut, local_off, tile_off, qitems, kitems, gblk_off, g, total;
-  int64_t max_qtiles, max_ktiles, g_blocks;
+  size_t ctr, edges, lut, local_off, tile_off, qitems, kitems, splits, parts, gblk_off, g, total;
+  int64_t max_qtiles, max_ktiles, q_extra, g_blocks;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Key-range splitting of long query tiles (the scheduler decides it on the
+// device): only possible when the (tile, head) items, at most max_qtiles x H,
+// cannot fill 2 kQuerySlots workgroups.  The scheduler keeps the parts beyond
+// one per tile within min(3 kQuerySlots / H, max_qtiles x ceil(max_seq_len /
+// 64) / kMinPartTiles), a bound that sizes the item list (tiles plus extra
+// parts), the split list (one entry per split tile, at most one per extra
+// part) and the partial slots (a split tile has at least two parts: at most
+// twice the extra parts), each slot [H][kSplitRows][d] fp32.
+int64_t q_extra_for(const hstu_problem_t* p, int64_t max_qtiles) {
+  if (max_qtiles * p->num_heads >= 2 * hstu::kQuerySlots) return 0;
+  const int64_t tile_cost = cdiv(p->max_seq_len, hstu::attn_k_tile_keys());
+  if (tile_cost <= hstu::kMinPartTiles) return 0;  // no walk is long enough to split
+  return std::min<int64_t>(cdiv(3 * hstu::kQuerySlots, p->num_heads),
+                           cdiv(max_qtiles * tile_cost, hstu::kMinPartTiles));
+}
 
 // Stored score gradients (backward, bf16, d >= 64, cp_size 1): the dK/dV pass
 // writes G, the dQ pass reads it instead of recomputing it.  Blocks needed:
@@ -200,10 +216,15 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
   off = align_up(off + (size_t)(p->num_seqs + 1) * sizeof(int64_t));
   l.tile_off = off;
   off = align_up(off + (size_t)2 * (p->num_seqs + 1) * sizeof(int));
+  l.q_extra = q_extra_for(p, l.max_qtiles);
   l.qitems = off;
-  off = align_up(off + (size_t)l.max_qtiles * sizeof(hstu::Item));
+  off = align_up(off + (size_t)(l.max_qtiles + l.q_extra) * sizeof(hstu::Item));
   l.kitems = off;
   off = align_up(off + (size_t)l.max_ktiles * sizeof(hstu::Item));
+  l.splits = off;
+  off = align_up(off + (size_t)l.q_extra * sizeof(hstu::SplitTile));
+  l.parts = off;
+  off = align_up(off + (size_t)(2 * l.q_extra * p->num_heads) * hstu::kSplitRows * p->d_v * sizeof(float));
   l.g_blocks = backward ? g_blocks_for(p) : 0;
   l.gblk_off = off;
   off = align_up(off + (l.g_blocks ? (size_t)(p->num_seqs + 1) * sizeof(int64_t) : 0));
@@ -335,6 +356,9 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   sp.dw_count = (int)(p->num_heads * p->num_buckets);
   sp.gblk_off = backward && l.g_blocks ? reinterpret_cast<int64_t*>(ws + l.gblk_off) : nullptr;
   sp.g_heads = (int)p->num_heads;
+  sp.heads = (int)p->num_heads;
+  sp.q_extra = (int)l.q_extra;
+  sp.splits = reinterpret_cast<hstu::SplitTile*>(ws + l.splits);
   sp.NB = (int)p->num_buckets;
   hstu::EdgeArg edges;
   if (!get_edges(p->num_buckets, &edges))
@@ -353,6 +377,10 @@ hstu::AttnParams attn_params(const hstu_problem_t* p, const Layout& l, char* ws)
   a.ctr = reinterpret_cast<int*>(ws + l.ctr);
   a.edges = reinterpret_cast<const uint32_t*>(ws + l.edges);
   a.lut = reinterpret_cast<const hstu::u32x2*>(ws + l.lut);
+  if (l.q_extra) {
+    a.parts = reinterpret_cast<float*>(ws + l.parts);
+    a.splits = reinterpret_cast<const hstu::SplitTile*>(ws + l.splits);
+  }
   if (l.g_blocks) {
     a.g = reinterpret_cast<uint16_t*>(ws + l.g);
     a.gblk_off = reinterpret_cast<const int64_t*>(ws + l.gblk_off);
@@ -449,11 +477,16 @@ int fwd_impl(const hstu_problem_t* p, const void* q, const void* k, const void* 
   a.out = out;
   a.num_targets = num_targets;
   a.targets_only = targets_only;
-  const int max_items = (int)(l.max_qtiles * p->num_heads);
-  const hipError_t e = timed(HSTU_KERNEL_FWD, s, [&] {
-    return hstu::launch_attn(a, p->dtype == HSTU_BF16, (int)p->d_qk, 0, max_items, cu_count(), s);
+  const int max_items = (int)((l.max_qtiles + l.q_extra) * p->num_heads);
+  const bool bf16 = p->dtype == HSTU_BF16;
+  hipError_t e = timed(HSTU_KERNEL_FWD, s, [&] {
+    return hstu::launch_attn(a, bf16, (int)p->d_qk, 0, max_items, cu_count(), s);
   });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
+  if (l.q_extra) {
+    e = timed(HSTU_KERNEL_REDUCE, s, [&] { return hstu::launch_reduce(a, bf16, (int)p->d_v, 0, (int)l.q_extra, s); });
+    if (e != hipSuccess) return hip_fail(e, "split-sum launch");
+  }
   return HSTU_OK;
 }
 
@@ -540,9 +573,14 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
   if (p->total_q > 0) {
     e = timed(HSTU_KERNEL_BWD_Q, s, [&] {
-      return hstu::launch_attn(a, bf16, (int)p->d_qk, 2, (int)(l.max_qtiles * p->num_heads), cu_count(), s);
+      return hstu::launch_attn(a, bf16, (int)p->d_qk, 2, (int)((l.max_qtiles + l.q_extra) * p->num_heads),
+                               cu_count(), s);
     });
     if (e != hipSuccess) return hip_fail(e, "dQ launch");
+    if (l.q_extra) {
+      e = timed(HSTU_KERNEL_REDUCE, s, [&] { return hstu::launch_reduce(a, bf16, (int)p->d_qk, 2, (int)l.q_extra, s); });
+      if (e != hipSuccess) return hip_fail(e, "split-sum launch");
+    }
   }
   return HSTU_OK;
 }

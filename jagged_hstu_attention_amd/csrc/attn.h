@@ -43,12 +43,25 @@ struct AttnParams {
   uint16_t* g;
   const int64_t* gblk_off;  // [B+1]
   int64_t g_blocks;
+  // Split query tiles (see Item): the partial sums of part slot s, head h are
+  // rows 0 .. n-1 of parts + (s * H + h) * kSplitRows * d, fp32 [rows][d],
+  // unscaled accumulators.  NULL when no tile can be split.
+  float* parts;
+  const SplitTile* splits;  // [split tiles], count in ctr[kCtrSplits]
   int H;
   int NB;
   int cp_size;
   int cp_rank;
   float alpha;
 };
+
+// Key-range splitting of query tiles, for problems with too few (tile, head)
+// items to fill the chip: the balance target is kQuerySlots workgroups (256
+// compute units, two query-pass workgroups each), and no part covers fewer
+// than kMinPartTiles 64-key tiles.
+constexpr int kQuerySlots = 512;
+constexpr int kMinPartTiles = 16;
+constexpr int kSplitRows = 128;  // rows of a query tile (partial-sum slot height)
 
 constexpr int kGKeys = 64;    // key rows of a stored-G block
 constexpr int kGRows = 128;   // query rows (columns) of a stored-G block
@@ -57,6 +70,12 @@ constexpr int kGBlockBytes = kGKeys * kGRows * 2;
 // which: 0 forward, 1 dK/dV/dW pass, 2 dQ pass.  max_items bounds the number
 // of (tile, head) work items (the grid never exceeds it).
 hipError_t launch_attn(const AttnParams& p, bool bf16, int d, int which, int max_items, int cus, hipStream_t s);
+
+// Sum the partial slots of every split query tile (in part order) into the
+// output of pass `which` (0: the forward's out, 2: the dQ pass's dq), with
+// that pass's output scale.  max_splits bounds the number of split tiles (the
+// count itself is read from the counters).
+hipError_t launch_reduce(const AttnParams& p, bool bf16, int d, int which, int max_splits, hipStream_t s);
 
 int attn_q_tile_rows();   // query rows per forward / dQ item
 int attn_k_tile_keys();   // keys per tile in the forward / dQ loops
@@ -82,6 +101,10 @@ struct SchedParams {
   int* ktile_off;    // [B+1] first key tile of each sequence
   int64_t* gblk_off; // [B+1] first stored-G block of each sequence (NULL: none)
   int g_heads;       // heads of the stored-G blocks
+  int heads;         // heads of the query items (the split balance counts tile x head items)
+  int q_extra;       // > 0: long query tiles may be split, into at most q_extra parts beyond
+                     // one per tile; 0: never
+  SplitTile* splits; // [split tiles] (when q_extra > 0)
   Item* qitems;
   Item* kitems;
   int* ctr;

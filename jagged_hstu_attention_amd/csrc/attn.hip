@@ -389,7 +389,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
     ln.ts64 = tsq;
     ln.tsr = lt.rel;
     int64_t tsv = 0;
-    int kt = ht > 0 ? 0 : d0;
+    // key tile at position pos of the walk; the item covers positions
+    // [it.w0, it.w1) (the whole walk unless the tile is split)
+    const auto walk = [&](int pos) { return pos < ht ? pos : d0 + (pos - ht); };
+    int kt = walk(it.w0);
     {
       const int nv0 = min(BN, kv_len - kt * BN);
       issue_kv<T, D>(sm, 0, Kh, Vh, ld, kt * BN, nv0, tid, lane_off);
@@ -398,12 +401,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
     }
     wait_loads();
     __syncthreads();
-    for (int par = 0; kt <= last; ++par) {
-      const int cur = par & 1;
+    for (int pos = it.w0; pos < it.w1; ++pos) {
+      const int cur = (pos - it.w0) & 1;
       const int key0 = kt * BN;
       const int nvalid = min(BN, kv_len - key0);
-      const int nkt = kt + 1 < ht ? kt + 1 : max(kt + 1, d0);
-      const bool more = nkt <= last;
+      const int nkt = walk(pos + 1);
+      const bool more = pos + 1 < it.w1;
       const int nk0 = nkt * BN, nnv = more ? min(BN, kv_len - nk0) : 0;
       if (more) {
         // the timestamps first: they are staged half-way through the tile
@@ -431,7 +434,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
       __syncthreads();
       kt = nkt;
     }
-    if (qvalid) store_scaled<T, D>(O + qrow * ld + h * D, oacc, kNegLn2, g);
+    if (qvalid) {
+      if (it.slot < 0)
+        store_scaled<T, D>(O + qrow * ld + h * D, oacc, kNegLn2, g);
+      else
+        store_row_from_acc<float, D>(p.parts + ((int64_t)it.slot * H + h) * kSplitRows * D + (int64_t)qi * D, oacc, g);
+    }
   }
 }
 
@@ -1259,7 +1267,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
     for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
 
     const int kv_len = it.pos0 + it.n;
-    const int n_kt = (kv_len + BN - 1) / BN;
     const int wave_qmin = it.pos0 + wave * 32;
     const T* Kh = K + seq0 * ld + h * D;
     const T* Vh = V + seq0 * ld + h * D;
@@ -1271,16 +1278,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
     ln.ts64 = tsq;
     ln.tsr = lt.rel;
     int64_t tsv = 0;
-    issue_kv<T, D>(sm, 0, Kh, Vh, ld, 0, min(BN, kv_len), tid, lane_off);
-    if (wave == 0) tsv = p.ts[seq0 + min(lane, kv_len - 1)];
-    if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, min(BN, kv_len), lane, base);
+    // the item covers key tiles [it.w0, it.w1) of its causal prefix (all of
+    // them unless the tile is split)
+    {
+      const int k0 = it.w0 * BN, nv0 = min(BN, kv_len - k0);
+      issue_kv<T, D>(sm, 0, Kh, Vh, ld, k0, nv0, tid, lane_off);
+      if (wave == 0) tsv = p.ts[seq0 + k0 + min(lane, nv0 - 1)];
+      if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, nv0, lane, base);
+    }
     wait_loads();
     __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int cur = kt & 1;
+    for (int kt = it.w0; kt < it.w1; ++kt) {
+      const int cur = (kt - it.w0) & 1;
       const int key0 = kt * BN;
       const int nvalid = min(BN, kv_len - key0);
-      const bool more = kt + 1 < n_kt;
+      const bool more = kt + 1 < it.w1;
       if (more) {
         // the timestamps first: they are staged half-way through the tile
         // (below), where waiting for them leaves the tile loads in flight
@@ -1306,7 +1318,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
       wait_loads();
       __syncthreads();
     }
-    if (qvalid) store_scaled<T, D>(dQ + qrow * ld + h * D, dqacc, p.alpha, g);
+    if (qvalid) {
+      if (it.slot < 0)
+        store_scaled<T, D>(dQ + qrow * ld + h * D, dqacc, p.alpha, g);
+      else
+        store_row_from_acc<float, D>(p.parts + ((int64_t)it.slot * H + h) * kSplitRows * D + (int64_t)qi * D, dqacc, g);
+    }
   }
 }
 
@@ -1372,22 +1389,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_g_kernel(const AttnParams p
     const int gi = it.pos0 / kGRows;
     const int64_t gbase = p.gblk_off[it.b] + h * nt * (nt + 1) + (int64_t)gi * (gi + 1);
     const int kv_len = it.pos0 + it.n;
-    const int n_kt = (kv_len + BN - 1) / BN;
     const T* Kh = K + seq0 * ld + h * D;
     f32x16 dqacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
     // a block outside the allocation (a length past max_seq_len) is never read
     const auto g_ok = [&](int kt) { return gbase + kt < p.g_blocks; };
-    tile_load_async<T, D, BN, kThreads>(sm.k[0], Kh, ld, min(BN, kv_len), tid, lane_off);
-    if (g_ok(0))
-      tile_load_async<T, kGRows, kGKeys, kThreads, 2>(sm.g[0], G + gbase * (kGKeys * kGRows), kGRows, kGKeys, tid,
-                                                   g_lane_off);
+    // the item covers key tiles [it.w0, it.w1) of its causal prefix (all of
+    // them unless the tile is split)
+    tile_load_async<T, D, BN, kThreads>(sm.k[0], Kh + (int64_t)it.w0 * BN * ld, ld, min(BN, kv_len - it.w0 * BN), tid,
+                                        lane_off);
+    if (g_ok(it.w0))
+      tile_load_async<T, kGRows, kGKeys, kThreads, 2>(sm.g[0], G + (gbase + it.w0) * (kGKeys * kGRows), kGRows, kGKeys,
+                                                   tid, g_lane_off);
     wait_loads();
     __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < n_kt) {
+    for (int kt = it.w0; kt < it.w1; ++kt) {
+      const int cur = (kt - it.w0) & 1;
+      if (kt + 1 < it.w1) {
         tile_load_async<T, D, BN, kThreads>(sm.k[cur ^ 1], Kh + (int64_t)(kt + 1) * BN * ld, ld,
                                             min(BN, kv_len - (kt + 1) * BN), tid, lane_off);
         if (g_ok(kt + 1))
@@ -1422,7 +1441,52 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_g_kernel(const AttnParams p
       wait_loads();
       __syncthreads();
     }
-    if (qvalid) store_scaled<T, D>(dQ + qrow * ld + h * D, dqacc, p.alpha, g);
+    if (qvalid) {
+      if (it.slot < 0)
+        store_scaled<T, D>(dQ + qrow * ld + h * D, dqacc, p.alpha, g);
+      else
+        store_row_from_acc<float, D>(p.parts + ((int64_t)it.slot * H + h) * kSplitRows * D + (int64_t)qi * D, dqacc, g);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sum of the parts of split query tiles.  A tile whose key walk was split
+// over several items has fp32 partial sums in consecutive slots; one
+// workgroup per (split tile, head) adds them in part order (so the result
+// does not depend on the order the parts ran in), scales and stores the rows.
+// ---------------------------------------------------------------------------
+constexpr int kReduceThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kReduceThreads) void reduce_parts_kernel(const float* __restrict__ parts,
+                                                                      const SplitTile* __restrict__ splits,
+                                                                      const int* __restrict__ ctr,
+                                                                      T* __restrict__ out, int H, float scale) {
+  const int idx = blockIdx.x;
+  if (idx >= ctr[kCtrSplits] * H) return;
+  const int h = idx % H;
+  const SplitTile st = splits[idx / H];
+  const int64_t ld = (int64_t)H * D;
+  constexpr int kVec = D / 4;  // float4 per row
+  for (int v = threadIdx.x; v < st.n * kVec; v += kReduceThreads) {
+    const int r = v / kVec, c = (v % kVec) * 4;
+    float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < st.nparts; ++k) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          parts + ((int64_t)(st.slot0 + k) * H + h) * kSplitRows * D + (int64_t)r * D + c);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    T* dst = out + (int64_t)(st.row0 + r) * ld + h * D + c;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc.x * scale, acc.y * scale),
+                                             pack_bf16x2(acc.z * scale, acc.w * scale)};
+    } else {
+      *reinterpret_cast<float4*>(dst) = float4{acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale};
+    }
   }
 }
 
@@ -1479,6 +1543,32 @@ hipError_t launch_d(const AttnParams& p, int d, int which, int max_items, int cu
 
 hipError_t launch_attn(const AttnParams& p, bool bf16, int d, int which, int max_items, int cus, hipStream_t s) {
   return bf16 ? launch_d<__bf16>(p, d, which, max_items, cus, s) : launch_d<float>(p, d, which, max_items, cus, s);
+}
+
+namespace {
+template <typename T, int D>
+hipError_t launch_reduce_t(const AttnParams& p, int which, int max_splits, hipStream_t s) {
+  T* out = static_cast<T*>(which == 0 ? p.out : p.dq);
+  const float scale = which == 0 ? kNegLn2 : p.alpha;
+  hipLaunchKernelGGL((reduce_parts_kernel<T, D>), dim3(max_splits * p.H), dim3(kReduceThreads), 0, s, p.parts,
+                     p.splits, p.ctr, out, p.H, scale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_reduce_d(const AttnParams& p, int d, int which, int max_splits, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_reduce_t<T, 32>(p, which, max_splits, s);
+    case 64: return launch_reduce_t<T, 64>(p, which, max_splits, s);
+    case 128: return launch_reduce_t<T, 128>(p, which, max_splits, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+hipError_t launch_reduce(const AttnParams& p, bool bf16, int d, int which, int max_splits, hipStream_t s) {
+  if (max_splits <= 0 || !p.parts) return hipSuccess;
+  return bf16 ? launch_reduce_d<__bf16>(p, d, which, max_splits, s) : launch_reduce_d<float>(p, d, which, max_splits, s);
 }
 
 int attn_q_tile_rows() { return BM; }

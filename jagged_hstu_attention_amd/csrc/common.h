@@ -17,22 +17,40 @@ constexpr int kMaxBuckets = 512;
 
 // Work item: one tile of rows of one sequence.  For query tiles `row0` is the
 // row in q/out (rank-local when context-parallel), `pos0` the position inside
-// the sequence of the first row, `n` the row count.  For key tiles `row0` is
-// the global row in k/v.
+// the sequence of the first row, `n` the row count, and [w0, w1) the part of
+// the tile's walk over 64-key tiles that the item covers (the whole walk
+// unless the tile is split); a split tile's part writes fp32 partial sums to
+// slot `slot` (-1: not split, the item writes the output itself).  For key
+// tiles `row0` is the global row in k/v (w0, w1, slot unused).
 struct Item {
   int32_t b;
   int32_t row0;
   int32_t pos0;
   int32_t n;
+  int32_t w0;
+  int32_t w1;
+  int32_t slot;
+  int32_t pad;
+};
+
+// A query tile whose key walk is split over several items: its rows, and the
+// partial-sum slots slot0 .. slot0 + nparts - 1 its parts wrote (in walk
+// order).
+struct SplitTile {
+  int32_t row0;
+  int32_t n;
+  int32_t slot0;
+  int32_t nparts;
 };
 
 // Counters written by the scheduler, read by the attention kernels.
 enum Ctr : int {
-  kCtrQTiles = 0,   // number of query tiles in the list
+  kCtrQTiles = 0,   // number of query items (tiles or tile parts) in the list
   kCtrQNext = 1,    // work counter popped by the forward / dQ kernel
   kCtrKTiles = 2,   // number of key tiles
   kCtrKNext = 3,    // work counter popped by the dK/dV kernel
   kCtrQNext2 = 4,   // second query-tile counter (backward dQ pass)
+  kCtrSplits = 5,   // number of split query tiles
   kCtrCount = 64
 };
 

@@ -193,12 +193,25 @@ __device__ u32x2 lut_entry(int idx, const EdgeArg& edges, int nb) {
   return u32x2{0u, (uint32_t)(b0 - 1)};
 }
 
+// Parts of a query tile whose walk covers `cost` key tiles, at most `cap` key
+// tiles per part; part k covers walk positions [k cost / n, (k+1) cost / n).
+__device__ __forceinline__ int nparts(int cost, int cap) { return cost > cap ? (cost + cap - 1) / cap : 1; }
+__device__ __forceinline__ int part_begin(int cost, int n, int k) { return (int)((int64_t)k * cost / n); }
+
+// Query tiles cached in LDS while splitting (the split is only considered
+// below 2 kQuerySlots (tile, head) items, so at most this many tiles).
+constexpr int kSplitTileCache = 2 * kQuerySlots;
+static_assert(kSplitTileCache <= kSchedThreads, "one pass over the cached tiles");
+
 }  // namespace
 
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams p, const EdgeArg edges) {
   __shared__ int histq[kSchedHist];
   __shared__ int histk[kSchedHist];
   __shared__ int64_t scan[kSchedThreads];
+  __shared__ QTile qcache[kSplitTileCache];
+  __shared__ int qslot[kSplitTileCache];
+  __shared__ int qcost_max;
   const int t = threadIdx.x;
   const int hs = p.hist_size;
 
@@ -210,6 +223,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
     histq[i] = 0;
     histk[i] = 0;
   }
+  if (t == 0) qcost_max = 0;
 
   // Rank-local offsets.
   int64_t carry = 0;
@@ -264,9 +278,58 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   __syncthreads();
   const int nqt = (int)qcarry, nkt = (int)kcarry;
 
-  // Pass 1: cost histograms.
+  // Key-range splitting of long query tiles, considered only when the (tile,
+  // head) items cannot fill 2 kQuerySlots workgroups, and done only when the
+  // longest tile exceeds 1.5 times both the mean load of a workgroup slot and
+  // kMinPartTiles (else the longest-first schedule is balanced already):
+  // then at most cap = max(kMinPartTiles, ceil(total cost x heads /
+  // (3 kQuerySlots))) key tiles per part, about three items per workgroup.
+  // The host sized the item list and the partial slots for q_extra parts
+  // beyond one per tile (a bound the cap keeps); the cap doubles should it not.
+  const bool split = p.q_extra > 0 && nqt > 0 && (int64_t)nqt * p.heads < 2 * kQuerySlots;
+  int cap = 0x3FFFFFFF;
+  if (split) {
+    const int j = t;  // nqt <= kSplitTileCache <= kSchedThreads: one tile per thread
+    int64_t csum = 0;
+    if (j < nqt) {
+      qcache[j] = query_tile(p, j);
+      csum = qcache[j].cost;
+      atomicMax(&qcost_max, qcache[j].cost);
+    }
+    int64_t tot;
+    block_scan(csum, scan, &tot);  // its barriers also publish qcost_max
+    const int64_t mean = (tot * p.heads + kQuerySlots - 1) / kQuerySlots;
+    if (2 * (int64_t)qcost_max > 3 * max<int64_t>(mean, kMinPartTiles))
+      cap = (int)max<int64_t>(kMinPartTiles, (tot * p.heads + 3 * kQuerySlots - 1) / (3 * kQuerySlots));
+    for (;;) {
+      const int64_t e = j < nqt ? nparts(qcache[j].cost, cap) - 1 : 0;
+      int64_t etot;
+      block_scan(e, scan, &etot);
+      if (etot <= p.q_extra) break;
+      cap *= 2;
+    }
+    // partial slots (low half) and split-list index (high half) of each split tile
+    const int np = j < nqt ? nparts(qcache[j].cost, cap) : 1;
+    int64_t stot;
+    const int64_t pre = block_scan(np > 1 ? ((int64_t)1 << 32) | np : 0, scan, &stot);
+    if (j < nqt) {
+      qslot[j] = np > 1 ? (int)(pre & 0xFFFFFFFF) : -1;
+      if (np > 1) p.splits[pre >> 32] = SplitTile{(int)qcache[j].row0, qcache[j].n, (int)(pre & 0xFFFFFFFF), np};
+    }
+    if (t == 0) p.ctr[kCtrSplits] = (int)(stot >> 32);
+    __syncthreads();
+  } else if (t == 0) {
+    p.ctr[kCtrSplits] = 0;
+  }
+
+  // Pass 1: cost histograms (of the parts when splitting).
   for (int j = t; j < nqt; j += kSchedThreads) {
-    atomicAdd(&histq[clampc(query_tile(p, j).cost, hs)], 1);
+    if (split) {
+      const int c = qcache[j].cost, np = nparts(c, cap);
+      for (int k = 0; k < np; ++k) atomicAdd(&histq[clampc(part_begin(c, np, k + 1) - part_begin(c, np, k), hs)], 1);
+    } else {
+      atomicAdd(&histq[clampc(query_tile(p, j).cost, hs)], 1);
+    }
   }
   for (int j = t; j < nkt; j += kSchedThreads) atomicAdd(&histk[clampc(key_tile(p, j).cost, hs)], 1);
   __syncthreads();
@@ -291,14 +354,18 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
 
   // Pass 2: scatter.
   for (int j = t; j < nqt; j += kSchedThreads) {
-    const QTile q = query_tile(p, j);
-    const int slot = atomicAdd(&histq[clampc(q.cost, hs)], 1);
-    p.qitems[slot] = Item{q.b, (int)q.row0, q.pos0, q.n};
+    const QTile q = split ? qcache[j] : query_tile(p, j);
+    const int np = split ? nparts(q.cost, cap) : 1;
+    for (int k = 0; k < np; ++k) {
+      const int w0 = part_begin(q.cost, np, k), w1 = part_begin(q.cost, np, k + 1);
+      const int slot = atomicAdd(&histq[clampc(w1 - w0, hs)], 1);
+      p.qitems[slot] = Item{q.b, (int)q.row0, q.pos0, q.n, w0, w1, np > 1 ? qslot[j] + k : -1, 0};
+    }
   }
   for (int j = t; j < nkt; j += kSchedThreads) {
     const KTile k = key_tile(p, j);
     const int slot = atomicAdd(&histk[clampc(k.cost, hs)], 1);
-    p.kitems[slot] = Item{k.b, (int)(p.offsets[k.b] + k.k0), k.k0, k.n};
+    p.kitems[slot] = Item{k.b, (int)(p.offsets[k.b] + k.k0), k.k0, k.n, 0, 0, -1, 0};
   }
   if (t == 0) {
     p.ctr[kCtrQNext] = 0;

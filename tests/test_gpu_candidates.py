@@ -87,3 +87,21 @@ def test_microbatch_of_1024_candidates_sampled():
         alone = oracle.attn_fwd(wl.q.f64[sub], wl.k.f64[sub], wl.v.f64[sub], [0, len(sub)], wl.ts[sub], wl.w.f64,
                                 wl.num_buckets)
         assert_close(got[n], alone[-1], "bf16", f"candidate {n}")
+
+
+@pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("fp32", 64)])
+def test_candidates_long_history_split(dtype, dim):
+    # one user with a long history: few query tiles, whose key walks (the
+    # history prefix, then the tiles holding the tile's own candidates) are
+    # split over several items and summed by a second kernel
+    lengths, targets = [3300, 40], [300, 10]
+    wl = synth.custom(lengths, num_heads=2, d_qk=dim, d_v=dim, num_buckets=128, dtype=dtype, gap_mean=600.0,
+                      seed=dim + 3, w_std=0.5, with_dout=False)
+    d = upload(wl)
+    full = run(wl, d, targets)
+    ref = oracle.attn_fwd_targets(wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, targets, wl.ts, wl.w.f64, 128)
+    assert_close(to_f64(full), ref, dtype, "full")
+    rows = oracle.target_rows(wl.offsets, targets)
+    cached = run(wl, d, targets, only=True, rows=rows)
+    ref_c = oracle.attn_fwd_cached(wl.q.f64[rows], wl.k.f64, wl.v.f64, wl.offsets, targets, wl.ts, wl.w.f64, 128)
+    assert_close(to_f64(cached), ref_c, dtype, "cached")
