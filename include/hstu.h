@@ -92,7 +92,12 @@ typedef struct {
 /* Bytes of workspace needed by hstu_jagged_attn_fwd (backward = 0) or
  * hstu_jagged_attn_bwd (backward = 1).  Returns 0 if the problem is invalid
  * (hstu_last_error() then says why).  For a forward, total_q may be smaller
- * than total_kv with cp_size 1 (the candidates-only pass). */
+ * than total_kv with cp_size 1 (the candidates-only pass).  Computed from the
+ * problem's host metadata alone.  Besides the work lists it holds, for
+ * problems with fewer than 1024 (128-row query tile, head) items and
+ * max_seq_len > 1024, room for fp32 partial sums: there the library may split
+ * the key range of long query tiles over several work items to fill the GPU
+ * (the parts are summed in a fixed order, so results stay deterministic). */
 size_t hstu_workspace_size(const hstu_problem_t* p, int backward);
 
 /* Forward.  HSTUAttention equation (CP paper §2.1) on jagged inputs.
@@ -129,7 +134,9 @@ int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k,
  *            history and the candidates).
  * Requires cp_size == 1 (else HSTU_EUNSUPPORTED).  Other arguments, the
  * workspace (hstu_workspace_size(p, 0)) and the errors are as for
- * hstu_jagged_attn_fwd.  Forward only. */
+ * hstu_jagged_attn_fwd.  Forward only.  A candidate row gets the same bits
+ * from both forms unless one of them splits the key range of the row's
+ * query tile (see hstu_workspace_size); then they agree to rounding. */
 int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q,
                                  const void* k, const void* v,
                                  const int64_t* offsets,
