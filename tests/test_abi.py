@@ -152,11 +152,13 @@ def test_timing_api_without_launches():
     m.timing_reset()
     m.timing_enable(True)
     m.timing_enable(False)
-    for k in ("sched", "fwd", "bwd_kv", "bwd_q", "reorder"):
+    for k in ("sched", "fwd", "bwd_kv", "bwd_q", "reorder", "reduce"):
         assert m.timing_read(k) == (0.0, 0)
     lib = _lib.load()
     ms, n = ctypes.c_double(), ctypes.c_int64()
-    assert lib.hstu_timing_read(7, ctypes.byref(ms), ctypes.byref(n)) == 1
+    assert lib.hstu_timing_read(5, ctypes.byref(ms), ctypes.byref(n)) == 0  # the split-sum kernel
+    assert lib.hstu_timing_read(6, ctypes.byref(ms), ctypes.byref(n)) == 1  # one past the last id
+    assert lib.hstu_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == 1
 
 
 def _lut_model(edges, nb):
