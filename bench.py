@@ -212,7 +212,7 @@ def time_kernels(case, steps):
     torch.cuda.synchronize()
     m.timing_enable(False)
     out = {}
-    for k in ("sched", "fwd", "bwd_kv", "bwd_q"):
+    for k in ("sched", "fwd", "bwd_kv", "bwd_q", "reduce"):  # reduce: sums of split key walks (0 if none)
         ms, n = m.timing_read(k)
         out[k] = ms / max(n, 1)
     m.timing_reset()
@@ -419,8 +419,10 @@ def main():
         f4f, f4b = flops(p4, wl4.num_heads, wl4.d_qk, wl4.d_v)
         t4f = time_loop(c4.fwd, args.steps, 2)
         t4b = time_loop(c4.bwd, args.steps, 2)
+        k4 = time_kernels(c4, args.steps)
         extra["cp8_rank3_len16384"] = {"fwd_ms": round(t4f, 4), "bwd_ms": round(t4b, 4),
-                                       "tflops": round((f4f + f4b) / (t4f + t4b) / 1e9, 2)}
+                                       "tflops": round((f4f + f4b) / (t4f + t4b) / 1e9, 2),
+                                       "kernels_ms": {k: round(v, 4) for k, v in k4.items()}}
         del c4
         torch.cuda.empty_cache()
         log("reorder bandwidth")

@@ -1463,29 +1463,43 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_parts_kernel(const floa
                                                                       const SplitTile* __restrict__ splits,
                                                                       const int* __restrict__ ctr,
                                                                       T* __restrict__ out, int H, float scale) {
+  constexpr int kVec = D / 4;                                   // float4 per row
+  constexpr int kPer = kSplitRows * kVec / kReduceThreads;      // float4 per thread
+  static_assert(kPer * kReduceThreads == kSplitRows * kVec, "whole rows per workgroup");
   const int idx = blockIdx.x;
   if (idx >= ctr[kCtrSplits] * H) return;
   const int h = idx % H;
   const SplitTile st = splits[idx / H];
   const int64_t ld = (int64_t)H * D;
-  constexpr int kVec = D / 4;  // float4 per row
-  for (int v = threadIdx.x; v < st.n * kVec; v += kReduceThreads) {
-    const int r = v / kVec, c = (v % kVec) * 4;
-    float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = 0; k < st.nparts; ++k) {
-      const float4 x = *reinterpret_cast<const float4*>(
-          parts + ((int64_t)(st.slot0 + k) * H + h) * kSplitRows * D + (int64_t)r * D + c);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+  const int nv = st.n * kVec;  // float4 of the tile's rows (a slot is [kSplitRows][D], rows >= n unused)
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f acc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < st.nparts; ++k) {
+    // all of this part's loads in flight at once, then the adds (part order
+    // kept: the sum does not depend on which part ran when)
+    const v4f* src = reinterpret_cast<const v4f*>(parts + ((int64_t)(st.slot0 + k) * H + h) * kSplitRows * D);
+    v4f x[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = threadIdx.x + i * kReduceThreads;
+      x[i] = v < nv ? __builtin_nontemporal_load(src + v) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) acc[i] += x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int v = threadIdx.x + i * kReduceThreads;
+    if (v >= nv) continue;
+    const int r = v / kVec, c = (v % kVec) * 4;
     T* dst = out + (int64_t)(st.row0 + r) * ld + h * D + c;
+    const v4f a = acc[i];
     if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc.x * scale, acc.y * scale),
-                                             pack_bf16x2(acc.z * scale, acc.w * scale)};
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(a.x * scale, a.y * scale), pack_bf16x2(a.z * scale, a.w * scale)};
     } else {
-      *reinterpret_cast<float4*>(dst) = float4{acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale};
+      *reinterpret_cast<float4*>(dst) = float4{a.x * scale, a.y * scale, a.z * scale, a.w * scale};
     }
   }
 }
