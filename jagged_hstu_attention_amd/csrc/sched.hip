@@ -301,17 +301,16 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
     const int64_t mean = (tot * p.heads + kQuerySlots - 1) / kQuerySlots;
     if (2 * (int64_t)qcost_max > 3 * max<int64_t>(mean, kMinPartTiles))
       cap = (int)max<int64_t>(kMinPartTiles, (tot * p.heads + 3 * kQuerySlots - 1) / (3 * kQuerySlots));
+    // partial slots (low half) and split-list index (high half) of each split
+    // tile; the extra parts are the slots less the split tiles
+    int np;
+    int64_t pre, stot;
     for (;;) {
-      const int64_t e = j < nqt ? nparts(qcache[j].cost, cap) - 1 : 0;
-      int64_t etot;
-      block_scan(e, scan, &etot);
-      if (etot <= p.q_extra) break;
+      np = j < nqt ? nparts(qcache[j].cost, cap) : 1;
+      pre = block_scan(np > 1 ? ((int64_t)1 << 32) | np : 0, scan, &stot);
+      if ((stot & 0xFFFFFFFF) - (stot >> 32) <= p.q_extra) break;
       cap *= 2;
     }
-    // partial slots (low half) and split-list index (high half) of each split tile
-    const int np = j < nqt ? nparts(qcache[j].cost, cap) : 1;
-    int64_t stot;
-    const int64_t pre = block_scan(np > 1 ? ((int64_t)1 << 32) | np : 0, scan, &stot);
     if (j < nqt) {
       qslot[j] = np > 1 ? (int)(pre & 0xFFFFFFFF) : -1;
       if (np > 1) p.splits[pre >> 32] = SplitTile{(int)qcache[j].row0, qcache[j].n, (int)(pre & 0xFFFFFFFF), np};
@@ -334,21 +333,25 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   for (int j = t; j < nkt; j += kSchedThreads) atomicAdd(&histk[clampc(key_tile(p, j).cost, hs)], 1);
   __syncthreads();
 
-  // Descending exclusive scan: start[c] = number of tiles with cost > c.
-  for (int which = 0; which < 2; ++which) {
-    int* hist = which == 0 ? histq : histk;
-    int64_t carry2 = 0;
-    for (int base = 0; base < hs; base += kSchedThreads) {
-      const int c = hs - 1 - (base + t);
-      const int64_t v = c >= 0 ? hist[c] : 0;
-      int64_t tot;
-      const int64_t pre = block_scan(v, scan, &tot);
-      __syncthreads();
-      if (c >= 0) hist[c] = (int)(carry2 + pre);
-      carry2 += tot;
-      __syncthreads();
+  // Descending exclusive scans of both histograms at once (query counts in
+  // the low half, key counts in the high half; both totals stay below 2^31):
+  // start[c] = number of tiles with cost > c.  Each thread rewrites only the
+  // bin it read.
+  int64_t carry2 = 0;
+  for (int base = 0; base < hs; base += kSchedThreads) {
+    const int c = hs - 1 - (base + t);
+    const int64_t v = c >= 0 ? ((int64_t)histk[c] << 32) | (uint32_t)histq[c] : 0;
+    int64_t tot;
+    const int64_t pre = carry2 + block_scan(v, scan, &tot);
+    if (c >= 0) {
+      histq[c] = (int)(pre & 0xFFFFFFFF);
+      histk[c] = (int)(pre >> 32);
     }
-    if (t == 0) p.ctr[which == 0 ? kCtrQTiles : kCtrKTiles] = (int)carry2;
+    carry2 += tot;
+  }
+  if (t == 0) {
+    p.ctr[kCtrQTiles] = (int)(carry2 & 0xFFFFFFFF);
+    p.ctr[kCtrKTiles] = (int)(carry2 >> 32);
   }
   __syncthreads();
 
