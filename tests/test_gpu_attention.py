@@ -108,7 +108,8 @@ SPLIT_LENGTHS = [4000, 100]
 
 
 @pytest.mark.parametrize("dtype,dim,recompute", [("bf16", 128, False), ("bf16", 128, True), ("bf16", 64, False),
-                                                 ("fp32", 64, False)])
+                                                 ("bf16", 32, False), ("fp32", 128, False), ("fp32", 64, False),
+                                                 ("fp32", 32, False)])
 def test_split_key_walks(dtype, dim, recompute):
     wl = synth.custom(SPLIT_LENGTHS, num_heads=2, d_qk=dim, d_v=dim, num_buckets=128, dtype=dtype, gap_mean=600.0,
                       seed=11 + dim, w_std=0.5)
