@@ -323,8 +323,12 @@ __device__ __forceinline__ void fwd_tile(f32x16* oacc, const T* kt, const T* vt,
 
 }  // namespace
 
+// bf16 with d <= 64 fits three workgroups per compute unit (the register cap
+// of 168 costs a few spills, the third wave per SIMD hides more latency)
+template <typename T, int D> constexpr int kFwdBlocks = sizeof(T) == 2 && D <= 64 ? 3 : 2;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, (kFwdBlocks<T, D>)) void fwd_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
   __shared__ KvSmem<T, D> sm;
