@@ -57,8 +57,8 @@ struct AttnParams {
 
 // Key-range splitting of query tiles, for problems with too few (tile, head)
 // items to fill the chip: the balance target is kQuerySlots workgroups (256
-// compute units, two query-pass workgroups each), and no part covers fewer
-// than kMinPartTiles 64-key tiles.
+// compute units at two workgroups each, the occupancy of the d = 128 query
+// passes), and no part covers fewer than kMinPartTiles 64-key tiles.
 constexpr int kQuerySlots = 512;
 constexpr int kMinPartTiles = 16;
 constexpr int kSplitRows = 128;  // rows of a query tile (partial-sum slot height)
