@@ -13,9 +13,10 @@ Shapes and distributions follow the workloads described for the method:
   Recommendations with Context Parallelism on HSTU, §2.2 "Jagged Tensors");
 * timestamps are int64, strictly increasing per sequence, with exponential gaps
   and a per-sequence start near 1.7e9 s so the int64 path is exercised;
-* bucket weights are drawn from a normal distribution (same paper, §2.1: the
-  ``ts_weights`` table is "initialized with values drawn from a normal
-  distribution"); the standard deviation 0.02 is the workload's choice.
+* bucket weights are drawn from a normal distribution (same paper, §2.1,
+  timestamp-bias paragraph: the learnable ``ts_weights`` table starts from
+  normally distributed values); the standard deviation 0.02 is the workload's
+  choice.
 
 bf16 values are produced by round-to-nearest-even of float32 draws and are
 returned both as raw uint16 bit patterns (for device upload) and as exact

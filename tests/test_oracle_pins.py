@@ -573,3 +573,92 @@ def test_planted_target_mask_mistakes_are_caught(monkeypatch):
                 failures += 1
         monkeypatch.setattr(ho, "target_mask", orig)
         assert failures > 0, bad.__name__
+
+
+# --------------------------------------------------------------------------
+# Per-row forms.  attn_fwd_rows, attn_bwd_q_rows and attn_bwd_kv_rows are the
+# checkers for sampled rows of problems too large for the whole-batch oracle,
+# so each is pinned to the whole-batch form (itself pinned above) at every row
+# of a ragged batch: empty and single-token sequences, first and last rows.
+# --------------------------------------------------------------------------
+
+ROW_LENGTHS = [5, 0, 1, 9, 0, 0, 7, 1, 3, 2]
+
+
+def row_forms_agree(wl, atol=1e-12):
+    """True when every row of the per-row forms equals the batch forms."""
+    rows = list(range(wl.total))
+    args = (wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
+    o = oracle.attn_fwd(*args)
+    dq, dk, dv, _ = oracle.attn_bwd(wl.dout.f64, *args)
+    ro = oracle.attn_fwd_rows(*args, rows)
+    rq = oracle.attn_bwd_q_rows(wl.dout.f64, *args, rows)
+    rk, rv = oracle.attn_bwd_kv_rows(wl.dout.f64, *args, rows)
+    return all(np.allclose(a, b, rtol=1e-12, atol=atol) for a, b in [(ro, o), (rq, dq), (rk, dk), (rv, dv)])
+
+
+@pytest.mark.parametrize("nb,gap,seed", [(128, 3600.0, 21), (7, 3.0, 22), (256, 600.0, 23)])
+def test_row_forms_equal_batch_forms_at_every_row(nb, gap, seed):
+    wl = small(ROW_LENGTHS, nb=nb, H=2, d=4, gap=gap, seed=seed, w_std=0.5)
+    assert wl.dout is not None
+    rows = list(range(wl.total))
+    args = (wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
+    o = oracle.attn_fwd(*args)
+    dq, dk, dv, _ = oracle.attn_bwd(wl.dout.f64, *args)
+    np.testing.assert_allclose(oracle.attn_fwd_rows(*args, rows), o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.attn_bwd_q_rows(wl.dout.f64, *args, rows), dq, rtol=1e-12, atol=1e-12)
+    rk, rv = oracle.attn_bwd_kv_rows(wl.dout.f64, *args, rows)
+    np.testing.assert_allclose(rk, dk, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rv, dv, rtol=1e-12, atol=1e-12)
+    # a subset in any order gives the same rows
+    sub = [wl.total - 1, 0, 6, 7, 15]
+    np.testing.assert_allclose(oracle.attn_fwd_rows(*args, sub), o[sub], rtol=1e-12, atol=1e-12)
+
+
+def test_row_form_pins_catch_planted_mistakes(monkeypatch):
+    wl = small(ROW_LENGTHS, nb=128, H=2, d=4, gap=3600.0, seed=21, w_std=0.5)
+    assert row_forms_agree(wl)
+    orig_row_seq = ho._row_seq
+    orig_kv_rows = ho.attn_bwd_kv_rows
+
+    # a row at a sequence's first position assigned to the sequence before it
+    def row_seq_left(offsets, row):
+        b = int(np.searchsorted(np.asarray(offsets), row, side="left")) - 1
+        b = max(b, 0)
+        return b, int(offsets[b]), int(offsets[b + 1])
+
+    monkeypatch.setattr(ho, "_row_seq", row_seq_left)
+    assert not row_forms_agree(wl)
+    monkeypatch.setattr(ho, "_row_seq", orig_row_seq)
+
+    # the diagonal pair dropped from a key's query range
+    def kv_rows_no_diagonal(dout, q, k, v, offsets, ts, w, num_buckets, rows):
+        dk, dv = orig_kv_rows(dout, q, k, v, offsets, ts, w, num_buckets, rows)
+        alpha = 1.0 / math.sqrt(q.shape[2])
+        for n, j in enumerate(rows):
+            for h in range(q.shape[1]):
+                s = alpha * (q[j, h] @ k[j, h] + w[h, 0])
+                sg = 1.0 / (1.0 + math.exp(-s))
+                dp = dout[j, h] @ v[j, h]
+                dv[n, h] -= s * sg * dout[j, h]
+                dk[n, h] -= alpha * dp * sg * (1.0 + s * (1.0 - sg)) * q[j, h]
+        return dk, dv
+
+    monkeypatch.setattr(ho, "attn_bwd_kv_rows", kv_rows_no_diagonal)
+    monkeypatch.setattr(oracle, "attn_bwd_kv_rows", kv_rows_no_diagonal)
+    assert not row_forms_agree(wl)
+
+    # the causal prefix of a query row stopping one key short
+    monkeypatch.setattr(ho, "attn_bwd_kv_rows", orig_kv_rows)
+    monkeypatch.setattr(oracle, "attn_bwd_kv_rows", orig_kv_rows)
+    orig_scores = ho._seq_scores
+
+    def short_prefix_scores(qb, kb, tsq, tsk, wh, nb, alpha):
+        s, b = orig_scores(qb, kb, tsq, tsk, wh, nb, alpha)
+        if s.shape[0] == 1 and s.shape[1] > 1:  # a query row against its prefix
+            s = s.copy()
+            s[0, -1] = -700.0                   # silu(-700) ~ 0: the diagonal drops out
+        return s, b
+
+    monkeypatch.setattr(ho, "_seq_scores", short_prefix_scores)
+    assert not row_forms_agree(wl)
