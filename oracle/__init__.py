@@ -16,6 +16,7 @@ from .hstu_oracle import (  # noqa: F401
     bucketize,
     causal_pairs,
     chunk_bounds,
+    cp_attn_blocks,
     cp_attn_bwd,
     cp_attn_fwd,
     cp_local_offsets,

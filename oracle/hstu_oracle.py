@@ -320,6 +320,56 @@ def cp_attn_bwd(dout_local, q_local, k, v, offsets, ts, w, num_buckets, cp_size,
     return dq, dk, dv, dw
 
 
+def cp_attn_blocks(dout_local, q_local, k, v, offsets, ts, w, num_buckets, cp_size, rank):
+    """One rank's share, forward and backward, as one masked block per
+    (sequence, head): the rank's query rows of a sequence (chunk r then chunk
+    2C-1-r, at their global positions p) against the keys 0 .. max p of that
+    sequence, key j visible to row p iff j <= p.  The same quantities as
+    cp_attn_fwd and cp_attn_bwd (and the same readings), with the rows of a
+    sequence stacked into one matrix instead of looped over.
+
+    Returns (out_local, dq_local, dk, dv, dw); dk, dv, dw are the rank's
+    partial sums as in cp_attn_bwd.
+    """
+    q_local = np.asarray(q_local, np.float64)
+    dout_local = np.asarray(dout_local, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    w = np.asarray(w, np.float64)
+    ts = np.asarray(ts, np.int64)
+    H, dqk = q_local.shape[1], q_local.shape[2]
+    alpha = 1.0 / math.sqrt(dqk)
+    out = np.zeros((q_local.shape[0], H, v.shape[2]), dtype=np.float64)
+    dq = np.zeros_like(q_local)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dw = np.zeros((H, num_buckets), dtype=np.float64)
+    local = 0
+    for b, seq_rows in enumerate(rank_rows(offsets, cp_size, rank)):
+        n = len(seq_rows)
+        if n == 0:
+            continue
+        start = int(offsets[b])
+        grows = np.array([g for g, _ in seq_rows], dtype=np.int64)
+        pos = np.array([p for _, p in seq_rows], dtype=np.int64)
+        nk = int(pos.max()) + 1
+        keys = slice(start, start + nk)
+        mask = np.arange(nk)[None, :] <= pos[:, None]
+        rows = slice(local, local + n)
+        for h in range(H):
+            s, bucket = _seq_scores(q_local[rows, h], k[keys, h], ts[grows], ts[keys], w[h], num_buckets, alpha)
+            a = np.where(mask, silu(s), 0.0)
+            out[rows, h] = a @ v[keys, h]
+            dp = dout_local[rows, h] @ v[keys, h].T
+            g = np.where(mask, alpha * dp * silu_grad(s), 0.0)
+            dv[keys, h] += a.T @ dout_local[rows, h]
+            dq[rows, h] = g @ k[keys, h]
+            dk[keys, h] += g.T @ q_local[rows, h]
+            dw[h] += np.bincount(bucket[mask], weights=g[mask], minlength=num_buckets)
+        local += n
+    return out, dq, dk, dv, dw
+
+
 # --------------------------------------------------------------------------
 # Counting (for the measurement: causal-effective pairs)
 # --------------------------------------------------------------------------

@@ -662,3 +662,35 @@ def test_row_form_pins_catch_planted_mistakes(monkeypatch):
 
     monkeypatch.setattr(ho, "_seq_scores", short_prefix_scores)
     assert not row_forms_agree(wl)
+
+
+# --------------------------------------------------------------------------
+# Block form of a CP rank's share (the checker of the full-size share): equal
+# to the per-row CP forms and to the rows of the unsharded oracle.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lengths,cp", [([37, 16, 0, 1], 2), ([37, 16, 0, 1], 4), ([64, 23], 8), ([5, 50], 1)])
+def test_cp_block_form_equals_row_form_and_unsharded(lengths, cp):
+    wl = small(lengths, nb=128, H=2, d=4, gap=3600.0, seed=31 + cp, w_std=0.5)
+    args = (wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, 128)
+    q_re, _ = oracle.reorder(wl.q.f64, wl.offsets, cp)
+    d_re, _ = oracle.reorder(wl.dout.f64, wl.offsets, cp)
+    full_o = oracle.attn_fwd(wl.q.f64, *args)
+    full_g = oracle.attn_bwd(wl.dout.f64, wl.q.f64, *args)
+    idx, seg = oracle.reorder_index(wl.offsets, cp)
+    B = len(lengths)
+    sums = [np.zeros_like(full_g[1]), np.zeros_like(full_g[2]), np.zeros_like(full_g[3])]
+    for r in range(cp):
+        lo, hi = int(seg[r * B]), int(seg[(r + 1) * B])
+        o, dq, dk, dv, dw = oracle.cp_attn_blocks(d_re[lo:hi], q_re[lo:hi], *args, cp, r)
+        np.testing.assert_allclose(o, oracle.cp_attn_fwd(q_re[lo:hi], *args, cp, r), rtol=1e-12, atol=1e-12)
+        rq, rk, rv, rw = oracle.cp_attn_bwd(d_re[lo:hi], q_re[lo:hi], *args, cp, r)
+        for got, want in [(dq, rq), (dk, rk), (dv, rv), (dw, rw)]:
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+        # rows of the unsharded problem
+        np.testing.assert_allclose(o, full_o[idx[lo:hi]], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dq, full_g[0][idx[lo:hi]], rtol=1e-12, atol=1e-12)
+        for acc, part in zip(sums, (dk, dv, dw)):
+            acc += part
+    for acc, want in zip(sums, full_g[1:]):
+        np.testing.assert_allclose(acc, want, rtol=1e-12, atol=1e-12)
