@@ -100,22 +100,36 @@ class Case:
         self.dk = torch.empty_like(self.k)
         self.dv = torch.empty_like(self.v)
         self.dw = torch.empty(self.w.shape, dtype=torch.float32, device="cuda")
-        p = m.problem(q, self.k, self.v, self.offsets, self.w, wl.max_seq_len, cp_size=cp_size, cp_rank=cp_rank)
+        # host metadata a caller has from its host copy of the offsets
+        self.sum_sq = int(sum(int(L) * int(L) for L in wl.lengths))
+        p = m.problem(q, self.k, self.v, self.offsets, self.w, wl.max_seq_len, cp_size=cp_size, cp_rank=cp_rank,
+                      sum_sq_len=self.sum_sq)
         self.ws_f = torch.empty(m.workspace_size(p, False), dtype=torch.uint8, device="cuda")
         self.ws_b = torch.empty(m.workspace_size(p, True), dtype=torch.uint8, device="cuda")
 
-    def fwd(self):
+    def fwd(self, shared=False):
         self.m.jagged_attn_fwd(self.q, self.k, self.v, self.offsets, self.ts, self.w, self.wl.max_seq_len,
-                               cp_size=self.cp_size, cp_rank=self.cp_rank, out=self.out, workspace=self.ws_f)
+                               cp_size=self.cp_size, cp_rank=self.cp_rank, out=self.out,
+                               workspace=self.ws_b if shared else self.ws_f, shared_schedule=shared,
+                               sum_sq_len=self.sum_sq)
 
-    def bwd(self):
+    def bwd(self, shared=False, recompute=False):
         self.m.jagged_attn_bwd(self.dout, self.q, self.k, self.v, self.offsets, self.ts, self.w,
                                self.wl.max_seq_len, cp_size=self.cp_size, cp_rank=self.cp_rank, dq=self.dq,
-                               dk=self.dk, dv=self.dv, dw=self.dw, workspace=self.ws_b)
+                               dk=self.dk, dv=self.dv, dw=self.dw, workspace=self.ws_b, recompute=recompute,
+                               shared_schedule=shared, sum_sq_len=self.sum_sq)
 
     def step(self):
-        self.fwd()
-        self.bwd()
+        """One training step of the attention: forward then backward, one
+        schedule shared by both (the backward stores the score gradient)."""
+        self.fwd(shared=True)
+        self.bwd(shared=True)
+
+    def step_recompute(self):
+        """The same step with the memory-efficient backward (nothing of the
+        size of the attention matrix stored; the dQ pass recomputes G)."""
+        self.fwd(shared=True)
+        self.bwd(shared=True, recompute=True)
 
 
 def kernel_flops(pairs, heads, dqk, dv):
@@ -207,8 +221,7 @@ def time_kernels(case, steps):
     m.timing_reset()
     m.timing_enable(True)
     for _ in range(steps):
-        case.fwd()
-        case.bwd()
+        case.step()
     torch.cuda.synchronize()
     m.timing_enable(False)
     out = {}
@@ -392,7 +405,8 @@ def main():
 
     ms_fwd = time_loop(case.fwd, args.steps, 2)
     ms_bwd = time_loop(case.bwd, args.steps, 2)
-    log(f"forward {ms_fwd:.3f} ms, backward {ms_bwd:.3f} ms")
+    ms_rec = time_loop(case.step_recompute, args.steps, 2)
+    log(f"forward {ms_fwd:.3f} ms, backward {ms_bwd:.3f} ms, step with the recompute backward {ms_rec:.3f} ms")
     kms = time_kernels(case, args.steps)
     kfl = kernel_flops(pairs, wl.num_heads, wl.d_qk, wl.d_v)
     log("per kernel (ms): " + ", ".join(f"{k} {v:.4f}" for k, v in kms.items()))
@@ -404,6 +418,11 @@ def main():
                 "ms_per_launch": round(kms[dom], 4), "flop_per_launch": kfl[dom]}
 
     extra = {
+        "value_backward": "stored score gradient (the dK/dV pass writes G = dS, the dQ pass reads it); "
+                          "one schedule shared by the forward and backward",
+        "len3072_step_recompute": {"ms": round(ms_rec, 4), "tflops": round((f_fwd + f_bwd) / ms_rec / 1e9, 2),
+                                   "backward": "memory-efficient: nothing of the size of the attention matrix "
+                                               "stored, the dQ pass recomputes S, dP and G"},
         "len3072_forward": {"ms": round(ms_fwd, 4), "tflops": round(f_fwd / ms_fwd / 1e9, 2)},
         "len3072_backward": {"ms": round(ms_bwd, 4), "tflops": round(f_bwd / ms_bwd / 1e9, 2)},
         "len3072_kernels_ms": {k: round(v, 4) for k, v in kms.items()},

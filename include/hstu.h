@@ -40,7 +40,16 @@
  *   - Argument errors are detected on the host before anything is launched:
  *     the call returns a non-zero hstu_status_t and hstu_last_error() gives a
  *     message.  Device-side data contracts (offsets non-decreasing with
- *     offsets[0] = 0 and offsets[B] = total_kv, |ts| < 2^62) are the caller's.
+ *     offsets[0] = 0 and offsets[B] = total_kv, every length <= max_seq_len,
+ *     sum of squared lengths <= sum_sq_len when stated, |ts| < 2^62) are the
+ *     caller's.
+ *   - HSTU_VALIDATE: when this environment variable is set to anything but ""
+ *     or "0", every call that takes offsets first checks that contract (all
+ *     but the timestamp bound, plus the query row count implied for a CP
+ *     share or a candidates-only pass) on the device, waits for the answer
+ *     (one host synchronisation, so not for use under stream capture) and
+ *     returns HSTU_EINVAL, naming what is broken, before launching anything
+ *     else.  Off by default: the calls then never synchronise.
  */
 #ifndef HSTU_H
 #define HSTU_H
@@ -60,7 +69,15 @@ enum {
    * (Actions Speak Louder than Words): nothing of the size of the attention
    * matrix is stored; the query-major pass recomputes the score gradient
    * instead of reading it from the workspace.  Smaller workspace, slower. */
-  HSTU_FLAG_RECOMPUTE_BWD = 1
+  HSTU_FLAG_RECOMPUTE_BWD = 1,
+  /* One schedule per training step: the forward and the backward of one step
+   * share one workspace of hstu_workspace_size(p, 1) bytes (both calls pass
+   * this flag, the same problem, the same offsets and that workspace, on one
+   * stream, forward first).  The forward then builds the work lists of both
+   * passes and the backward launches no scheduler of its own.  Between the
+   * two calls the caller must not change offsets, the workspace or the
+   * problem; a backward without its forward reads stale lists. */
+  HSTU_FLAG_SHARED_SCHEDULE = 2
 };
 
 typedef enum {
@@ -74,7 +91,7 @@ typedef enum {
 /* Problem description shared by the attention calls. */
 typedef struct {
   int32_t dtype;        /* hstu_dtype_t of q, k, v, out, dout, ts_weights, dq, dk, dv */
-  int32_t flags;        /* 0 or HSTU_FLAG_RECOMPUTE_BWD; other bits must be 0 */
+  int32_t flags;        /* HSTU_FLAG_* bits (RECOMPUTE_BWD, SHARED_SCHEDULE); others 0 */
   int64_t num_seqs;     /* B >= 0 */
   int64_t num_heads;    /* H >= 1 */
   int64_t d_qk;         /* Q/K head width; supported: 32, 64, 128 */
@@ -87,6 +104,9 @@ typedef struct {
                            rank's row count sum_b (|chunk r| + |chunk 2C-1-r|) */
   int64_t cp_size;      /* C >= 1 (1 = whole sequences) */
   int64_t cp_rank;      /* r in [0, C) */
+  int64_t sum_sq_len;   /* host copy of sum_b (offsets[b+1] - offsets[b])^2, or an upper
+                           bound; 0 = not stated.  Only sizes the backward's stored
+                           score gradient more tightly than max_seq_len alone can. */
 } hstu_problem_t;
 
 /* Bytes of workspace needed by hstu_jagged_attn_fwd (backward = 0) or
@@ -159,10 +179,14 @@ int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q,
  * workspace and the query-major pass computes dQ = G K from it (unless
  * p->flags has HSTU_FLAG_RECOMPUTE_BWD);
  * hstu_workspace_size(p, 1) then includes room for H (N + 1)
- * (ceil(total_kv / 128) + B) blocks, N = ceil(max_seq_len / 128), unless
- * that passes 16 GiB, in which case dQ recomputes G instead.  Here
- * max_seq_len must bound every sequence length (blocks beyond the room are
- * dropped, not written out of bounds). */
+ * (ceil(total_kv / 128) + B) blocks, N = ceil(max_seq_len / 128), or, when
+ * p->sum_sq_len is stated and gives fewer, H ceil((sum_sq_len + 382 total_kv
+ * + 32385 B) / 16384) blocks, unless that passes 16 GiB, in which case dQ
+ * recomputes G instead.  Here max_seq_len must bound every sequence length and
+ * sum_sq_len (when stated) the sum of squared lengths (blocks beyond the room
+ * are dropped, not written out of bounds; HSTU_VALIDATE checks both).
+ * d_ts_weights is written by the last kernel of the call (its sums are kept
+ * in the workspace until then). */
 int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* q,
                          const void* k, const void* v, const int64_t* offsets,
                          const int64_t* timestamps, const void* ts_weights,

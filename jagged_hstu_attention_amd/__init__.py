@@ -20,10 +20,10 @@ import math
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import HSTU_BF16, HSTU_FLAG_RECOMPUTE_BWD, HSTU_FP32, HstuError, Problem  # noqa: F401
+from ._lib import HSTU_BF16, HSTU_FLAG_RECOMPUTE_BWD, HSTU_FLAG_SHARED_SCHEDULE, HSTU_FP32, HstuError, Problem  # noqa: F401
 
 __all__ = [
-    "Problem", "HstuError", "HSTU_FLAG_RECOMPUTE_BWD", "problem", "workspace_size", "jagged_attn_fwd",
+    "Problem", "HstuError", "HSTU_FLAG_RECOMPUTE_BWD", "HSTU_FLAG_SHARED_SCHEDULE", "problem", "workspace_size", "jagged_attn_fwd",
     "jagged_attn_fwd_targets", "jagged_attn_bwd",
     "cp_reorder", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
 ]
@@ -65,12 +65,16 @@ def _stream(device) -> int:
 
 
 def problem(q, k, v, offsets, ts_weights, max_seq_len: int, *, cp_size: int = 1, cp_rank: int = 0,
-            recompute_bwd: bool = False) -> Problem:
+            recompute_bwd: bool = False, shared_schedule: bool = False, sum_sq_len: int = 0) -> Problem:
     """Fill the hstu_problem_t for these tensors (host metadata only).
-    recompute_bwd: the memory-efficient backward (no stored score gradient)."""
+    recompute_bwd: the memory-efficient backward (no stored score gradient).
+    shared_schedule: the forward and backward of one step share one workspace
+    and one schedule (see HSTU_FLAG_SHARED_SCHEDULE).  sum_sq_len: host copy of
+    the sum of squared sequence lengths (0: not stated)."""
     p = Problem()
     p.dtype = _dtype_code(q)
-    p.flags = HSTU_FLAG_RECOMPUTE_BWD if recompute_bwd else 0
+    p.flags = (HSTU_FLAG_RECOMPUTE_BWD if recompute_bwd else 0) | (HSTU_FLAG_SHARED_SCHEDULE if shared_schedule else 0)
+    p.sum_sq_len = int(sum_sq_len)
     p.num_seqs = int(offsets.shape[0]) - 1
     p.num_heads = int(q.shape[1])
     p.d_qk = int(q.shape[2])
@@ -100,10 +104,14 @@ def _workspace(p: Problem, backward: bool, device, workspace=None):
 
 
 def jagged_attn_fwd(q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1, cp_rank: int = 0,
-                    out=None, workspace=None):
-    """Forward of jagged HSTU attention; returns out [total_q, H, d_v]."""
+                    out=None, workspace=None, shared_schedule: bool = False, sum_sq_len: int = 0):
+    """Forward of jagged HSTU attention; returns out [total_q, H, d_v].
+    shared_schedule: also build the backward's work lists in `workspace` (sized
+    for the backward) for a jagged_attn_bwd(..., shared_schedule=True) with the
+    same workspace to reuse."""
     torch = _torch()
-    p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank)
+    p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank,
+                shared_schedule=shared_schedule, sum_sq_len=sum_sq_len)
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
     ws, ws_bytes = _workspace(p, False, q.device, workspace)
@@ -134,13 +142,14 @@ def jagged_attn_fwd_targets(q, k, v, offsets, num_targets, ts, ts_weights, max_s
 
 def jagged_attn_bwd(dout, q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1,
                     cp_rank: int = 0, dq=None, dk=None, dv=None, dw=None, workspace=None,
-                    recompute: bool = False):
+                    recompute: bool = False, shared_schedule: bool = False, sum_sq_len: int = 0):
     """Backward; returns (dq, dk, dv, d_ts_weights) with d_ts_weights in fp32.
     recompute: memory-efficient form (the dQ pass recomputes the score
-    gradient instead of reading it from the workspace)."""
+    gradient instead of reading it from the workspace).  shared_schedule: reuse
+    the work lists the preceding forward built in the same workspace."""
     torch = _torch()
     p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank,
-                recompute_bwd=recompute)
+                recompute_bwd=recompute, shared_schedule=shared_schedule, sum_sq_len=sum_sq_len)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libhstu.so")
 HSTU_BF16 = 0
 HSTU_FP32 = 1
 HSTU_FLAG_RECOMPUTE_BWD = 1
+HSTU_FLAG_SHARED_SCHEDULE = 2
 
 STATUS = {0: "HSTU_OK", 1: "HSTU_EINVAL", 2: "HSTU_EUNSUPPORTED", 3: "HSTU_EWORKSPACE", 4: "HSTU_EHIP"}
 
@@ -33,6 +34,7 @@ class Problem(ctypes.Structure):
         ("total_q", ctypes.c_int64),
         ("cp_size", ctypes.c_int64),
         ("cp_rank", ctypes.c_int64),
+        ("sum_sq_len", ctypes.c_int64),
     ]
 
 

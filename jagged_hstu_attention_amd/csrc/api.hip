@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -161,7 +162,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ctr, edges, lut, local_off, tile_off, qitems, kitems, splits, parts, gblk_off, g, total;
+  size_t ctr, edges, lut, dw_acc, local_off, tile_off, qitems, kitems, splits, parts, gblk_off, g, total;
   int64_t max_qtiles, max_ktiles, q_extra, g_blocks;
 };
 
@@ -187,7 +188,8 @@ int64_t q_extra_for(const hstu_problem_t* p, int64_t max_qtiles) {
 // writes G, the dQ pass reads it instead of recomputing it.  Blocks needed:
 // sum over sequences and heads of n(n+1), n = ceil(L / kGRows).  Bound from
 // host metadata (every L <= max_seq_len): n <= N = ceil(max_seq_len / kGRows)
-// and sum n <= ceil(T / kGRows) + B, so H (N + 1) (ceil(T / kGRows) + B).
+// and sum n <= ceil(T / kGRows) + B, so H (N + 1) (ceil(T / kGRows) + B); when
+// the caller states sum_sq_len (sum of L^2), also the bound below from it.
 // 0 (recompute) when the path does not apply, the caller asks for the
 // memory-efficient backward, or the bound passes kGMaxBytes.
 constexpr int64_t kGMaxBytes = 16ll << 30;
@@ -196,11 +198,22 @@ int64_t g_blocks_for(const hstu_problem_t* p) {
       (p->flags & HSTU_FLAG_RECOMPUTE_BWD))
     return 0;
   const int64_t n = cdiv(p->max_seq_len, hstu::kGRows);
-  const int64_t blocks = p->num_heads * (n + 1) * (cdiv(p->total_kv, hstu::kGRows) + p->num_seqs);
+  int64_t per_head = (n + 1) * (cdiv(p->total_kv, hstu::kGRows) + p->num_seqs);
+  if (p->sum_sq_len > 0) {
+    // n_b (n_b + 1) <= (L_b + 127)(L_b + 255) / 128^2 for n_b = ceil(L_b / 128),
+    // summed: (sum L^2 + 382 T + 32385 B) / 16384
+    const int64_t r = hstu::kGRows;
+    const int64_t sq = std::min(p->sum_sq_len, p->max_seq_len * p->total_kv);  // sum L^2 <= max L * sum L
+    const int64_t tight = cdiv(sq + (3 * r - 2) * p->total_kv + (r - 1) * (2 * r - 1) * p->num_seqs, r * r);
+    per_head = std::min(per_head, tight);
+  }
+  const int64_t blocks = p->num_heads * per_head;
   return blocks > kGMaxBytes / hstu::kGBlockBytes ? 0 : blocks;
 }
 
 Layout layout_for(const hstu_problem_t* p, bool backward) {
+  // a forward whose schedule the backward shares builds the backward's lists too
+  backward = backward || (p->flags & HSTU_FLAG_SHARED_SCHEDULE);
   Layout l{};
   const int64_t segs = p->cp_size == 1 ? 1 : 2;
   l.max_qtiles = cdiv(p->total_q, hstu::attn_q_tile_rows()) + segs * p->num_seqs;
@@ -212,6 +225,8 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
   off = align_up(off + (hstu::kMaxBuckets + 4) * sizeof(uint32_t));
   l.lut = off;
   off = align_up(off + hstu::kLutSize * sizeof(hstu::u32x2));
+  l.dw_acc = off;
+  off = align_up(off + (size_t)p->num_heads * p->num_buckets * sizeof(float));
   l.local_off = off;
   off = align_up(off + (size_t)(p->num_seqs + 1) * sizeof(int64_t));
   l.tile_off = off;
@@ -241,7 +256,9 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 int validate(const hstu_problem_t* p, bool q_subset = false) {
   if (!p) return fail(HSTU_EINVAL, "problem is NULL");
   if (p->dtype != HSTU_BF16 && p->dtype != HSTU_FP32) return fail(HSTU_EINVAL, "dtype %d is not bf16 (0) or fp32 (1)", p->dtype);
-  if (p->flags & ~HSTU_FLAG_RECOMPUTE_BWD) return fail(HSTU_EINVAL, "unknown flags 0x%x", (unsigned)p->flags);
+  if (p->flags & ~(HSTU_FLAG_RECOMPUTE_BWD | HSTU_FLAG_SHARED_SCHEDULE))
+    return fail(HSTU_EINVAL, "unknown flags 0x%x", (unsigned)p->flags);
+  if (p->sum_sq_len < 0) return fail(HSTU_EINVAL, "sum_sq_len %lld < 0", (long long)p->sum_sq_len);
   if (p->num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)p->num_seqs);
   if (p->num_heads < 1) return fail(HSTU_EINVAL, "num_heads %lld < 1", (long long)p->num_heads);
   if (p->d_qk != 32 && p->d_qk != 64 && p->d_qk != 128)
@@ -352,7 +369,9 @@ int schedule(const hstu_problem_t* p, const Layout& l, const int64_t* offsets, c
   sp.ctr = reinterpret_cast<int*>(ws + l.ctr);
   sp.edges_out = reinterpret_cast<uint32_t*>(ws + l.edges);
   sp.lut_out = reinterpret_cast<hstu::u32x2*>(ws + l.lut);
-  sp.dw = dw;
+  // the d(ts_weights) sums start at zero (dw: an explicit target instead, for
+  // problems with nothing to attend)
+  sp.dw = dw ? dw : reinterpret_cast<float*>(ws + l.dw_acc);
   sp.dw_count = (int)(p->num_heads * p->num_buckets);
   sp.gblk_off = backward && l.g_blocks ? reinterpret_cast<int64_t*>(ws + l.gblk_off) : nullptr;
   sp.g_heads = (int)p->num_heads;
@@ -377,6 +396,7 @@ hstu::AttnParams attn_params(const hstu_problem_t* p, const Layout& l, char* ws)
   a.ctr = reinterpret_cast<int*>(ws + l.ctr);
   a.edges = reinterpret_cast<const uint32_t*>(ws + l.edges);
   a.lut = reinterpret_cast<const hstu::u32x2*>(ws + l.lut);
+  a.dw_acc = reinterpret_cast<float*>(ws + l.dw_acc);
   if (l.q_extra) {
     a.parts = reinterpret_cast<float*>(ws + l.parts);
     a.splits = reinterpret_cast<const hstu::SplitTile*>(ws + l.splits);
@@ -394,6 +414,56 @@ hstu::AttnParams attn_params(const hstu_problem_t* p, const Layout& l, char* ws)
   return a;
 }
 
+
+// Optional device check of the offsets contract: with HSTU_VALIDATE set to a
+// value other than "0" in the environment, every call first checks offsets
+// (and the host metadata stated with them) on the device and waits for the
+// result (one host synchronisation), returning HSTU_EINVAL before any other
+// launch when the contract is broken.
+bool validate_enabled() {
+  const char* v = std::getenv("HSTU_VALIDATE");
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+int check_offsets(const hstu::CheckParams& cp, hipStream_t s) {
+  if (!validate_enabled()) return HSTU_OK;
+  static std::mutex mu;  // one flag per device: checks on one device take turns
+  std::lock_guard<std::mutex> lk(mu);
+  int* flag = nullptr;
+  hipError_t e = hstu::check_flag_ptr(&flag);
+  if (e != hipSuccess) return hip_fail(e, "offsets check flag");
+  e = hstu::launch_check(cp, flag, s);
+  if (e != hipSuccess) return hip_fail(e, "offsets check launch");
+  int bits = 0;
+  e = hipMemcpyAsync(&bits, flag, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "offsets check read-back");
+  if (!bits) return HSTU_OK;
+  std::string why;
+  const struct { int bit; const char* text; } msgs[] = {
+      {hstu::kBadFirst, "offsets[0] != 0"},
+      {hstu::kBadOrder, "offsets decrease"},
+      {hstu::kBadTotal, "offsets[B] != the row count"},
+      {hstu::kBadMaxLen, "a sequence is longer than max_seq_len"},
+      {hstu::kBadSumSq, "the sum of squared lengths exceeds sum_sq_len"},
+      {hstu::kBadRows, "the query row count differs from what the offsets imply"}};
+  for (const auto& m : msgs)
+    if (bits & m.bit) why += (why.empty() ? "" : "; ") + std::string(m.text);
+  return fail(HSTU_EINVAL, "offsets check (HSTU_VALIDATE): %s", why.c_str());
+}
+
+hstu::CheckParams check_params(const hstu_problem_t* p, const int64_t* offsets) {
+  hstu::CheckParams c{};
+  c.offsets = offsets;
+  c.B = p->num_seqs;
+  c.total_kv = p->total_kv;
+  c.max_seq_len = p->max_seq_len;
+  c.sum_sq_len = p->sum_sq_len;
+  c.total_q = p->total_q;
+  c.cp_size = (int)p->cp_size;
+  c.cp_rank = (int)p->cp_rank;
+  return c;
+}
 
 }  // namespace
 
@@ -458,14 +528,21 @@ int fwd_impl(const hstu_problem_t* p, const void* q, const void* k, const void* 
   CHECK_PTR8(offsets, "offsets");
   CHECK_PTR8(timestamps, "timestamps");
   if (!ts_weights) return fail(HSTU_EINVAL, "ts_weights is NULL");
-  const Layout l = layout_for(p, false);
+  const Layout l = layout_for(p, false);  // the backward's layout with HSTU_FLAG_SHARED_SCHEDULE
   if (!workspace) return fail(HSTU_EWORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(HSTU_EINVAL, "workspace is not 16-byte aligned");
   if (workspace_bytes < l.total)
     return fail(HSTU_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  int rc = schedule(p, l, offsets, ws, nullptr, s, false, num_targets, targets_only);
+  hstu::CheckParams cp = check_params(p, offsets);
+  cp.num_targets = num_targets;
+  cp.targets_only = targets_only;
+  int rc = check_offsets(cp, s);
+  if (rc != HSTU_OK) return rc;
+  // with a shared schedule the forward also builds the backward's key lists
+  const bool shared = (p->flags & HSTU_FLAG_SHARED_SCHEDULE) != 0;
+  rc = schedule(p, l, offsets, ws, nullptr, s, shared, num_targets, targets_only);
   if (rc != HSTU_OK) return rc;
   hstu::AttnParams a = attn_params(p, l, ws);
   a.q = q;
@@ -507,6 +584,8 @@ int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q, const v
   const int rc = validate(p, q_targets_only == 1);
   if (rc != HSTU_OK) return rc;
   if (p->cp_size != 1) return fail(HSTU_EUNSUPPORTED, "candidates with cp_size %lld > 1", (long long)p->cp_size);
+  if (p->flags & HSTU_FLAG_SHARED_SCHEDULE)
+    return fail(HSTU_EUNSUPPORTED, "a shared schedule is for a forward and backward pair; candidates have no backward");
   if (q_targets_only != 0 && q_targets_only != 1) return fail(HSTU_EINVAL, "q_targets_only %d is not 0 or 1", q_targets_only);
   if (!q_targets_only && p->total_q != p->total_kv)
     return fail(HSTU_EINVAL, "total_q %lld != total_kv %lld with q_targets_only 0", (long long)p->total_q,
@@ -526,18 +605,29 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
   if (rc != HSTU_OK) return rc;
   if (p->num_seqs == 0 || p->total_kv == 0) {
     // Nothing to attend: gradients of an empty problem.  d_ts_weights still
-    // has to be written (zeros); use the scheduler with no lists.
+    // has to be written (zeros); the scheduler does it, with no lists.
     if (!d_ts_weights) return fail(HSTU_EINVAL, "d_ts_weights is NULL");
+    if (((uintptr_t)d_ts_weights & 3) != 0) return fail(HSTU_EINVAL, "d_ts_weights is not 4-byte aligned");
+    if (p->num_seqs > 0) CHECK_PTR8(offsets, "offsets");  // the scheduler reads offsets[0 .. B]
     const Layout l = layout_for(p, true);
-    if (!workspace || workspace_bytes < l.total) return fail(HSTU_EWORKSPACE, "workspace too small");
+    if (!workspace) return fail(HSTU_EWORKSPACE, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(HSTU_EINVAL, "workspace is not 16-byte aligned");
+    if (workspace_bytes < l.total)
+      return fail(HSTU_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
+    if (p->num_seqs == 0) return schedule(p, l, offsets, static_cast<char*>(workspace), d_ts_weights,
+                                          static_cast<hipStream_t>(stream), true);
+    rc = check_offsets(check_params(p, offsets), static_cast<hipStream_t>(stream));
+    if (rc != HSTU_OK) return rc;
     return schedule(p, l, offsets, static_cast<char*>(workspace), d_ts_weights, static_cast<hipStream_t>(stream),
                     true);
   }
-  CHECK_PTR(dout, "dout");
-  CHECK_PTR(q, "q");
+  if (p->total_q > 0) {
+    CHECK_PTR(dout, "dout");
+    CHECK_PTR(q, "q");
+    CHECK_PTR(dq, "dq");
+  }
   CHECK_PTR(k, "k");
   CHECK_PTR(v, "v");
-  CHECK_PTR(dq, "dq");
   CHECK_PTR(dk, "dk");
   CHECK_PTR(dv, "dv");
   CHECK_PTR8(offsets, "offsets");
@@ -552,8 +642,14 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
     return fail(HSTU_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  rc = schedule(p, l, offsets, ws, d_ts_weights, s, true);
+  rc = check_offsets(check_params(p, offsets), s);
   if (rc != HSTU_OK) return rc;
+  // with a shared schedule the forward of this step built the lists already
+  // (and reset the d(ts_weights) sums)
+  if (!(p->flags & HSTU_FLAG_SHARED_SCHEDULE)) {
+    rc = schedule(p, l, offsets, ws, nullptr, s, true);
+    if (rc != HSTU_OK) return rc;
+  }
   hstu::AttnParams a = attn_params(p, l, ws);
   a.q = q;
   a.k = k;
@@ -571,13 +667,15 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
     return hstu::launch_attn(a, bf16, (int)p->d_qk, 1, (int)(l.max_ktiles * p->num_heads), cu_count(), s);
   });
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
-  if (p->total_q > 0) {
+  {
+    // the dQ pass also publishes d(ts_weights) (it runs with no items when
+    // there are no query rows)
     e = timed(HSTU_KERNEL_BWD_Q, s, [&] {
       return hstu::launch_attn(a, bf16, (int)p->d_qk, 2, (int)((l.max_qtiles + l.q_extra) * p->num_heads),
                                cu_count(), s);
     });
     if (e != hipSuccess) return hip_fail(e, "dQ launch");
-    if (l.q_extra) {
+    if (l.q_extra && p->total_q > 0) {
       e = timed(HSTU_KERNEL_REDUCE, s, [&] { return hstu::launch_reduce(a, bf16, (int)p->d_qk, 2, (int)l.q_extra, s); });
       if (e != hipSuccess) return hip_fail(e, "split-sum launch");
     }
@@ -610,6 +708,14 @@ int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t*
   const int64_t max_pair_bytes = 2 * ((max_seq_len + nch - 1) / nch) * row_bytes;
   if (max_pair_bytes / (64 * 1024) >= 65535) return fail(HSTU_EUNSUPPORTED, "sequence too long for the reorder grid");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hstu::CheckParams cp{};
+  cp.offsets = offsets;
+  cp.B = num_seqs;
+  cp.total_kv = total_rows;
+  cp.max_seq_len = max_seq_len;
+  cp.total_q = -1;
+  const int rc = check_offsets(cp, s);
+  if (rc != HSTU_OK) return rc;
   const hipError_t e = timed(HSTU_KERNEL_REORDER, s, [&] {
     return hstu::launch_reorder(in, out, row_bytes, offsets, num_seqs, total_rows, max_seq_len, (int)cp_size,
                                 inverse != 0, out_offsets, s);

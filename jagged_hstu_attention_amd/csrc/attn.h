@@ -22,7 +22,9 @@ struct AttnParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dw;                 // [H, NB] fp32, zeroed by the scheduler
+  float* dw_acc;             // [H, NB] fp32 workspace sums, zeroed by the scheduler, added to by
+                             // the dK/dV pass
+  float* dw;                 // [H, NB] fp32 output d(ts_weights), written by the dQ pass
   const Item* qitems;
   const Item* kitems;
   int* ctr;
@@ -122,6 +124,34 @@ struct EdgeArg {
 hipError_t launch_sched(const SchedParams& p, const EdgeArg& edges, hipStream_t s);
 
 constexpr int kSchedHist = 4096;
+
+// Device-side check of the caller's offsets contract (one workgroup).  The
+// result is a bit set of CheckBits written to *flag (the flag is cleared by
+// the kernel itself first).  total_q < 0 skips the row-count check.
+enum CheckBits : int {
+  kBadFirst = 1,   // offsets[0] != 0
+  kBadOrder = 2,   // offsets decrease somewhere
+  kBadTotal = 4,   // offsets[B] != total_kv
+  kBadMaxLen = 8,  // a sequence is longer than max_seq_len
+  kBadSumSq = 16,  // sum of squared lengths exceeds the stated bound
+  kBadRows = 32    // the query rows implied by the offsets differ from total_q
+};
+struct CheckParams {
+  const int64_t* offsets;
+  int64_t B;
+  int64_t total_kv;
+  int64_t max_seq_len;
+  int64_t sum_sq_len;  // 0: not checked
+  int64_t total_q;     // < 0: not checked
+  int cp_size;
+  int cp_rank;
+  const int64_t* num_targets;  // rows counted are the clamped candidates when targets_only
+  int targets_only;
+};
+hipError_t launch_check(const CheckParams& p, int* flag, hipStream_t s);
+// Device address of the library's check flag on the current device (looked up
+// once per device).
+hipError_t check_flag_ptr(int** out);
 
 hipError_t launch_reorder(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t B,
                           int64_t total_rows, int64_t max_seq_len, int cp_size, bool inverse,

@@ -136,6 +136,15 @@ __device__ __forceinline__ int pop_item(int* slot, int* counter, int tid) {
   return __builtin_amdgcn_readfirstlane(*slot);
 }
 
+// d(ts_weights): the dK/dV pass, which ran before the dQ pass on the same
+// stream, left the finished sums in the workspace; workgroup 0 of the dQ pass
+// copies them to the output.
+template <int NT = kThreads>
+__device__ __forceinline__ void publish_dw(const AttnParams& p, int tid) {
+  if (blockIdx.x == 0 && p.dw)
+    for (int i = tid; i < p.H * p.NB; i += NT) p.dw[i] = p.dw_acc[i];
+}
+
 // Lane timestamp relative to the item base, and whether every valid lane of
 // the wave is within 2^30 of it (then the 32-bit paths apply to tiles that are
 // not wide).
@@ -715,7 +724,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
       float v = 0.0f;
 #pragma unroll
       for (int c = 0; c < kCopies; ++c) v += dwbins[c][i];
-      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, p.alpha * v);
+      if (v != 0.0f) atomicAdd(p.dw_acc + (int64_t)h * NB + i, p.alpha * v);
     }
   }
 }
@@ -1177,7 +1186,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
       float v = 0.0f;
 #pragma unroll
       for (int c = 0; c < kHalfDwCopies; ++c) v += dwbins[c][i];
-      if (v != 0.0f) atomicAdd(p.dw + (int64_t)h * NB + i, p.alpha * v);
+      if (v != 0.0f) atomicAdd(p.dw_acc + (int64_t)h * NB + i, p.alpha * v);
     }
   }
 }
@@ -1240,6 +1249,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
   const T* V = static_cast<const T*>(p.v);
   const T* dO = static_cast<const T*>(p.dout);
   T* dQ = static_cast<T*>(p.dq);
+  publish_dw(p, tid);
   load_bucket_tables(bl, p, tid);
   const int n_work = p.ctr[kCtrQTiles] * H;
 
@@ -1378,6 +1388,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_g_kernel(const AttnParams p
   const T* K = static_cast<const T*>(p.k);
   T* dQ = static_cast<T*>(p.dq);
   const T* G = reinterpret_cast<const T*>(p.g);
+  publish_dw(p, tid);
   const int n_work = p.ctr[kCtrQTiles] * H;
 
   for (;;) {

@@ -7,6 +7,8 @@
 //     pop items in order take the longest work first,
 // and resets the work counters.  Tiles lying entirely above the causal
 // diagonal are never emitted: a query tile's key range stops at its last row.
+#include <mutex>
+
 #include "attn.h"
 #include "bias.h"
 
@@ -380,6 +382,101 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
 hipError_t launch_sched(const SchedParams& p, const EdgeArg& edges, hipStream_t s) {
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, s, p, edges);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Check of the offsets contract (run only when the caller asks for it): the
+// jagged layout of §2.2 of the CP paper (values plus offsets plus max_lengths)
+// is valid when offsets start at 0, never decrease and end at the row count,
+// and no sequence is longer than the stated maximum.  One workgroup; each
+// thread folds its sequences into a bit set and two sums, which thread 0
+// combines.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kCheckThreads = 1024;
+
+__global__ __launch_bounds__(kCheckThreads) void check_kernel(const CheckParams p, int* flag) {
+  __shared__ int bits;
+  __shared__ unsigned __int128 sq[kCheckThreads];
+  __shared__ unsigned long long rows[kCheckThreads];
+  const int t = threadIdx.x;
+  if (t == 0) bits = 0;
+  __syncthreads();
+  int mine = 0;
+  unsigned __int128 sumsq = 0;
+  unsigned long long nrows = 0;
+  for (int64_t b = t; b < p.B; b += kCheckThreads) {
+    const int64_t lo = p.offsets[b], hi = p.offsets[b + 1];
+    if (hi < lo) {
+      mine |= kBadOrder;
+      continue;
+    }
+    const int64_t L = hi - lo;
+    if (L > p.max_seq_len) mine |= kBadMaxLen;
+    sumsq += (unsigned __int128)L * (unsigned __int128)L;
+    if (p.total_q >= 0) {
+      if (p.targets_only) {
+        const int64_t m = p.num_targets ? p.num_targets[b] : 0;
+        nrows += (unsigned long long)(m < 0 ? 0 : (m > L ? L : m));
+      } else if (p.cp_size > 1) {
+        const int64_t nch = 2 * (int64_t)p.cp_size;
+        const int64_t c0 = p.cp_rank, c1 = nch - 1 - p.cp_rank;
+        nrows += (unsigned long long)(((c0 + 1) * L / nch - c0 * L / nch) + ((c1 + 1) * L / nch - c1 * L / nch));
+      } else {
+        nrows += (unsigned long long)L;
+      }
+    }
+  }
+  if (t == 0) {
+    if (p.offsets[0] != 0) mine |= kBadFirst;
+    if (p.offsets[p.B] != p.total_kv) mine |= kBadTotal;
+  }
+  if (mine) atomicOr(&bits, mine);
+  sq[t] = sumsq;
+  rows[t] = nrows;
+  __syncthreads();
+  if (t == 0) {
+    unsigned __int128 s2 = 0;
+    unsigned long long r = 0;
+    for (int i = 0; i < kCheckThreads; ++i) {
+      s2 += sq[i];
+      r += rows[i];
+    }
+    int out = bits;
+    if (p.sum_sq_len > 0 && s2 > (unsigned __int128)p.sum_sq_len) out |= kBadSumSq;
+    if (p.total_q >= 0 && r != (unsigned long long)p.total_q) out |= kBadRows;
+    *flag = out;
+  }
+}
+
+// The check's result on each device: a file-scope device variable, one copy
+// per GPU, read back by the host after the check kernel.
+__device__ int g_check_flag;
+
+}  // namespace
+
+hipError_t launch_check(const CheckParams& p, int* flag, hipStream_t s) {
+  hipLaunchKernelGGL(check_kernel, dim3(1), dim3(kCheckThreads), 0, s, p, flag);
+  return hipGetLastError();
+}
+
+hipError_t check_flag_ptr(int** out) {
+  static std::mutex mu;
+  static int* cache[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_check_flag));
+    if (e != hipSuccess) return e;
+    cache[dev] = static_cast<int*>(ptr);
+  }
+  *out = cache[dev];
+  return hipSuccess;
 }
 
 }  // namespace hstu

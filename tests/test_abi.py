@@ -95,7 +95,7 @@ def test_backward_workspace_holds_score_gradient_blocks(kw, stored):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=5), 1), (dict(flags=2), 1), (dict(flags=-1), 1), (dict(num_seqs=-1), 1), (dict(num_heads=0), 1),
+    (dict(dtype=5), 1), (dict(flags=4), 1), (dict(flags=-1), 1), (dict(sum_sq_len=-1), 1), (dict(num_seqs=-1), 1), (dict(num_heads=0), 1),
     (dict(d_qk=48, d_v=48), 2), (dict(d_v=32), 2), (dict(num_buckets=0), 1), (dict(num_buckets=1000), 2),
     (dict(cp_size=0), 1), (dict(cp_size=2, cp_rank=2), 1), (dict(cp_rank=-1), 1),
     (dict(total_q=10), 1), (dict(max_seq_len=400), 1), (dict(max_seq_len=0), 1),
@@ -241,3 +241,84 @@ def test_candidates_forward_validation():
     p = make_problem(total_q=10)
     assert lib.hstu_jagged_attn_fwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
                                     1 << 30, None) == 1
+
+
+def test_shared_schedule_uses_the_backward_layout():
+    # with HSTU_FLAG_SHARED_SCHEDULE the forward builds the backward's lists,
+    # so both calls need the backward's workspace
+    for kw in (dict(), dict(dtype=1), dict(cp_size=2, total_q=150)):
+        shared = make_problem(flags=hstu.HSTU_FLAG_SHARED_SCHEDULE, **kw)
+        plain = make_problem(**kw)
+        assert hstu.workspace_size(shared, False) == hstu.workspace_size(plain, True)
+        assert hstu.workspace_size(shared, True) == hstu.workspace_size(plain, True)
+        assert hstu.workspace_size(plain, False) < hstu.workspace_size(plain, True)
+
+
+def test_candidates_reject_shared_schedule():
+    lib = _lib.load()
+    dummy = ctypes.c_void_p(16)
+    p = make_problem(flags=hstu.HSTU_FLAG_SHARED_SCHEDULE)
+    rc = lib.hstu_jagged_attn_fwd_targets(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, 0, dummy, dummy,
+                                          dummy, dummy, 1 << 30, None)
+    assert rc == 2 and b"shared schedule" in lib.hstu_last_error()
+
+
+@pytest.mark.parametrize("lengths", [[3072] * 16, [100, 3000, 17, 1, 900], [129] * 40])
+def test_stated_sum_of_squares_tightens_the_score_gradient_room(lengths):
+    # n_b (n_b + 1) <= (L_b + 127)(L_b + 255) / 128^2: the stated sum of squared
+    # lengths bounds the stored blocks; the room never falls below the exact
+    # block count, and never exceeds the max_seq_len bound
+    T, B, M = sum(lengths), len(lengths), max(lengths)
+    kw = dict(num_seqs=B, total_kv=T, total_q=T, max_seq_len=M, d_qk=128, d_v=128, num_heads=4)
+    sq = sum(L * L for L in lengths)
+    loose = hstu.workspace_size(make_problem(**kw), True)
+    tight = hstu.workspace_size(make_problem(sum_sq_len=sq, **kw), True)
+    lean = hstu.workspace_size(make_problem(flags=hstu.HSTU_FLAG_RECOMPUTE_BWD, **kw), True)
+    exact_blocks = 4 * sum((-(-L // 128)) * (-(-L // 128) + 1) for L in lengths)
+    room = (tight - lean - (-(-(B + 1) * 8 // 256) * 256)) // (64 * 128 * 2)
+    assert exact_blocks <= room
+    assert room == 4 * (-(-(min(sq, M * T) + 382 * T + 32385 * B) // 16384)) or tight == loose
+    assert tight <= loose
+
+
+def test_empty_backward_checks_offsets_and_workspace():
+    # num_seqs > 0 with no rows: the scheduler still reads offsets[0..B], so a
+    # NULL or misaligned offsets pointer, or a misaligned workspace, is an
+    # argument error found before any launch
+    lib = _lib.load()
+    p = make_problem(total_kv=0, total_q=0, max_seq_len=0)
+    ws = hstu.workspace_size(p, True)
+    good = ctypes.c_void_p(1 << 20)
+    dw = ctypes.c_void_p(1 << 21)
+
+    def call(offsets, workspace=good):
+        return lib.hstu_jagged_attn_bwd(ctypes.byref(p), good, good, good, good, offsets, good, good, good, good,
+                                        good, dw, workspace, ws, None)
+
+    assert call(None) == 1 and b"offsets is NULL" in lib.hstu_last_error()
+    assert call(ctypes.c_void_p((1 << 20) + 4)) == 1 and b"offsets" in lib.hstu_last_error()
+    assert call(good, ctypes.c_void_p((1 << 20) + 8)) == 1 and b"workspace" in lib.hstu_last_error()
+
+
+def test_validate_env_runs_the_offsets_check_first(monkeypatch):
+    # HSTU_VALIDATE=1: the device check of the offsets is the first launch of a
+    # call (here, with no GPU, it is the launch that fails); unset or "0": the
+    # call goes straight to the scheduler
+    lib = _lib.load()
+    p = make_problem()
+    ws = hstu.workspace_size(p, False)
+    g = ctypes.c_void_p(1 << 20)
+
+    def call():
+        return lib.hstu_jagged_attn_fwd(ctypes.byref(p), g, g, g, g, g, g, g, g, ws, None)
+
+    monkeypatch.setenv("HSTU_VALIDATE", "1")
+    assert call() == 4 and b"offsets check" in lib.hstu_last_error()
+    o = ctypes.c_void_p(1 << 21)
+    assert lib.hstu_cp_reorder(g, o, 8, g, 2, 10, 5, 2, 0, None, None) == 4
+    assert b"offsets check" in lib.hstu_last_error()
+    for off in ("0", ""):
+        monkeypatch.setenv("HSTU_VALIDATE", off)
+        assert call() == 4 and b"offsets check" not in lib.hstu_last_error()
+    monkeypatch.delenv("HSTU_VALIDATE")
+    assert call() == 4 and b"offsets check" not in lib.hstu_last_error()

@@ -307,27 +307,51 @@ def test_bf16_forward_u256_1024(seed):
     assert_close(out, oracle_fwd(wl), "bf16", "out")
 
 
-def test_len3072_forward_backward_sampled():
-    wl = synth.config("bf16_len3072")
+_LEN3072_REF = {}
+
+
+def len3072_reference(seed):
+    """Whole-batch oracle of the 3072-length workload (every element), kept
+    for the tests of this module that share the seed."""
+    if seed not in _LEN3072_REF:
+        wl = synth.config("bf16_len3072", seed=seed)
+        args = (wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
+        _LEN3072_REF[seed] = (wl, oracle.attn_fwd(*args), oracle.attn_bwd(wl.dout.f64, *args))
+    return _LEN3072_REF[seed]
+
+
+@pytest.mark.parametrize("seed", [1003, 1103])
+def test_len3072_forward_backward_full(seed):
+    # every element of O, dQ, dK, dV and every head of d(ts_weights), in the
+    # launch configuration bench.py times (one schedule shared by the step)
+    wl, ro, (rq, rk, rv, rw) = len3072_reference(seed)
     d = upload(wl)
-    out = to_f64(run_fwd(wl, d))
-    dq, dk, dv, dw = [to_f64(x) for x in run_bwd(wl, d)]
-    rows = sample_rows(wl.offsets, 48, seed=1)
-    args = (wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
-    assert_close(out[rows], oracle.attn_fwd_rows(*args, rows), "bf16", "out")
-    assert_close(dq[rows], oracle.attn_bwd_q_rows(wl.dout.f64, *args, rows), "bf16", "dq")
-    rk, rv = oracle.attn_bwd_kv_rows(wl.dout.f64, *args, rows)
-    assert_close(dk[rows], rk, "bf16", "dk")
-    assert_close(dv[rows], rv, "bf16", "dv")
-    # d(ts_weights) of head 0 over the whole batch, from the oracle on head 0 only
-    sub = lambda x: x[:, :1]
-    _, _, _, rw = oracle.attn_bwd(sub(wl.dout.f64), sub(wl.q.f64), sub(wl.k.f64), sub(wl.v.f64), wl.offsets,
-                                  wl.ts, wl.w.f64[:1], wl.num_buckets)
-    assert_close(dw[:1], rw, "bf16", "dw[head 0]")
+    m = hstu()
+    sq = int(sum(int(L) ** 2 for L in wl.lengths))
+    args = (d["q"], d["k"], d["v"], d["offsets"], d["ts"], d["w"], wl.max_seq_len)
+    import torch
+    p = m.problem(d["q"], d["k"], d["v"], d["offsets"], d["w"], wl.max_seq_len, shared_schedule=True, sum_sq_len=sq)
+    ws = torch.empty(m.workspace_size(p, True), dtype=torch.uint8, device="cuda")
+    out = m.jagged_attn_fwd(*args, workspace=ws, shared_schedule=True, sum_sq_len=sq)
+    dq, dk, dv, dw = m.jagged_attn_bwd(d["dout"], *args, workspace=ws, shared_schedule=True, sum_sq_len=sq)
+    assert_close(to_f64(out), ro, "bf16", "out")
+    for name, got, r in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(to_f64(got), r, "bf16", name)
 
 
-def test_skewed_powerlaw_sampled():
-    wl = synth.config("skewed_powerlaw")
+def test_len3072_backward_recompute_full():
+    # the memory-efficient backward at full size, every element
+    wl, _, (rq, rk, rv, rw) = len3072_reference(1003)
+    d = upload(wl)
+    got = hstu().jagged_attn_bwd(d["dout"], d["q"], d["k"], d["v"], d["offsets"], d["ts"], d["w"], wl.max_seq_len,
+                                 recompute=True)
+    for name, g, r in zip(("dq", "dk", "dv", "dw"), got, (rq, rk, rv, rw)):
+        assert_close(to_f64(g), r, "bf16", name)
+
+
+@pytest.mark.parametrize("seed", [1005, 1105])
+def test_skewed_powerlaw_sampled(seed):
+    wl = synth.config("skewed_powerlaw", seed=seed)
     d = upload(wl)
     out = to_f64(run_fwd(wl, d))
     dq, dk, dv, dw = [to_f64(x) for x in run_bwd(wl, d)]
@@ -343,9 +367,10 @@ def test_skewed_powerlaw_sampled():
     assert_close(dv[rows], rv, "bf16", "dv")
 
 
-def test_skewed_powerlaw_subset_full():
+@pytest.mark.parametrize("seed", [1005, 1105])
+def test_skewed_powerlaw_subset_full(seed):
     # the first 24 sequences of the skewed batch, every output and dW
-    wl = synth.config("skewed_powerlaw", num_seqs=24)
+    wl = synth.config("skewed_powerlaw", seed=seed, num_seqs=24)
     d = upload(wl)
     assert_close(to_f64(run_fwd(wl, d)), oracle_fwd(wl), "bf16", "out")
     dq, dk, dv, dw = run_bwd(wl, d)

@@ -127,8 +127,12 @@ def test_cp_share_matches_oracle_and_unsharded(dtype, lengths, cps):
         assert_close(sdw.cpu().numpy(), to_f64(fdw), dtype, f"cp{cp} summed dw vs unsharded")
 
 
-def test_cp8_rank3_len16384_sampled():
-    wl = synth.config("cp8_rank3_len16384")
+@pytest.mark.parametrize("seed", [1004, 1104])
+def test_cp8_rank3_len16384_full(seed):
+    # every element of the rank's O and dQ and of its partial dK, dV and
+    # d(ts_weights) over all keys and heads, against the oracle's block form of
+    # the share
+    wl = synth.config("cp8_rank3_len16384", seed=seed)
     d = upload(wl)
     m = hstu()
     cp, r = synth.CP_SIZE, synth.CP_RANK
@@ -139,33 +143,13 @@ def test_cp8_rank3_len16384_sampled():
     dq, dk, dv, dw = [to_f64(x) for x in m.jagged_attn_bwd(dol, ql, d["k"], d["v"], d["offsets"], d["ts"], d["w"],
                                                            wl.max_seq_len, cp_size=cp, cp_rank=r)]
     idx, _ = oracle.reorder_index(wl.offsets, cp)
-    glob = idx[lo:hi]  # global row of each local row
-    rng = np.random.default_rng(5)
-    local = sorted(set(rng.integers(0, hi - lo, size=24).tolist() + [0, 1023, 1024, 2047, 2048, 8191]))
-    rows = [int(glob[i]) for i in local]
-    args = (wl.q.f64, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64, wl.num_buckets)
-    assert_close(o[local], oracle.attn_fwd_rows(*args, rows), "bf16", "out")
-    assert_close(dq[local], oracle.attn_bwd_q_rows(wl.dout.f64, *args, rows), "bf16", "dq")
+    q_loc, d_loc = wl.q.f64[idx[lo:hi]], wl.dout.f64[idx[lo:hi]]
+    ro, rq, rk, rv, rw = oracle.cp_attn_blocks(d_loc, q_loc, wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64,
+                                               wl.num_buckets, cp, r)
+    assert_close(o, ro, "bf16", "out")
+    for name, got, ref in [("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv), ("dw", dw, rw)]:
+        assert_close(got, ref, "bf16", name)
     # keys past the rank's last chunk (chunk 12 ends at 13*1024) get no gradient
     for b in range(4):
         tail = slice(int(wl.offsets[b]) + 13 * 1024, int(wl.offsets[b + 1]))
         assert np.all(dk[tail] == 0) and np.all(dv[tail] == 0)
-    # sampled keys: this rank's partial sums, from the oracle's CP backward on
-    # one sequence with the rank's rows
-    b = 1
-    sl = slice(int(wl.offsets[b]), int(wl.offsets[b + 1]))
-    sub_off = np.array([0, 16384])
-    q_sub, _ = oracle.reorder(wl.q.f64[sl], sub_off, cp)
-    d_sub, _ = oracle.reorder(wl.dout.f64[sl], sub_off, cp)
-    seg = oracle.cp_local_offsets(sub_off, cp, r)
-    n_before = sum(int(x) for x in oracle.cp_local_offsets(sub_off, cp, 0)[-1:])  # rank 0 rows
-    lo_r = sum(oracle.cp_local_offsets(sub_off, cp, rr)[-1] for rr in range(r))
-    qr = q_sub[lo_r:lo_r + seg[-1]]
-    dr = d_sub[lo_r:lo_r + seg[-1]]
-    del n_before
-    # only a handful of heads/keys to keep the oracle fast: head 0, keys sampled
-    _, rk, rv, _ = oracle.cp_attn_bwd(dr[:, :1], qr[:, :1], wl.k.f64[sl][:, :1], wl.v.f64[sl][:, :1], sub_off,
-                                      wl.ts[sl], wl.w.f64[:1], wl.num_buckets, cp, r)
-    keys = [0, 1, 1023, 3000, 3071, 3072, 5000, 12287, 12288, 13311]
-    assert_close(dk[sl][keys, :1], rk[keys], "bf16", "dk sampled")
-    assert_close(dv[sl][keys, :1], rv[keys], "bf16", "dv sampled")
