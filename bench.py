@@ -107,11 +107,11 @@ class Case:
         self.ws_f = torch.empty(m.workspace_size(p, False), dtype=torch.uint8, device="cuda")
         self.ws_b = torch.empty(m.workspace_size(p, True), dtype=torch.uint8, device="cuda")
 
-    def fwd(self, shared=False):
+    def fwd(self, shared=False, recompute=False):
         self.m.jagged_attn_fwd(self.q, self.k, self.v, self.offsets, self.ts, self.w, self.wl.max_seq_len,
                                cp_size=self.cp_size, cp_rank=self.cp_rank, out=self.out,
                                workspace=self.ws_b if shared else self.ws_f, shared_schedule=shared,
-                               sum_sq_len=self.sum_sq)
+                               sum_sq_len=self.sum_sq, recompute_bwd=recompute)
 
     def bwd(self, shared=False, recompute=False):
         self.m.jagged_attn_bwd(self.dout, self.q, self.k, self.v, self.offsets, self.ts, self.w,
@@ -128,7 +128,7 @@ class Case:
     def step_recompute(self):
         """The same step with the memory-efficient backward (nothing of the
         size of the attention matrix stored; the dQ pass recomputes G)."""
-        self.fwd(shared=True)
+        self.fwd(shared=True, recompute=True)
         self.bwd(shared=True, recompute=True)
 
 

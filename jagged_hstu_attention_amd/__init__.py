@@ -104,14 +104,16 @@ def _workspace(p: Problem, backward: bool, device, workspace=None):
 
 
 def jagged_attn_fwd(q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1, cp_rank: int = 0,
-                    out=None, workspace=None, shared_schedule: bool = False, sum_sq_len: int = 0):
+                    out=None, workspace=None, shared_schedule: bool = False, sum_sq_len: int = 0,
+                    recompute_bwd: bool = False):
     """Forward of jagged HSTU attention; returns out [total_q, H, d_v].
     shared_schedule: also build the backward's work lists in `workspace` (sized
     for the backward) for a jagged_attn_bwd(..., shared_schedule=True) with the
-    same workspace to reuse."""
+    same workspace to reuse; the two calls describe the same problem, so
+    recompute_bwd states which backward follows."""
     torch = _torch()
     p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank,
-                shared_schedule=shared_schedule, sum_sq_len=sum_sq_len)
+                shared_schedule=shared_schedule, sum_sq_len=sum_sq_len, recompute_bwd=recompute_bwd)
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
     ws, ws_bytes = _workspace(p, False, q.device, workspace)

@@ -107,7 +107,7 @@ def test_shared_schedule_equals_separate_schedules(dtype, dim, recompute):
                   recompute_bwd=recompute)
     ws = torch.empty(m.workspace_size(p, True), dtype=torch.uint8, device="cuda")
     for _ in range(3):
-        o = m.jagged_attn_fwd(*args, workspace=ws, shared_schedule=True)
+        o = m.jagged_attn_fwd(*args, workspace=ws, shared_schedule=True, recompute_bwd=recompute)
         g = m.jagged_attn_bwd(d["dout"], *args, workspace=ws, shared_schedule=True, recompute=recompute)
         assert torch.equal(o, o_ref)
         for name, a, b in zip(("dq", "dk", "dv"), g, g_ref):
