@@ -26,6 +26,10 @@ from .hstu_oracle import (  # noqa: F401
     reorder,
     reorder_index,
     silu,
+    sl_keeps_whole,
+    sl_select,
+    sl_target_length,
+    gather_rows,
     silu_grad,
     target_mask,
     target_rows,

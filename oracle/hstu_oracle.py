@@ -39,6 +39,17 @@ What is computed, with the readings taken where the pages are open
    timestamps, and attend to their causal key prefix of the full sequence.
 5. Reorder, [CP] §2.3 (memory-reordering data shuffle): the rank-major
    permutation of rows; rank, then sequence, then chunk r then chunk 2C-1-r.
+7. Stochastic Length, [HSTU] §3.2 and §4.2 (sequence sparsity by subsequence
+   selection; at alpha = 1.6 a length-4096 history becomes length 776 most of
+   the time) and App. E (the subsequence is chosen by recency, at random, or
+   by feature weights).  Readings: a sequence of length n is cut to
+   L = floor(n^(alpha/2)) rows (4096^0.8 = 776.05), except that with
+   probability n^(alpha-2) it is kept whole (so the printed case is cut with
+   probability 1 - 4096^-0.4 = 0.964, "most of the time"); the draw is an
+   input u_b in [0, 1), kept whole iff u_b < n^(alpha-2).  The kept rows are
+   the last L (recency) or the L with the smallest random keys, ties broken by
+   position (random, the keys are inputs), in their original order.
+   Feature-weighted selection needs features the pages do not define.
 
 All floating-point arithmetic is float64; timestamps stay exact integers.
 Every function takes the exact values the device sees (bf16 inputs widened
@@ -48,6 +59,8 @@ exactly to float64).
 from __future__ import annotations
 
 import math
+from decimal import Decimal, localcontext
+from fractions import Fraction
 from typing import List, Sequence, Tuple
 
 import numpy as np
@@ -368,6 +381,69 @@ def cp_attn_blocks(dout_local, q_local, k, v, offsets, ts, w, num_buckets, cp_si
             dw[h] += np.bincount(bucket[mask], weights=g[mask], minlength=num_buckets)
         local += n
     return out, dq, dk, dv, dw
+
+
+# --------------------------------------------------------------------------
+# 7. Stochastic Length ([HSTU] §3.2, §4.2, App. E)
+# --------------------------------------------------------------------------
+
+def _pow_exact(n: int, exponent: Fraction) -> Decimal:
+    """n ** exponent to 60 significant digits (the exponent is an exact
+    rational: the float the caller passed, halved or shifted exactly)."""
+    with localcontext() as ctx:
+        ctx.prec = 60
+        return Decimal(n) ** (Decimal(exponent.numerator) / Decimal(exponent.denominator))
+
+
+def sl_target_length(n: int, alpha: float) -> int:
+    """L = floor(n^(alpha/2)), at most n."""
+    if n <= 0:
+        return 0
+    return min(int(math.floor(_pow_exact(n, Fraction(alpha) / 2))), n)
+
+
+def sl_keeps_whole(n: int, alpha: float, u: float) -> bool:
+    """The sequence is kept whole iff u < n^(alpha-2) (so with probability
+    n^(alpha-2) for u ~ U[0, 1)), or when the cut would not shorten it."""
+    if n <= 1 or sl_target_length(n, alpha) >= n:
+        return True
+    with localcontext() as ctx:
+        ctx.prec = 60
+        return Decimal(float(u)) < _pow_exact(n, Fraction(alpha) - 2)
+
+
+def sl_select(offsets, alpha: float, seq_uniform, token_keys=None):
+    """Rows kept by Stochastic Length, sequence by sequence.
+
+    offsets int64 [B+1]; seq_uniform [B] (the keep-whole draws); token_keys
+    [T] uint32 (random selection) or None (recency: the last L rows).
+    Returns (out_offsets [B+1], index [T_out]): output row i is input row
+    index[i]."""
+    out_off = [0]
+    idx = []
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        n = hi - lo
+        if n <= 0:
+            out_off.append(len(idx))
+            continue
+        if sl_keeps_whole(n, alpha, float(seq_uniform[b])):
+            kept = list(range(lo, hi))
+        else:
+            L = sl_target_length(n, alpha)
+            if token_keys is None:
+                kept = list(range(hi - L, hi))
+            else:
+                order = sorted(range(lo, hi), key=lambda r: (int(token_keys[r]), r))
+                kept = sorted(order[:L])
+        idx.extend(kept)
+        out_off.append(len(idx))
+    return np.asarray(out_off, dtype=np.int64), np.asarray(idx, dtype=np.int64)
+
+
+def gather_rows(x, index):
+    """out[i] = x[index[i]] (rows of any shape and dtype, bytes unchanged)."""
+    return np.asarray(x)[np.asarray(index, dtype=np.int64)]
 
 
 # --------------------------------------------------------------------------

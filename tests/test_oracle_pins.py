@@ -694,3 +694,168 @@ def test_cp_block_form_equals_row_form_and_unsharded(lengths, cp):
             acc += part
     for acc, want in zip(sums, full_g[1:]):
         np.testing.assert_allclose(acc, want, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Stochastic Length ([HSTU] §3.2, §4.2, App. E)
+# --------------------------------------------------------------------------
+
+def iroot(x: int, k: int) -> int:
+    """floor(x^(1/k)) for integers, by bisection on exact integer powers."""
+    lo, hi = 0, 1
+    while hi ** k <= x:
+        hi *= 2
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if mid ** k <= x:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def test_sl_printed_length_after_sampling():
+    # the pages' one printed case: alpha = 1.6, length 4096 -> 776
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "sl_length_at_alpha_1_6.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    assert rows
+    for alpha, n, want in rows:
+        assert oracle.sl_target_length(int(n), float(alpha)) == int(want)
+
+
+@pytest.mark.parametrize("alpha,k,p", [(1.0, 2, 1), (1.5, 4, 3), (1.75, 8, 7), (0.5, 4, 1), (1.25, 8, 5)])
+def test_sl_target_length_equals_integer_roots(alpha, k, p):
+    # alpha/2 = p/k exactly (dyadic alphas), so floor(n^(alpha/2)) is the
+    # integer k-th root of n^p: a different route from the decimal power
+    for n in list(range(1, 3000)) + [4095, 4096, 4097, 8191, 8192, 16384, 65535, 65536, 1 << 20]:
+        assert oracle.sl_target_length(n, alpha) == min(iroot(n ** p, k), n), n
+
+
+def test_sl_keep_whole_rule():
+    from fractions import Fraction
+    # alpha = 1: kept whole iff u < n^-1 = 1/n (exact rational compare)
+    rng = np.random.default_rng(3)
+    for n in [2, 3, 7, 100, 4096]:
+        for u in list(rng.random(50)) + [1.0 / n, np.nextafter(1.0 / n, 0.0), np.nextafter(1.0 / n, 1.0)]:
+            assert oracle.sl_keeps_whole(n, 1.0, float(u)) == (Fraction(float(u)) < Fraction(1, n)), (n, u)
+    # alpha >= 2 never shortens; length 1 and 0 are untouched
+    assert all(oracle.sl_keeps_whole(n, 2.0, 0.999) for n in (1, 5, 4096))
+    assert oracle.sl_keeps_whole(1, 1.6, 0.5)
+    # the printed case is shortened "most of the time": for u spread over
+    # [0, 1) it is kept whole only below 4096^-0.4 = 0.0359
+    us = (np.arange(10000) + 0.5) / 10000
+    kept = np.mean([oracle.sl_keeps_whole(4096, 1.6, float(u)) for u in us])
+    assert abs(kept - 4096 ** -0.4) < 1e-3 and kept < 0.5
+
+
+def sl_brute(offsets, alpha, u, keys):
+    idx, off = [], [0]
+    for b in range(len(offsets) - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        n = hi - lo
+        if n > 0 and not oracle.sl_keeps_whole(n, alpha, float(u[b])):
+            L = oracle.sl_target_length(n, alpha)
+            if keys is None:
+                rows = np.arange(hi - L, hi)
+            else:
+                order = np.lexsort((np.arange(lo, hi), keys[lo:hi]))  # by key, then position
+                rows = lo + np.sort(order[:L])
+        else:
+            rows = np.arange(lo, hi)
+        idx.extend(int(r) for r in rows)
+        off.append(len(idx))
+    return np.asarray(off), np.asarray(idx, dtype=np.int64)
+
+
+@pytest.mark.parametrize("mode", ["random", "recency", "random_ties"])
+def test_sl_selection_matches_brute_force(mode):
+    rng = np.random.default_rng(11)
+    lengths = [0, 1, 2, 5, 64, 300, 1000, 4096, 17]
+    off = synth.offsets_from_lengths(lengths)
+    T = int(off[-1])
+    u = rng.random(len(lengths))
+    u[7] = 0.5  # the 4096-row sequence is cut
+    keys = None
+    if mode == "random":
+        keys = rng.integers(0, 1 << 32, size=T, dtype=np.uint64).astype(np.uint32)
+    elif mode == "random_ties":
+        keys = rng.integers(0, 7, size=T).astype(np.uint32)  # many equal keys
+    for alpha in (1.6, 1.2, 1.0):
+        got_off, got = oracle.sl_select(off, alpha, u, keys)
+        want_off, want = sl_brute(off, alpha, u, keys)
+        assert np.array_equal(got_off, want_off) and np.array_equal(got, want)
+        # structure: per sequence a sorted subset of its rows
+        for b in range(len(lengths)):
+            seg = got[got_off[b]:got_off[b + 1]]
+            assert np.all(np.diff(seg) > 0) and np.all((seg >= off[b]) & (seg < off[b + 1]))
+        if alpha == 1.6:
+            assert got_off[8] - got_off[7] == 776
+
+
+def test_sl_random_selection_is_uniform():
+    # with uniform random keys every position of a sequence is kept with
+    # probability L/n (here 776/4096), whatever its place
+    rng = np.random.default_rng(12)
+    off = np.array([0, 4096])
+    hits = np.zeros(4096)
+    for _ in range(200):
+        keys = rng.integers(0, 1 << 32, size=4096, dtype=np.uint64).astype(np.uint32)
+        _, idx = oracle.sl_select(off, 1.6, [0.9], keys)
+        hits[idx] += 1
+    p = hits / 200
+    assert abs(p.mean() - 776 / 4096) < 1e-9
+    assert abs(p[:2048].mean() - p[2048:].mean()) < 0.01
+
+
+def test_sl_gather_rows():
+    x = np.arange(40, dtype=np.int64).reshape(10, 4)
+    assert np.array_equal(oracle.gather_rows(x, [3, 0, 9]), x[[3, 0, 9]])
+
+
+def test_sl_planted_mistakes_are_caught(monkeypatch):
+    orig = ho.sl_target_length
+
+    def ceil_length(n, alpha):
+        return min(int(math.ceil(float(ho._pow_exact(n, ho.Fraction(alpha) / 2)))), n)
+
+    def full_alpha(n, alpha):
+        return min(int(math.floor(float(ho._pow_exact(n, ho.Fraction(alpha))))), n)
+
+    for bad in (ceil_length, full_alpha):
+        monkeypatch.setattr(ho, "sl_target_length", bad)
+        monkeypatch.setattr(oracle, "sl_target_length", bad)
+        with pytest.raises(AssertionError):
+            test_sl_printed_length_after_sampling()
+    monkeypatch.setattr(ho, "sl_target_length", orig)
+    monkeypatch.setattr(oracle, "sl_target_length", orig)
+    # ties broken the wrong way, and kept rows not in their original order
+    orig_select = ho.sl_select
+
+    def unordered(offsets, alpha, u, keys=None):
+        o, idx = orig_select(offsets, alpha, u, keys)
+        for b in range(len(o) - 1):
+            idx[o[b]:o[b + 1]] = idx[o[b]:o[b + 1]][::-1].copy()
+        return o, idx
+
+    monkeypatch.setattr(oracle, "sl_select", unordered)
+    with pytest.raises(AssertionError):
+        test_sl_selection_matches_brute_force("random")
+
+    def late_ties(offsets, alpha, u, keys=None):
+        if keys is None:
+            return orig_select(offsets, alpha, u, keys)
+        out_off, idx = [0], []
+        for b in range(len(offsets) - 1):
+            lo, hi = int(offsets[b]), int(offsets[b + 1])
+            n = hi - lo
+            if n and not ho.sl_keeps_whole(n, alpha, float(u[b])):
+                order = sorted(range(lo, hi), key=lambda r: (int(keys[r]), -r))
+                idx.extend(sorted(order[:ho.sl_target_length(n, alpha)]))
+            else:
+                idx.extend(range(lo, hi))
+            out_off.append(len(idx))
+        return np.asarray(out_off), np.asarray(idx, dtype=np.int64)
+
+    monkeypatch.setattr(oracle, "sl_select", late_ties)
+    with pytest.raises(AssertionError):
+        test_sl_selection_matches_brute_force("random_ties")
