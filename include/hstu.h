@@ -193,6 +193,31 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
                          void* dq, void* dk, void* dv, float* d_ts_weights,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward that allocates nothing, for callers that cannot allocate device
+ * memory or call hipMalloc: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same operation, arguments (minus the
+ * workspace), layout and errors as hstu_jagged_attn_fwd; the scratch it needs
+ * (work lists, counters, bucket tables, split partial sums) lives in a
+ * library-owned device array of hstu_noalloc_scratch_bytes() bytes (16 MiB)
+ * that each GPU holds from the first call until the process ends.  Problems
+ * whose work lists do not fit it return HSTU_EWORKSPACE before any launch
+ * (about 500k query tiles of 128 rows); when the partial sums of split key
+ * walks do not fit, long query tiles are walked in one item instead (same
+ * result up to the order of the fp32 sums).  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (several streams, several
+ * host threads) race and must be serialised by the caller.  No call to
+ * hipMalloc, hipFree or hipMemset is made; the scheduler kernel rewrites all
+ * the state a call reads. */
+int hstu_jagged_attn_fwd_noalloc(const hstu_problem_t* p, const void* q,
+                                 const void* k, const void* v,
+                                 const int64_t* offsets,
+                                 const int64_t* timestamps,
+                                 const void* ts_weights, void* out,
+                                 void* stream);
+
+/* Bytes of the no-allocation forward's per-GPU scratch array. */
+size_t hstu_noalloc_scratch_bytes(void);
+
 /* Load-balanced chunk-pair reorder (CP paper §2.3, memory-reordering shuffle).
  * A pure row permutation of `in` [total_rows, row_bytes] into `out` (same size,
  * must not overlap `in`).  inverse = 0: sequence-major -> rank-major, i.e. for

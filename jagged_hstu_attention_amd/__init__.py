@@ -24,7 +24,7 @@ from ._lib import HSTU_BF16, HSTU_FLAG_RECOMPUTE_BWD, HSTU_FLAG_SHARED_SCHEDULE,
 
 __all__ = [
     "Problem", "HstuError", "HSTU_FLAG_RECOMPUTE_BWD", "HSTU_FLAG_SHARED_SCHEDULE", "problem", "workspace_size", "jagged_attn_fwd",
-    "jagged_attn_fwd_targets", "jagged_attn_bwd",
+    "jagged_attn_fwd_targets", "jagged_attn_fwd_noalloc", "jagged_attn_bwd",
     "cp_reorder", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
 ]
 
@@ -120,6 +120,21 @@ def jagged_attn_fwd(q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_si
     lib = _lib.load()
     _lib.check(lib.hstu_jagged_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets), _ptr(ts),
                                         _ptr(ts_weights), _ptr(out), _ptr(ws), ws_bytes, _stream(q.device)))
+    return out
+
+
+def jagged_attn_fwd_noalloc(q, k, v, offsets, ts, ts_weights, max_seq_len: int, *, cp_size: int = 1,
+                            cp_rank: int = 0, out=None):
+    """Forward through the entry point that allocates nothing: its scratch is
+    the library's static per-GPU array (calls on one GPU must not overlap).
+    Returns out [total_q, H, d_v] (allocated here by torch unless given)."""
+    torch = _torch()
+    p = problem(q, k, v, offsets, ts_weights, max_seq_len, cp_size=cp_size, cp_rank=cp_rank)
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    lib = _lib.load()
+    _lib.check(lib.hstu_jagged_attn_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                                                _ptr(ts), _ptr(ts_weights), _ptr(out), _stream(q.device)))
     return out
 
 

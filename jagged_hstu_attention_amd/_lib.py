@@ -50,6 +50,8 @@ EXPORTS = [
     "hstu_timing_enable",
     "hstu_timing_reset",
     "hstu_timing_read",
+    "hstu_jagged_attn_fwd_noalloc",
+    "hstu_noalloc_scratch_bytes",
 ]
 
 KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4, "reduce": 5}
@@ -81,6 +83,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_fwd_targets.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                                  ctypes.c_size_t, vp]
     lib.hstu_jagged_attn_fwd_targets.restype = ctypes.c_int
+    lib.hstu_jagged_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hstu_jagged_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.hstu_noalloc_scratch_bytes.argtypes = []
+    lib.hstu_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.hstu_jagged_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.hstu_jagged_attn_bwd.restype = ctypes.c_int
     lib.hstu_cp_reorder.argtypes = [vp, vp, i64, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp]

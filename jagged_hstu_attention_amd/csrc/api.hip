@@ -211,7 +211,7 @@ int64_t g_blocks_for(const hstu_problem_t* p) {
   return blocks > kGMaxBytes / hstu::kGBlockBytes ? 0 : blocks;
 }
 
-Layout layout_for(const hstu_problem_t* p, bool backward) {
+Layout layout_for(const hstu_problem_t* p, bool backward, bool allow_split = true) {
   // a forward whose schedule the backward shares builds the backward's lists too
   backward = backward || (p->flags & HSTU_FLAG_SHARED_SCHEDULE);
   Layout l{};
@@ -231,7 +231,7 @@ Layout layout_for(const hstu_problem_t* p, bool backward) {
   off = align_up(off + (size_t)(p->num_seqs + 1) * sizeof(int64_t));
   l.tile_off = off;
   off = align_up(off + (size_t)2 * (p->num_seqs + 1) * sizeof(int));
-  l.q_extra = q_extra_for(p, l.max_qtiles);
+  l.q_extra = allow_split ? q_extra_for(p, l.max_qtiles) : 0;
   l.qitems = off;
   off = align_up(off + (size_t)(l.max_qtiles + l.q_extra) * sizeof(hstu::Item));
   l.kitems = off;
@@ -519,7 +519,7 @@ namespace {
 
 int fwd_impl(const hstu_problem_t* p, const void* q, const void* k, const void* v, const int64_t* offsets,
              const int64_t* num_targets, int targets_only, const int64_t* timestamps, const void* ts_weights,
-             void* out, void* workspace, size_t workspace_bytes, void* stream) {
+             void* out, void* workspace, size_t workspace_bytes, void* stream, bool allow_split = true) {
   if (p->total_q == 0 || p->num_seqs == 0) return HSTU_OK;
   CHECK_PTR(q, "q");
   CHECK_PTR(k, "k");
@@ -528,7 +528,7 @@ int fwd_impl(const hstu_problem_t* p, const void* q, const void* k, const void* 
   CHECK_PTR8(offsets, "offsets");
   CHECK_PTR8(timestamps, "timestamps");
   if (!ts_weights) return fail(HSTU_EINVAL, "ts_weights is NULL");
-  const Layout l = layout_for(p, false);  // the backward's layout with HSTU_FLAG_SHARED_SCHEDULE
+  const Layout l = layout_for(p, false, allow_split);  // the backward's layout with HSTU_FLAG_SHARED_SCHEDULE
   if (!workspace) return fail(HSTU_EWORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(HSTU_EINVAL, "workspace is not 16-byte aligned");
   if (workspace_bytes < l.total)
@@ -681,6 +681,78 @@ int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* 
     }
   }
   return HSTU_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward without allocation (hstu_jagged_attn_fwd_noalloc): its workspace is
+// `scratch`, a file-scope device array of kScratchBytes that every GPU the
+// library runs on holds until the process ends.  In host code the array's
+// name is only a stand-in for the symbol: the device address of each GPU's
+// copy is looked up once per device with hipGetSymbolAddress (that device
+// current) and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = 16u << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+int scratch_ptr(char** out) {
+  static std::mutex mu;
+  static char* cache[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "no-allocation forward: current device");
+  if (dev < 0 || dev >= 64) return fail(HSTU_EUNSUPPORTED, "device index %d >= 64", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "no-allocation forward: scratch address");
+    cache[dev] = static_cast<char*>(ptr);
+  }
+  *out = cache[dev];
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hstu_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int hstu_jagged_attn_fwd_noalloc(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+                                 const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
+                                 void* stream) {
+  int rc = validate(p);
+  if (rc != HSTU_OK) return rc;
+  if (p->flags & HSTU_FLAG_SHARED_SCHEDULE)
+    return fail(HSTU_EUNSUPPORTED, "the no-allocation forward does not share its schedule with a backward");
+  // the work lists must fit the static scratch: with split key walks if their
+  // partial sums fit too, else without (each query tile then walks its keys
+  // in one item)
+  bool split = true;
+  size_t need = layout_for(p, false, true).total;
+  if (need > kScratchBytes) {
+    split = false;
+    need = layout_for(p, false, false).total;
+  }
+  if (need > kScratchBytes)
+    return fail(HSTU_EWORKSPACE, "problem needs %zu bytes of scratch; the no-allocation forward has %zu", need,
+                kScratchBytes);
+  if (p->total_q == 0 || p->num_seqs == 0) return HSTU_OK;
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(out, "out");
+  CHECK_PTR8(offsets, "offsets");
+  CHECK_PTR8(timestamps, "timestamps");
+  if (!ts_weights) return fail(HSTU_EINVAL, "ts_weights is NULL");
+  char* ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc != HSTU_OK) return rc;
+  return fwd_impl(p, q, k, v, offsets, nullptr, 0, timestamps, ts_weights, out, ws, kScratchBytes, stream, split);
 }
 
 int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t num_seqs,

@@ -322,3 +322,21 @@ def test_validate_env_runs_the_offsets_check_first(monkeypatch):
         assert call() == 4 and b"offsets check" not in lib.hstu_last_error()
     monkeypatch.delenv("HSTU_VALIDATE")
     assert call() == 4 and b"offsets check" not in lib.hstu_last_error()
+
+
+def test_noalloc_forward_rejects_problems_beyond_its_scratch():
+    lib = _lib.load()
+    assert lib.hstu_noalloc_scratch_bytes() == 16 << 20
+    g = ctypes.c_void_p(1 << 20)
+    # 2^30 rows need 8M query tiles of work list: far past 16 MiB, refused before any launch
+    big = make_problem(num_seqs=1, total_kv=1 << 30, total_q=1 << 30, max_seq_len=1 << 30)
+    rc = lib.hstu_jagged_attn_fwd_noalloc(ctypes.byref(big), g, g, g, g, g, g, g, None)
+    assert rc == 3 and b"scratch" in lib.hstu_last_error()
+    # a shared schedule needs a backward-sized workspace: refused
+    shared = make_problem(flags=hstu.HSTU_FLAG_SHARED_SCHEDULE)
+    assert lib.hstu_jagged_attn_fwd_noalloc(ctypes.byref(shared), g, g, g, g, g, g, g, None) == 2
+    # argument checks as for the forward with a workspace
+    p = make_problem()
+    assert lib.hstu_jagged_attn_fwd_noalloc(ctypes.byref(p), None, g, g, g, g, g, g, None) == 1
+    assert lib.hstu_jagged_attn_fwd_noalloc(ctypes.byref(make_problem(dtype=5)), g, g, g, g, g, g, g, None) == 1
+
