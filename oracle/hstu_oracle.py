@@ -43,7 +43,9 @@ What is computed, with the readings taken where the pages are open
    selection; at alpha = 1.6 a length-4096 history becomes length 776 most of
    the time) and App. E (the subsequence is chosen by recency, at random, or
    by feature weights).  Readings: a sequence of length n is cut to
-   L = floor(n^(alpha/2)) rows (4096^0.8 = 776.05), except that with
+   L = floor(n^(alpha/2)) rows (4096^0.8 = 776.05; the power carries a 2^-40
+   relative tolerance so that a float alpha such as 1.2 gives 32^0.6 = 8,
+   not the 7 its binary value would), except that with
    probability n^(alpha-2) it is kept whole (so the printed case is cut with
    probability 1 - 4096^-0.4 = 0.964, "most of the time"); the draw is an
    input u_b in [0, 1), kept whole iff u_b < n^(alpha-2).  The kept rows are
@@ -395,11 +397,20 @@ def _pow_exact(n: int, exponent: Fraction) -> Decimal:
         return Decimal(n) ** (Decimal(exponent.numerator) / Decimal(exponent.denominator))
 
 
+# alpha arrives as a binary float (1.2 is not 6/5), so n^(alpha/2) at a
+# perfect power (32^0.6 = 8) can fall a hair below the integer the caller
+# means; a relative tolerance of 2^-40 on the power absorbs that.
+SL_REL_TOL = Fraction(1, 1 << 40)
+
+
 def sl_target_length(n: int, alpha: float) -> int:
-    """L = floor(n^(alpha/2)), at most n."""
+    """L = floor(n^(alpha/2) (1 + 2^-40)), at most n."""
     if n <= 0:
         return 0
-    return min(int(math.floor(_pow_exact(n, Fraction(alpha) / 2))), n)
+    with localcontext() as ctx:
+        ctx.prec = 60
+        x = _pow_exact(n, Fraction(alpha) / 2) * (1 + Decimal(SL_REL_TOL.numerator) / Decimal(SL_REL_TOL.denominator))
+    return min(int(math.floor(x)), n)
 
 
 def sl_keeps_whole(n: int, alpha: float, u: float) -> bool:

@@ -731,6 +731,19 @@ def test_sl_target_length_equals_integer_roots(alpha, k, p):
         assert oracle.sl_target_length(n, alpha) == min(iroot(n ** p, k), n), n
 
 
+def test_sl_float_alpha_at_perfect_powers():
+    # alpha = 1.2 as a float is slightly below 6/5: the length at perfect
+    # fifth powers is still the integer k^3 (the 2^-40 tolerance), and away
+    # from integers the floor is unchanged
+    for k in range(2, 9):
+        assert oracle.sl_target_length(k ** 5, 1.2) == k ** 3
+    assert oracle.sl_target_length(4096, 1.2) == 147  # 2^7.2 = 147.03
+    for n in range(2, 5000):
+        exact = n ** 0.6
+        if abs(exact - round(exact)) > 1e-6:
+            assert oracle.sl_target_length(n, 1.2) == math.floor(exact), n
+
+
 def test_sl_keep_whole_rule():
     from fractions import Fraction
     # alpha = 1: kept whole iff u < n^-1 = 1/n (exact rational compare)
