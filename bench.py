@@ -19,7 +19,9 @@ Besides the JSON contract fields it reports:
                 power-law batch (forward+backward), the uniform 256..1024
                 forward, and the candidates pass: 16 users with a 3072-row
                 history and a micro-batch of 1024 candidates each, candidates
-                only against cached history K/V (candidates/s and TFLOP/s).
+                only against cached history K/V (candidates/s and TFLOP/s), and
+                Stochastic Length on the skewed batch (selection time, gather
+                GB/s against the HBM peak).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --counter-run          (the program profiled for HBM counters)
@@ -283,6 +285,50 @@ def candidates_pass(m, steps, users=16, hist=3072, cands=1024):
             "tflops": round(fl / t / 1e9, 2)}
 
 
+def stochastic_length(m, steps):
+    """Stochastic Length on the skewed power-law batch (B = 256, lengths
+    16..8192, H = 8, d = 64, bf16) at alpha = 1.6 with random selection:
+    the selection (kept lengths, offsets, row index) and the gather of q, k,
+    v and the timestamps into the sampled jagged batch.  The gather moves
+    2 x kept rows x row bytes per tensor (read + write) against the 8 TB/s
+    HBM peak."""
+    import numpy as np
+    import torch
+    import synth
+    wl = synth.config("skewed_powerlaw", with_dout=False)
+
+    def up(t):
+        return torch.from_numpy(t.raw.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    ts = torch.from_numpy(wl.ts).cuda()
+    off = torch.from_numpy(wl.offsets).cuda()
+    rng = np.random.default_rng(1006)
+    u = torch.from_numpy(rng.random(wl.num_seqs).astype(np.float32)).cuda()
+    keys = torch.from_numpy(rng.integers(0, 1 << 32, size=wl.total, dtype=np.uint64).astype(np.uint32)
+                            .view(np.int32)).cuda()
+    out_off = torch.empty(wl.num_seqs + 1, dtype=torch.int64, device="cuda")
+    out_idx = torch.empty(wl.total, dtype=torch.int64, device="cuda")
+    outs = [torch.empty_like(t) for t in (q, k, v, ts)]
+
+    def select():
+        m.sl_select(off, wl.max_seq_len, 1.6, u, keys, out_offsets=out_off, out_index=out_idx)
+
+    def gather():
+        for src, dst in zip((q, k, v, ts), outs):
+            m.gather_rows(src, out_idx, out_off[-1:], out=dst)
+
+    t_sel = time_loop(select, steps, 3)
+    t_gat = time_loop(gather, steps, 3)
+    kept = int(out_off[-1].item())
+    row_bytes = sum(t.element_size() * int(np.prod(t.shape[1:])) for t in (q, k, v, ts))
+    moved = 2 * kept * row_bytes
+    return {"alpha": 1.6, "rows_in": wl.total, "rows_kept": kept, "select_ms": round(t_sel, 4),
+            "gather_ms": round(t_gat, 4), "gather_gbs": round(moved / t_gat / 1e6, 1),
+            "gather_frac_hbm": round(moved / t_gat / 1e6 / HBM_PEAK_GBS, 4),
+            "rows_per_s": round(wl.total / ((t_sel + t_gat) * 1e-3), 1)}
+
+
 def cpu_baseline(max_seconds=30.0):
     """The float64 oracle, as it stands, on a bounded sample of the 3072-length
     workload: whole sequences (all 4 heads, forward + backward), as many as fit
@@ -469,6 +515,9 @@ def main():
         torch.cuda.empty_cache()
         log("candidates against cached history")
         extra["candidates_b16_hist3072_m1024"] = candidates_pass(m, args.steps)
+        torch.cuda.empty_cache()
+        log("stochastic length on the skewed batch")
+        extra["stochastic_length_skewed_alpha1.6"] = stochastic_length(m, args.steps)
 
     cpu = None
     if not args.no_cpu:

@@ -236,6 +236,42 @@ int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes,
                     int64_t max_seq_len, int64_t cp_size, int inverse,
                     int64_t* out_offsets, void* stream);
 
+/* Stochastic Length (Actions Speak Louder than Words, §3.2 and §4.2: long
+ * histories are sparsified by keeping a subsequence; at alpha = 1.6 a
+ * length-4096 history becomes length 776 most of the time; App. E: the
+ * subsequence is chosen by recency or at random, among other criteria).
+ * Selection only; hstu_gather_rows then moves any tensor's rows.
+ *   offsets      int64 [B+1], sequence offsets of the input rows
+ *   alpha        in (0, 64): a sequence of length n is cut to
+ *                L = floor(n^(alpha/2)) rows (computed in double precision,
+ *                an exact integer power kept exact), unless
+ *   seq_uniform  float [B], one draw in [0, 1) per sequence: kept whole when
+ *                seq_uniform[b] < n^(alpha-2) (probability n^(alpha-2)), or
+ *                when L >= n
+ *   token_keys   uint32 [total_rows] random keys (device), or NULL.  Keys
+ *                given: the L rows with the smallest keys are kept (equal
+ *                keys in position order); NULL: the last L rows (recency).
+ *   out_offsets  int64 [B+1] (written): offsets of the kept rows
+ *   out_index    int64 [total_rows] (written for the first out_offsets[B]
+ *                entries): the input row of every output row; the kept rows
+ *                of a sequence stay in their original order.
+ * The output row count out_offsets[B] stays on the device (no host sync);
+ * total_rows bounds it.  Two launches on `stream`. */
+int hstu_sl_select(const int64_t* offsets, int64_t num_seqs, int64_t total_rows,
+                   int64_t max_seq_len, double alpha, const float* seq_uniform,
+                   const uint32_t* token_keys, int64_t* out_offsets,
+                   int64_t* out_index, void* stream);
+
+/* Row gather: out[i] = in[index[i]] for i < min(*count, max_rows), rows of
+ * row_bytes bytes copied unchanged (bit-exact, widest of 16/8/4/1-byte
+ * accesses that row_bytes and both pointers allow).  count is a device
+ * pointer (e.g. out_offsets + B of hstu_sl_select), so the call needs no host
+ * synchronisation; max_rows bounds the launch.  index entries must be valid
+ * rows of `in` (the caller's contract, as hstu_sl_select's output is). */
+int hstu_gather_rows(const void* in, void* out, int64_t row_bytes,
+                     const int64_t* index, const int64_t* count,
+                     int64_t max_rows, void* stream);
+
 /* Host helper: the integer bucket edges the kernels use.  Writes NB+1 uint32
  * values to host memory edges_out: edges_out[0] = 0, edges_out[k] = E_k =
  * ceil(2^(32k/NB)) for 1 <= k < NB, edges_out[NB] = 0xFFFFFFFF (sentinel). */
@@ -258,7 +294,9 @@ typedef enum {
   HSTU_KERNEL_BWD_Q = 3,    /* backward, query-major pass: dQ */
   HSTU_KERNEL_REORDER = 4,  /* chunk-pair reorder */
   HSTU_KERNEL_REDUCE = 5,   /* sum of the parts of split query tiles (forward or dQ) */
-  HSTU_KERNEL_COUNT = 6
+  HSTU_KERNEL_SL = 6,       /* Stochastic Length selection (lengths, then rows) */
+  HSTU_KERNEL_GATHER = 7,   /* row gather */
+  HSTU_KERNEL_COUNT = 8
 } hstu_kernel_t;
 int hstu_timing_enable(int on);
 int hstu_timing_reset(void);

@@ -25,7 +25,7 @@ from ._lib import HSTU_BF16, HSTU_FLAG_RECOMPUTE_BWD, HSTU_FLAG_SHARED_SCHEDULE,
 __all__ = [
     "Problem", "HstuError", "HSTU_FLAG_RECOMPUTE_BWD", "HSTU_FLAG_SHARED_SCHEDULE", "problem", "workspace_size", "jagged_attn_fwd",
     "jagged_attn_fwd_targets", "jagged_attn_fwd_noalloc", "jagged_attn_bwd",
-    "cp_reorder", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
+    "cp_reorder", "sl_select", "gather_rows", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
 ]
 
 
@@ -197,6 +197,42 @@ def cp_reorder(x, offsets, max_seq_len: int, cp_size: int, *, inverse: bool = Fa
                                    int(max_seq_len), int(cp_size), 1 if inverse else 0,
                                    _ptr(out_offsets) if out_offsets is not None else None, _stream(x.device)))
     return out, out_offsets
+
+
+def sl_select(offsets, max_seq_len: int, alpha: float, seq_uniform, token_keys=None, *, out_offsets=None,
+              out_index=None):
+    """Stochastic Length selection.  offsets int64 [B+1]; seq_uniform float32
+    [B] (keep-whole draws in [0, 1)); token_keys uint32-valued int32 [T] (the
+    L smallest are kept) or None (recency).  Returns (out_offsets [B+1],
+    out_index [T]); only the first out_offsets[B] entries of out_index are
+    written (the count stays on the device)."""
+    torch = _torch()
+    B = int(offsets.shape[0]) - 1
+    T = int(token_keys.shape[0]) if token_keys is not None else None
+    if out_offsets is None:
+        out_offsets = torch.empty(B + 1, dtype=torch.int64, device=offsets.device)
+    if out_index is None:
+        if T is None:
+            raise ValueError("out_index must be given (or token_keys, whose length is the row count)")
+        out_index = torch.empty(T, dtype=torch.int64, device=offsets.device)
+    total = int(out_index.shape[0])
+    _lib.check(_lib.load().hstu_sl_select(_ptr(offsets), B, total, int(max_seq_len), float(alpha), _ptr(seq_uniform),
+                                          _ptr(token_keys), _ptr(out_offsets), _ptr(out_index),
+                                          _stream(offsets.device)))
+    return out_offsets, out_index
+
+
+def gather_rows(x, index, count, *, out=None):
+    """out[i] = x[index[i]] for i < count[0] (count: a one-element device
+    tensor, e.g. out_offsets[-1:]); rows past the count are left as they are.
+    out defaults to a tensor of x's shape."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    row_bytes = x.element_size() * math.prod(x.shape[1:])
+    _lib.check(_lib.load().hstu_gather_rows(_ptr(x), _ptr(out), row_bytes, _ptr(index), _ptr(count),
+                                            min(int(index.shape[0]), int(out.shape[0])), _stream(x.device)))
+    return out
 
 
 def bucket_edges(num_buckets: int):

@@ -52,9 +52,11 @@ EXPORTS = [
     "hstu_timing_read",
     "hstu_jagged_attn_fwd_noalloc",
     "hstu_noalloc_scratch_bytes",
+    "hstu_sl_select",
+    "hstu_gather_rows",
 ]
 
-KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4, "reduce": 5}
+KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4, "reduce": 5, "sl": 6, "gather": 7}
 
 _lib = None
 
@@ -91,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_jagged_attn_bwd.restype = ctypes.c_int
     lib.hstu_cp_reorder.argtypes = [vp, vp, i64, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp]
     lib.hstu_cp_reorder.restype = ctypes.c_int
+    lib.hstu_sl_select.argtypes = [vp, i64, i64, i64, ctypes.c_double, vp, vp, vp, vp, vp]
+    lib.hstu_sl_select.restype = ctypes.c_int
+    lib.hstu_gather_rows.argtypes = [vp, vp, i64, vp, vp, i64, vp]
+    lib.hstu_gather_rows.restype = ctypes.c_int
     lib.hstu_bucket_edges.argtypes = [i64, ctypes.POINTER(ctypes.c_uint32)]
     lib.hstu_bucket_edges.restype = ctypes.c_int
     lib.hstu_last_error.argtypes = []

@@ -15,6 +15,7 @@
 #include "attn.h"
 #include "bias.h"
 #include "hstu.h"
+#include "sl.h"
 
 namespace {
 
@@ -753,6 +754,58 @@ int hstu_jagged_attn_fwd_noalloc(const hstu_problem_t* p, const void* q, const v
   rc = scratch_ptr(&ws);
   if (rc != HSTU_OK) return rc;
   return fwd_impl(p, q, k, v, offsets, nullptr, 0, timestamps, ts_weights, out, ws, kScratchBytes, stream, split);
+}
+
+int hstu_sl_select(const int64_t* offsets, int64_t num_seqs, int64_t total_rows, int64_t max_seq_len, double alpha,
+                   const float* seq_uniform, const uint32_t* token_keys, int64_t* out_offsets, int64_t* out_index,
+                   void* stream) {
+  if (num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)num_seqs);
+  if (total_rows < 0) return fail(HSTU_EINVAL, "total_rows %lld < 0", (long long)total_rows);
+  if (total_rows >= (1ll << 31)) return fail(HSTU_EUNSUPPORTED, "total_rows %lld >= 2^31", (long long)total_rows);
+  if (num_seqs >= (1ll << 31)) return fail(HSTU_EUNSUPPORTED, "num_seqs too large");
+  if (max_seq_len < 0 || max_seq_len > total_rows)
+    return fail(HSTU_EINVAL, "max_seq_len %lld not in [0, total_rows]", (long long)max_seq_len);
+  if (!(alpha > 0.0) || !(alpha < 64.0)) return fail(HSTU_EINVAL, "alpha %g not in (0, 64)", alpha);
+  if (num_seqs == 0) return HSTU_OK;
+  CHECK_PTR8(offsets, "offsets");
+  CHECK_PTR8(out_offsets, "out_offsets");
+  if (!seq_uniform || ((uintptr_t)seq_uniform & 3)) return fail(HSTU_EINVAL, "seq_uniform is NULL or misaligned");
+  if (token_keys && ((uintptr_t)token_keys & 3)) return fail(HSTU_EINVAL, "token_keys is not 4-byte aligned");
+  if (total_rows > 0) CHECK_PTR8(out_index, "out_index");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hstu::CheckParams cp{};
+  cp.offsets = offsets;
+  cp.B = num_seqs;
+  cp.total_kv = total_rows;
+  cp.max_seq_len = max_seq_len;
+  cp.total_q = -1;
+  const int rc = check_offsets(cp, s);
+  if (rc != HSTU_OK) return rc;
+  const hipError_t e = timed(HSTU_KERNEL_SL, s, [&] {
+    return hstu::launch_sl_select(offsets, num_seqs, alpha, seq_uniform, token_keys, out_offsets, out_index, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "stochastic length launch");
+  return HSTU_OK;
+}
+
+int hstu_gather_rows(const void* in, void* out, int64_t row_bytes, const int64_t* index, const int64_t* count,
+                     int64_t max_rows, void* stream) {
+  if (row_bytes < 1) return fail(HSTU_EINVAL, "row_bytes %lld < 1", (long long)row_bytes);
+  if (max_rows < 0) return fail(HSTU_EINVAL, "max_rows %lld < 0", (long long)max_rows);
+  if (max_rows > 0 && row_bytes > (1ll << 40) / max_rows) return fail(HSTU_EUNSUPPORTED, "max_rows * row_bytes >= 2^40");
+  if (max_rows == 0) return HSTU_OK;
+  if (!in || !out) return fail(HSTU_EINVAL, "in/out is NULL");
+  CHECK_PTR8(index, "index");
+  CHECK_PTR8(count, "count");
+  int vec = 16;
+  while (vec > 1 && (row_bytes % vec || ((uintptr_t)in | (uintptr_t)out) % vec)) vec >>= 1;
+  if (vec == 2) vec = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(HSTU_KERNEL_GATHER, s, [&] {
+    return hstu::launch_gather_rows(in, out, row_bytes, index, count, max_rows, vec, cu_count(), s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return HSTU_OK;
 }
 
 int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t num_seqs,
