@@ -30,6 +30,8 @@ from .hstu_oracle import (  # noqa: F401
     sl_select,
     sl_target_length,
     gather_rows,
+    hstu_norm_gate,
+    hstu_projection,
     silu_grad,
     target_mask,
     target_rows,

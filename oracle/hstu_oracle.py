@@ -39,6 +39,16 @@ What is computed, with the readings taken where the pages are open
    timestamps, and attend to their causal key prefix of the full sequence.
 5. Reorder, [CP] §2.3 (memory-reordering data shuffle): the rank-major
    permutation of rows; rank, then sequence, then chunk r then chunk 2C-1-r.
+8. HSTU layer steps either side of the attention, [HSTU] §3 (residual
+   layers of pointwise projection, spatial aggregation and pointwise
+   transformation; the interaction Norm(A(X)V(X)) ⊙ U(X)).  Readings: the
+   projection is one linear map without bias followed by SiLU, split into
+   U, V, Q, K in that order: [U V Q K] = SiLU(X Wᵀ) with W [H(2 d_v +
+   2 d_qk), d_model] (the layout of a linear layer's weight); Norm is layer
+   normalisation over each row's H d_v attention outputs, eps = 1e-6, no
+   learned scale or shift; the step returns Norm(O) ⊙ U, O the attention
+   output.  The output projection and residual add are not printed and are
+   not part of it.
 7. Stochastic Length, [HSTU] §3.2 and §4.2 (sequence sparsity by subsequence
    selection; at alpha = 1.6 a length-4096 history becomes length 776 most of
    the time) and App. E (the subsequence is chosen by recency, at random, or
@@ -455,6 +465,41 @@ def sl_select(offsets, alpha: float, seq_uniform, token_keys=None):
 def gather_rows(x, index):
     """out[i] = x[index[i]] (rows of any shape and dtype, bytes unchanged)."""
     return np.asarray(x)[np.asarray(index, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------
+# 8. HSTU layer steps ([HSTU] §3: pointwise projection; Norm(A(X)V(X)) ⊙ U(X))
+# --------------------------------------------------------------------------
+
+LAYER_NORM_EPS = 1e-6
+
+
+def hstu_projection(x, w, num_heads: int, d_qk: int, d_v: int):
+    """[U V Q K] = SiLU(x wᵀ): x [T, d_model], w [H (2 d_v + 2 d_qk), d_model].
+    Returns U, V [T, H, d_v] and Q, K [T, H, d_qk] (float64)."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    h = silu(x @ w.T)
+    T = x.shape[0]
+    cu, cv, cq = num_heads * d_v, 2 * num_heads * d_v, 2 * num_heads * d_v + num_heads * d_qk
+    u = h[:, :cu].reshape(T, num_heads, d_v)
+    v = h[:, cu:cv].reshape(T, num_heads, d_v)
+    q = h[:, cv:cq].reshape(T, num_heads, d_qk)
+    k = h[:, cq:].reshape(T, num_heads, d_qk)
+    return u, v, q, k
+
+
+def hstu_norm_gate(o, u, eps: float = LAYER_NORM_EPS):
+    """Norm(O) ⊙ U: o, u [T, H, d_v]; layer norm over each row's H d_v
+    values (mean 0, variance 1, biased variance, eps inside the root).
+    Returns [T, H d_v] (float64)."""
+    o = np.asarray(o, np.float64)
+    u = np.asarray(u, np.float64)
+    T = o.shape[0]
+    flat = o.reshape(T, -1)
+    mean = flat.mean(axis=1, keepdims=True)
+    var = ((flat - mean) ** 2).mean(axis=1, keepdims=True)
+    return (flat - mean) / np.sqrt(var + eps) * u.reshape(T, -1)
 
 
 # --------------------------------------------------------------------------

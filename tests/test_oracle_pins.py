@@ -872,3 +872,77 @@ def test_sl_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oracle, "sl_select", late_ties)
     with pytest.raises(AssertionError):
         test_sl_selection_matches_brute_force("random_ties")
+
+
+# --------------------------------------------------------------------------
+# HSTU layer steps ([HSTU] §3): projection with SiLU, Norm(O) ⊙ U
+# --------------------------------------------------------------------------
+
+def test_projection_matches_brute_force_and_split_order():
+    rng = np.random.default_rng(41)
+    T, Dm, H, dqk, dv = 5, 6, 2, 3, 4
+    x = rng.standard_normal((T, Dm))
+    w = rng.standard_normal((H * (2 * dv + 2 * dqk), Dm))
+    u, v, q, k = oracle.hstu_projection(x, w, H, dqk, dv)
+    # per-element loop: column c of the projection, SiLU, then the split
+    cols = []
+    for t in range(T):
+        row = []
+        for c in range(w.shape[0]):
+            acc = 0.0
+            for e in range(Dm):
+                acc += x[t, e] * w[c, e]
+            row.append(acc / (1.0 + math.exp(-acc)))
+        cols.append(row)
+    h = np.array(cols)
+    np.testing.assert_allclose(u.reshape(T, -1), h[:, :H * dv], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(v.reshape(T, -1), h[:, H * dv:2 * H * dv], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(q.reshape(T, -1), h[:, 2 * H * dv:2 * H * dv + H * dqk], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(k.reshape(T, -1), h[:, 2 * H * dv + H * dqk:], rtol=1e-12, atol=1e-12)
+    # one-hot input column: each output is SiLU of one weight column
+    e0 = np.zeros((1, Dm)); e0[0, 2] = 1.0
+    uu, vv, qq, kk = oracle.hstu_projection(e0, w, H, dqk, dv)
+    np.testing.assert_allclose(np.concatenate([a.reshape(1, -1) for a in (uu, vv, qq, kk)], axis=1)[0],
+                               oracle.silu(w[:, 2]), rtol=1e-14, atol=1e-14)
+
+
+def test_norm_gate_against_library_layer_norm():
+    import torch
+    rng = np.random.default_rng(42)
+    T, H, dv = 7, 3, 8
+    o = rng.standard_normal((T, H, dv)) * 5 + 2
+    u = rng.standard_normal((T, H, dv))
+    got = oracle.hstu_norm_gate(o, u)
+    ln = torch.nn.functional.layer_norm(torch.from_numpy(o.reshape(T, -1)), (H * dv,), eps=1e-6)
+    np.testing.assert_allclose(got, ln.numpy() * u.reshape(T, -1), rtol=1e-12, atol=1e-12)
+    # invariants: with U = 1 every row has mean 0 and variance var/(var+eps);
+    # a positive scale and a shift of O do not change the result (eps aside)
+    ones = np.ones_like(u)
+    n1 = oracle.hstu_norm_gate(o, ones)
+    np.testing.assert_allclose(n1.mean(axis=1), 0.0, atol=1e-12)
+    var = o.reshape(T, -1).var(axis=1)
+    np.testing.assert_allclose(n1.var(axis=1), var / (var + 1e-6), rtol=1e-12)
+    np.testing.assert_allclose(oracle.hstu_norm_gate(3.0 * o + 7.0, u, eps=0.0), oracle.hstu_norm_gate(o, u, eps=0.0),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_layer_step_planted_mistakes_are_caught(monkeypatch):
+    # a norm over each head instead of the whole row, and U and V swapped
+    def per_head(o, u, eps=1e-6):
+        o = np.asarray(o, np.float64)
+        m = o.mean(axis=2, keepdims=True)
+        va = ((o - m) ** 2).mean(axis=2, keepdims=True)
+        return ((o - m) / np.sqrt(va + eps) * u).reshape(o.shape[0], -1)
+
+    monkeypatch.setattr(oracle, "hstu_norm_gate", per_head)
+    with pytest.raises(AssertionError):
+        test_norm_gate_against_library_layer_norm()
+    orig = ho.hstu_projection
+
+    def swapped(x, w, H, dqk, dv):
+        u, v, q, k = orig(x, w, H, dqk, dv)
+        return v, u, q, k
+
+    monkeypatch.setattr(oracle, "hstu_projection", swapped)
+    with pytest.raises(AssertionError):
+        test_projection_matches_brute_force_and_split_order()
