@@ -21,7 +21,8 @@ Besides the JSON contract fields it reports:
                 history and a micro-batch of 1024 candidates each, candidates
                 only against cached history K/V (candidates/s and TFLOP/s), and
                 Stochastic Length on the skewed batch (selection time, gather
-                GB/s against the HBM peak).
+                GB/s against the HBM peak), and the layer steps around the
+                attention (projection TFLOP/s, norm-gate GB/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --counter-run          (the program profiled for HBM counters)
@@ -329,6 +330,41 @@ def stochastic_length(m, steps):
             "rows_per_s": round(wl.total / ((t_sel + t_gat) * 1e-3), 1)}
 
 
+def layer_steps(m, steps):
+    """The HSTU layer steps around the attention at the 3072-length workload's
+    shape (T = 49152 rows, d_model = 512, H = 4, d = 128, bf16): the projection
+    GEMM with SiLU (2 T d_model N FLOP, N = H (2 d_v + 2 d_qk) = 2048, against
+    the bf16 dense peak) and the norm-gate (reads O and U, writes Y: 3 T H d_v
+    x 2 bytes, against the HBM peak)."""
+    import torch
+    import synth
+    T, Dm, H, d = 49152, 512, 4, 128
+    li = synth.layer_inputs(T, Dm, H, d, d, seed=1007)
+
+    def up(t):
+        import numpy as np
+        return torch.from_numpy(t.raw.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+    x, w = up(li.x), up(li.w)
+    outs = tuple(torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(4))
+    y = torch.empty((T, H * d), dtype=torch.bfloat16, device="cuda")
+
+    def proj():
+        m.layer_projection(x, w, H, d, d, out=outs)
+
+    def gate():
+        m.layer_norm_gate(outs[1], outs[0], out=y)
+
+    t_p = time_loop(proj, steps, 3)
+    t_g = time_loop(gate, steps, 3)
+    fl = 2 * T * Dm * H * 4 * d
+    nbytes = 3 * T * H * d * 2
+    return {"workload": "T=49152, d_model=512, H=4, d=128, bf16", "projection_ms": round(t_p, 4),
+            "projection_tflops": round(fl / t_p / 1e9, 2), "projection_frac_bf16_peak": round(fl / t_p / 1e9 / BF16_PEAK_TFLOPS, 4),
+            "norm_gate_ms": round(t_g, 4), "norm_gate_gbs": round(nbytes / t_g / 1e6, 1),
+            "norm_gate_frac_hbm": round(nbytes / t_g / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(max_seconds=30.0):
     """The float64 oracle, as it stands, on a bounded sample of the 3072-length
     workload: whole sequences (all 4 heads, forward + backward), as many as fit
@@ -518,6 +554,9 @@ def main():
         torch.cuda.empty_cache()
         log("stochastic length on the skewed batch")
         extra["stochastic_length_skewed_alpha1.6"] = stochastic_length(m, args.steps)
+        torch.cuda.empty_cache()
+        log("layer steps (projection, norm-gate)")
+        extra["layer_steps_len3072_shape"] = layer_steps(m, args.steps)
 
     cpu = None
     if not args.no_cpu:

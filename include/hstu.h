@@ -272,6 +272,34 @@ int hstu_gather_rows(const void* in, void* out, int64_t row_bytes,
                      const int64_t* index, const int64_t* count,
                      int64_t max_rows, void* stream);
 
+/* HSTU layer steps either side of the attention (Actions Speak Louder than
+ * Words, §3: pointwise projection, spatial aggregation, pointwise
+ * transformation; the interaction is Norm(A(X)V(X)) ⊙ U(X)).  bf16 in and out,
+ * fp32 accumulation.  The pages name the steps but not their exact form; the
+ * forms built are: the projection is one linear map without bias then SiLU,
+ * split in the order U, V, Q, K; Norm is layer normalisation over a row's
+ * H d_v attention outputs without learned scale or shift.
+ *
+ * Projection: [U V Q K] = SiLU(x wᵀ).
+ *   x  [total_rows, d_model]; d_model a multiple of 64
+ *   w  [H (2 d_v + 2 d_qk), d_model] (a linear layer's weight layout)
+ *   u, v  [total_rows, H, d_v] (written); q, k [total_rows, H, d_qk] (written),
+ *   ready for hstu_jagged_attn_fwd.  H d_v and H d_qk must be multiples of 128
+ *   (else HSTU_EUNSUPPORTED). */
+int hstu_layer_projection(const void* x, const void* w, int64_t total_rows,
+                          int64_t d_model, int64_t num_heads, int64_t d_qk,
+                          int64_t d_v, void* u, void* v, void* q, void* k,
+                          void* stream);
+
+/* Pointwise transformation: y = Norm(o) ⊙ u, row by row.
+ *   o  [total_rows, width] (the attention output [T, H, d_v], width = H d_v)
+ *   u  [total_rows, width]; y [total_rows, width] (written)
+ *   Norm(r) = (r - mean(r)) / sqrt(var(r) + eps), biased variance, statistics
+ *   in fp32; width a multiple of 8, at most 4096. */
+int hstu_layer_norm_gate(const void* o, const void* u, void* y,
+                         int64_t total_rows, int64_t width, double eps,
+                         void* stream);
+
 /* Host helper: the integer bucket edges the kernels use.  Writes NB+1 uint32
  * values to host memory edges_out: edges_out[0] = 0, edges_out[k] = E_k =
  * ceil(2^(32k/NB)) for 1 <= k < NB, edges_out[NB] = 0xFFFFFFFF (sentinel). */
@@ -296,7 +324,9 @@ typedef enum {
   HSTU_KERNEL_REDUCE = 5,   /* sum of the parts of split query tiles (forward or dQ) */
   HSTU_KERNEL_SL = 6,       /* Stochastic Length selection (lengths, then rows) */
   HSTU_KERNEL_GATHER = 7,   /* row gather */
-  HSTU_KERNEL_COUNT = 8
+  HSTU_KERNEL_PROJ = 8,     /* layer projection GEMM with SiLU */
+  HSTU_KERNEL_NORM_GATE = 9,  /* layer norm-gate */
+  HSTU_KERNEL_COUNT = 10
 } hstu_kernel_t;
 int hstu_timing_enable(int on);
 int hstu_timing_reset(void);

@@ -25,7 +25,7 @@ from ._lib import HSTU_BF16, HSTU_FLAG_RECOMPUTE_BWD, HSTU_FLAG_SHARED_SCHEDULE,
 __all__ = [
     "Problem", "HstuError", "HSTU_FLAG_RECOMPUTE_BWD", "HSTU_FLAG_SHARED_SCHEDULE", "problem", "workspace_size", "jagged_attn_fwd",
     "jagged_attn_fwd_targets", "jagged_attn_fwd_noalloc", "jagged_attn_bwd",
-    "cp_reorder", "sl_select", "gather_rows", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
+    "cp_reorder", "sl_select", "gather_rows", "layer_projection", "layer_norm_gate", "bucket_edges", "version", "library_path", "timing_enable", "timing_reset", "timing_read",
 ]
 
 
@@ -232,6 +232,34 @@ def gather_rows(x, index, count, *, out=None):
     row_bytes = x.element_size() * math.prod(x.shape[1:])
     _lib.check(_lib.load().hstu_gather_rows(_ptr(x), _ptr(out), row_bytes, _ptr(index), _ptr(count),
                                             min(int(index.shape[0]), int(out.shape[0])), _stream(x.device)))
+    return out
+
+
+def layer_projection(x, w, num_heads: int, d_qk: int, d_v: int, *, out=None):
+    """[U V Q K] = SiLU(x wᵀ) split per head: x [T, d_model] bf16, w [H (2 d_v +
+    2 d_qk), d_model] bf16.  Returns (u, v, q, k) as [T, H, d] tensors."""
+    torch = _torch()
+    T = int(x.shape[0])
+    if out is None:
+        out = (torch.empty((T, num_heads, d_v), dtype=x.dtype, device=x.device),
+               torch.empty((T, num_heads, d_v), dtype=x.dtype, device=x.device),
+               torch.empty((T, num_heads, d_qk), dtype=x.dtype, device=x.device),
+               torch.empty((T, num_heads, d_qk), dtype=x.dtype, device=x.device))
+    u, v, q, k = out
+    _lib.check(_lib.load().hstu_layer_projection(_ptr(x), _ptr(w), T, int(x.shape[1]), int(num_heads), int(d_qk),
+                                                 int(d_v), _ptr(u), _ptr(v), _ptr(q), _ptr(k), _stream(x.device)))
+    return u, v, q, k
+
+
+def layer_norm_gate(o, u, *, eps: float = 1e-6, out=None):
+    """Norm(o) ⊙ u per row: o, u [T, H, d_v] bf16 (or [T, width]); returns
+    [T, H * d_v]."""
+    torch = _torch()
+    T = int(o.shape[0])
+    width = math.prod(o.shape[1:])
+    if out is None:
+        out = torch.empty((T, width), dtype=o.dtype, device=o.device)
+    _lib.check(_lib.load().hstu_layer_norm_gate(_ptr(o), _ptr(u), _ptr(out), T, width, float(eps), _stream(o.device)))
     return out
 
 

@@ -54,9 +54,11 @@ EXPORTS = [
     "hstu_noalloc_scratch_bytes",
     "hstu_sl_select",
     "hstu_gather_rows",
+    "hstu_layer_projection",
+    "hstu_layer_norm_gate",
 ]
 
-KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4, "reduce": 5, "sl": 6, "gather": 7}
+KERNELS = {"sched": 0, "fwd": 1, "bwd_kv": 2, "bwd_q": 3, "reorder": 4, "reduce": 5, "sl": 6, "gather": 7, "proj": 8, "norm_gate": 9}
 
 _lib = None
 
@@ -97,6 +99,10 @@ def load() -> ctypes.CDLL:
     lib.hstu_sl_select.restype = ctypes.c_int
     lib.hstu_gather_rows.argtypes = [vp, vp, i64, vp, vp, i64, vp]
     lib.hstu_gather_rows.restype = ctypes.c_int
+    lib.hstu_layer_projection.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.hstu_layer_projection.restype = ctypes.c_int
+    lib.hstu_layer_norm_gate.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, vp]
+    lib.hstu_layer_norm_gate.restype = ctypes.c_int
     lib.hstu_bucket_edges.argtypes = [i64, ctypes.POINTER(ctypes.c_uint32)]
     lib.hstu_bucket_edges.restype = ctypes.c_int
     lib.hstu_last_error.argtypes = []

@@ -15,6 +15,7 @@
 #include "attn.h"
 #include "bias.h"
 #include "hstu.h"
+#include "layer.h"
 #include "sl.h"
 
 namespace {
@@ -805,6 +806,66 @@ int hstu_gather_rows(const void* in, void* out, int64_t row_bytes, const int64_t
     return hstu::launch_gather_rows(in, out, row_bytes, index, count, max_rows, vec, cu_count(), s);
   });
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return HSTU_OK;
+}
+
+int hstu_layer_projection(const void* x, const void* w, int64_t total_rows, int64_t d_model, int64_t num_heads,
+                          int64_t d_qk, int64_t d_v, void* u, void* v, void* q, void* k, void* stream) {
+  if (total_rows < 0) return fail(HSTU_EINVAL, "total_rows %lld < 0", (long long)total_rows);
+  if (num_heads < 1 || d_qk < 1 || d_v < 1 || d_model < 1) return fail(HSTU_EINVAL, "sizes must be positive");
+  const int64_t tc = hstu::proj_tile_cols(), tk = hstu::proj_tile_k();
+  if (d_model % tk) return fail(HSTU_EUNSUPPORTED, "d_model %lld is not a multiple of %lld", (long long)d_model, (long long)tk);
+  if ((num_heads * d_v) % tc || (num_heads * d_qk) % tc)
+    return fail(HSTU_EUNSUPPORTED, "H * d_v and H * d_qk must be multiples of %lld", (long long)tc);
+  if (num_heads * (2 * d_v + 2 * d_qk) >= (1ll << 24) || d_model >= (1ll << 24))
+    return fail(HSTU_EUNSUPPORTED, "projection too wide");
+  if (total_rows >= (1ll << 31) / 1) {
+    if (total_rows * d_model >= (1ll << 40)) return fail(HSTU_EUNSUPPORTED, "total_rows * d_model too large");
+  }
+  if (total_rows == 0) return HSTU_OK;
+  CHECK_PTR(x, "x");
+  CHECK_PTR(w, "w");
+  CHECK_PTR(u, "u");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  if ((total_rows + hstu::proj_tile_rows() - 1) / hstu::proj_tile_rows() >= 65536)
+    return fail(HSTU_EUNSUPPORTED, "total_rows %lld too large for the projection grid", (long long)total_rows);
+  hstu::ProjParams pp{};
+  pp.x = x;
+  pp.w = w;
+  pp.out[0] = u;
+  pp.out[1] = v;
+  pp.out[2] = q;
+  pp.out[3] = k;
+  pp.width[0] = pp.width[1] = (int)(num_heads * d_v);
+  pp.width[2] = pp.width[3] = (int)(num_heads * d_qk);
+  pp.T = total_rows;
+  pp.Dm = d_model;
+  pp.N = num_heads * (2 * d_v + 2 * d_qk);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(HSTU_KERNEL_PROJ, s, [&] { return hstu::launch_proj(pp, s); });
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return HSTU_OK;
+}
+
+int hstu_layer_norm_gate(const void* o, const void* u, void* y, int64_t total_rows, int64_t width, double eps,
+                         void* stream) {
+  if (total_rows < 0) return fail(HSTU_EINVAL, "total_rows %lld < 0", (long long)total_rows);
+  if (width < 8 || width % 8) return fail(HSTU_EUNSUPPORTED, "width %lld is not a positive multiple of 8", (long long)width);
+  if (width > hstu::norm_max_width())
+    return fail(HSTU_EUNSUPPORTED, "width %lld > %d", (long long)width, hstu::norm_max_width());
+  if (!(eps >= 0.0) || !(eps < 1.0)) return fail(HSTU_EINVAL, "eps %g not in [0, 1)", eps);
+  if (total_rows >= (1ll << 31)) return fail(HSTU_EUNSUPPORTED, "total_rows too large");
+  if (total_rows == 0) return HSTU_OK;
+  CHECK_PTR(o, "o");
+  CHECK_PTR(u, "u");
+  CHECK_PTR(y, "y");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(HSTU_KERNEL_NORM_GATE, s, [&] {
+    return hstu::launch_norm_gate(o, u, y, total_rows, (int)width, (float)eps, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "norm-gate launch");
   return HSTU_OK;
 }
 

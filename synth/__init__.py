@@ -201,3 +201,22 @@ def custom(lengths, *, num_heads=2, d_qk=32, d_v=32, num_buckets=128, dtype="fp3
     return make_workload("custom", lengths, num_heads=num_heads, d_qk=d_qk, d_v=d_v,
                          num_buckets=num_buckets, dtype=dtype, gap_mean=gap_mean,
                          seed=seed, w_std=w_std, with_dout=with_dout)
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    x: Tensor        # [T, d_model]
+    w: Tensor        # [H (2 d_v + 2 d_qk), d_model]
+    num_heads: int
+    d_qk: int
+    d_v: int
+
+
+def layer_inputs(total_rows: int, d_model: int, num_heads: int, d_qk: int, d_v: int, *, dtype: str = "bf16",
+                 seed: int = 0) -> LayerInputs:
+    """Inputs of the layer steps around the attention: X ~ N(0, 1) and a
+    projection weight ~ N(0, 1 / d_model) (unit-variance outputs)."""
+    rng = np.random.default_rng(seed)
+    x = make_tensor(rng, (total_rows, d_model), dtype)
+    w = make_tensor(rng, (num_heads * (2 * d_v + 2 * d_qk), d_model), dtype, std=1.0 / np.sqrt(d_model))
+    return LayerInputs(x, w, num_heads, d_qk, d_v)

@@ -154,13 +154,13 @@ def test_timing_api_without_launches():
     m.timing_reset()
     m.timing_enable(True)
     m.timing_enable(False)
-    for k in ("sched", "fwd", "bwd_kv", "bwd_q", "reorder", "reduce", "sl", "gather"):
+    for k in ("sched", "fwd", "bwd_kv", "bwd_q", "reorder", "reduce", "sl", "gather", "proj", "norm_gate"):
         assert m.timing_read(k) == (0.0, 0)
     lib = _lib.load()
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.hstu_timing_read(5, ctypes.byref(ms), ctypes.byref(n)) == 0  # the split-sum kernel
-    assert lib.hstu_timing_read(7, ctypes.byref(ms), ctypes.byref(n)) == 0  # the row gather
-    assert lib.hstu_timing_read(8, ctypes.byref(ms), ctypes.byref(n)) == 1  # one past the last id
+    assert lib.hstu_timing_read(9, ctypes.byref(ms), ctypes.byref(n)) == 0  # the norm-gate
+    assert lib.hstu_timing_read(10, ctypes.byref(ms), ctypes.byref(n)) == 1  # one past the last id
     assert lib.hstu_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == 1
 
 
@@ -374,3 +374,21 @@ def test_sl_and_gather_validation():
     assert lib.hstu_gather_rows(g, g, 8, None, g, 4, None) == 1
     assert lib.hstu_gather_rows(g, g, 8, g, None, 4, None) == 1
     assert lib.hstu_gather_rows(g, g, 8, g, g, 0, None) == 0                           # nothing to do
+
+
+def test_layer_step_validation():
+    lib = _lib.load()
+    g = ctypes.c_void_p(1 << 20)
+    P = lib.hstu_layer_projection
+    assert P(g, g, 100, 500, 4, 128, 128, g, g, g, g, None) == 2      # d_model not a multiple of 64
+    assert P(g, g, 100, 512, 1, 64, 64, g, g, g, g, None) == 2        # H d not a multiple of 128
+    assert P(g, g, -1, 512, 4, 128, 128, g, g, g, g, None) == 1
+    assert P(None, g, 100, 512, 4, 128, 128, g, g, g, g, None) == 1
+    assert P(g, g, 100, 512, 4, 128, 128, g, g, ctypes.c_void_p((1 << 20) + 4), g, None) == 1
+    assert P(g, g, 0, 512, 4, 128, 128, None, None, None, None, None) == 0   # nothing to do
+    N = lib.hstu_layer_norm_gate
+    assert N(g, g, g, 10, 12, 1e-6, None) == 2        # width not a multiple of 8
+    assert N(g, g, g, 10, 8192, 1e-6, None) == 2      # wider than a wave holds
+    assert N(g, g, g, 10, 512, -1.0, None) == 1
+    assert N(None, g, g, 10, 512, 1e-6, None) == 1
+    assert N(g, g, g, 0, 512, 1e-6, None) == 0        # nothing to do
