@@ -146,16 +146,16 @@ def kernel_flops(pairs, heads, dqk, dv):
             "bwd_q": 2 * dqk * pairs * heads}
 
 
+ATTN_SOURCES = ("api.hip", "attn.h", "attn.hip", "bias.h", "common.h", "sched.hip", "swtile.h")
+
+
 def source_digest():
-    """sha256 over the sources of the kernels the counter summary covers (to
-    tell whether stored counters are current); the reorder kernel is not one of
-    them."""
-    import glob
+    """sha256 over the sources of the attention kernels and their launches (to
+    tell whether the stored counters of those kernels are current)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "jagged_hstu_attention_amd", "csrc")
-    files = glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))
-    for f in sorted(f for f in files if os.path.basename(f) != "reorder.hip"):
+    for f in sorted(os.path.join(csrc, n) for n in ATTN_SOURCES):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
@@ -182,7 +182,8 @@ COUNTER_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o <name>
 # Substrings of the kernel symbols (for bf16 with d >= 64 the backward runs
 # bwd_kv_half_kernel and bwd_q_g_kernel, otherwise bwd_kv_kernel and
 # bwd_q_kernel).
-KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_", "bwd_q": "bwd_q_", "sched": "sched_kernel"}
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_", "bwd_q": "bwd_q_", "sched": "sched_kernel",
+                  "reorder": "reorder_kernel"}
 
 
 def traffic_summary(fetch_csv, write_csv, out_path):
@@ -213,6 +214,81 @@ def traffic_summary(fetch_csv, write_csv, out_path):
         json.dump(out, f, indent=1)
         f.write("\n")
     return out
+
+
+def profile_workload(m, name, steps, warmup):
+    """W warmup steps, then K steps timed per kernel with the library's HIP
+    events (the program rocprofv3 traces; its last K dispatches of each
+    kernel are the timed ones)."""
+    import torch
+    import synth
+    if name == "len3072":
+        wl = synth.config("bf16_len3072")
+    elif name == "skewed":
+        wl = synth.config("skewed_powerlaw")
+    else:  # the skewed batch's head shape on uniform lengths: 16 x 3072, H = 8, d = 64, 256 buckets
+        wl = synth.custom([3072] * 16, num_heads=8, d_qk=64, d_v=64, num_buckets=256, dtype="bf16",
+                          gap_mean=600.0, seed=1008)
+    case = Case(wl)
+    for _ in range(warmup):
+        case.step()
+    kms = time_kernels(case, steps)
+    pairs = causal_pairs(wl.lengths)
+    kfl = kernel_flops(pairs, wl.num_heads, wl.d_qk, wl.d_v)
+    torch.cuda.synchronize()
+    return {"profile": name, "warmup": warmup, "steps": steps, "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+            "kernels_tflops": {k: round(kfl[k] / kms[k] / 1e9, 2) for k in kfl if kms.get(k)},
+            "pairs": pairs, "heads": wl.num_heads, "d": wl.d_qk}
+
+
+def trace_summary(path, last):
+    """Average duration (us) of the last `last` dispatches of each kernel in a
+    rocprofv3 kernel_trace.csv, next to the average over all of them."""
+    import csv
+    import re
+    rows = list(csv.DictReader(open(path)))
+    by = {}
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+        name = re.sub(r"\(.*", "", r["Kernel_Name"])[:80]
+        by.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    return {k: {"dispatches": len(v), "avg_us_all": round(sum(v) / len(v), 2),
+                f"avg_us_last_{min(last, len(v))}": round(sum(v[-last:]) / len(v[-last:]), 2)}
+            for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1]))}
+
+
+def balance_model(name):
+    """Longest-first (descending cost, each item to the earliest-free slot)
+    schedule of the attention items, from the scheduler's cost rules: a
+    (128-row query tile, head) item costs the 64-key tiles of its causal
+    prefix (forward, dQ); a (128-key tile, head) item costs the 64-row query
+    steps from its first key on (dK/dV).  Slots: 512 for the forward and dQ
+    passes (two workgroups per compute unit at d = 128; three for the d = 64
+    forward), 256 for the dK/dV pass."""
+    import heapq
+    import synth
+    wl = synth.config("bf16_len3072" if name == "len3072" else "skewed_powerlaw", with_dout=False)
+    H = wl.num_heads
+    q_items, k_items = [], []
+    for L in map(int, wl.lengths):
+        for i in range(0, L, 128):
+            q_items += [(min(i + 128, L) + 63) // 64] * H
+        for k0 in range(0, L, 128):
+            k_items += [(L - k0 + 63) // 64] * H
+
+    def lpt(costs, slots):
+        heap = [0] * slots
+        for c in sorted(costs, reverse=True):
+            t = heapq.heappop(heap)
+            heapq.heappush(heap, t + c)
+        makespan = max(heap)
+        mean = sum(costs) / slots
+        return {"items": len(costs), "slots": slots, "total_cost": sum(costs), "max_item": max(costs),
+                "makespan": makespan, "mean_load": round(mean, 2), "makespan_over_mean": round(makespan / mean, 4)}
+
+    fwd_slots = 768 if wl.d_qk <= 64 else 512
+    return {"workload": name, "lengths": {"B": len(wl.lengths), "max": int(max(wl.lengths)),
+                                          "sum": int(sum(wl.lengths))},
+            "forward": lpt(q_items, fwd_slots), "dq": lpt(q_items, 512), "dkdv": lpt(k_items, 256)}
 
 
 def time_kernels(case, steps):
@@ -443,10 +519,26 @@ def main():
     ap.add_argument("--counter-run", action="store_true",
                     help="for rocprofv3 --pmc: a 256 MiB device copy (calibration), then 3 forward+backward "
                          "steps of the 3072-length workload; no timing")
+    ap.add_argument("--profile", choices=["len3072", "skewed", "uniform_d64"],
+                    help="for rocprofv3 --kernel-trace: W warmup then K timed steps of one workload (one schedule "
+                         "per step); prints the per-kernel HIP-event averages of the timed steps as JSON")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="CPU only: per-kernel average duration of the last --last dispatches of each kernel in a "
+                         "rocprofv3 kernel_trace.csv")
+    ap.add_argument("--last", type=int, default=20)
+    ap.add_argument("--balance-model", choices=["len3072", "skewed"],
+                    help="CPU only: longest-first schedule of the attention work items over the workgroup slots "
+                         "(makespan against the mean load), from the scheduler's cost rules")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="CPU only: turn the two --pmc counter CSVs of --counter-run into "
                          "profiles/traffic_len3072.json and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary, args.last), indent=1))
+        return
+    if args.balance_model:
+        print(json.dumps(balance_model(args.balance_model), indent=1))
+        return
     if args.traffic_summary:
         t = traffic_summary(*args.traffic_summary, os.path.join(ROOT, "profiles", "traffic_len3072.json"))
         print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk.endswith("bytes")}
@@ -472,7 +564,22 @@ def main():
         for _ in range(3):
             case.step()
         torch.cuda.synchronize()
+        del case, dst
+        torch.cuda.empty_cache()
+        # the chunk-pair reorder of the CP=8 length-16384 bf16 tensor, on 5
+        # rotating buffer pairs (640 MiB, past the last-level cache), 3 passes
+        off = torch.from_numpy(synth.offsets_from_lengths([16384] * 4)).cuda()
+        bufs = [(torch.randn(65536, 4, 128, device="cuda").to(torch.bfloat16),
+                 torch.empty(65536, 4, 128, dtype=torch.bfloat16, device="cuda")) for _ in range(5)]
+        seg = torch.empty(8 * 4 + 1, dtype=torch.int64, device="cuda")
+        for _ in range(3):
+            for a, b in bufs:
+                m.cp_reorder(a, off, 16384, 8, out=b, out_offsets=seg)
+        torch.cuda.synchronize()
         print(json.dumps({"counter_run": True, "copy_bytes": src.numel()}), flush=True)
+        return
+    if args.profile:
+        print(json.dumps(profile_workload(m, args.profile, args.steps, args.warmup)), flush=True)
         return
     log("uploading the 3072-length workload")
     wl = synth.config("bf16_len3072")
