@@ -44,26 +44,28 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(const char* __
                                                                   int64_t rb, const int64_t* __restrict__ offsets,
                                                                   int64_t B, int64_t T, int64_t C, int inverse,
                                                                   int64_t* __restrict__ out_offsets) {
-  __shared__ int64_t start_s;
+  __shared__ int64_t wave_part[kReorderThreads / 64];
   const int64_t pair = blockIdx.x;
   const int64_t r = pair / B, b = pair % B;
   const int64_t nch = 2 * C;
   const int tid = threadIdx.x;
 
   // Start of segment (r, b) in the rank-major layout: all rows of ranks < r,
-  // plus rank r's rows of sequences < b (a short serial sum: B is the number
-  // of sequences, and the copy below dominates).
-  if (tid == 0) {
-    int64_t part = 0;
-    for (int64_t bb = 0; bb < B; ++bb) {
-      const int64_t Lb = offsets[bb + 1] - offsets[bb];
-      part += rows_before_rank(Lb, r, nch);
-      if (bb < b) part += pair_rows(Lb, r, nch);
-    }
-    start_s = part;
+  // plus rank r's rows of sequences < b.  The workgroup sums the sequences
+  // with a stride (each thread B / 256 of them), then reduces across waves.
+  int64_t part = 0;
+  for (int64_t bb = tid; bb < B; bb += kReorderThreads) {
+    const int64_t Lb = offsets[bb + 1] - offsets[bb];
+    part += rows_before_rank(Lb, r, nch);
+    if (bb < b) part += pair_rows(Lb, r, nch);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  if ((tid & 63) == 0) wave_part[tid >> 6] = part;
   __syncthreads();
-  const int64_t start = start_s;
+  int64_t start = 0;
+#pragma unroll
+  for (int w = 0; w < kReorderThreads / 64; ++w) start += wave_part[w];
 
   const int64_t o0 = offsets[b];
   const int64_t L = offsets[b + 1] - o0;
