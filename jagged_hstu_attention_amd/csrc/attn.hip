@@ -743,32 +743,39 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
 // ---------------------------------------------------------------------------
 namespace {
 
-// Transpose-read offsets of the d blocks in this wave's half.
-template <int D> struct HalfTrOffsets {
-  static constexpr int kBlocks = D / 64;  // 32-column d blocks per half
-  int tr[kBlocks][2];
-  __device__ __forceinline__ void init(int lane, int hf) {
+// Per-lane LDS byte offsets of the tile reads of this kernel, compressed: the
+// swizzle puts the row read of contraction slice kk at row0 ^ (kk << 5), the
+// transpose read of d block j at tr0[h] ^ (j << 6), and rows 16 apart at a
+// constant distance (D = 64 and 128).  The kernel passes the three registers
+// through an empty asm statement at every step, so that the compiler derives
+// the offsets there instead of keeping each of them in a register of its own
+// for the whole kernel.
+struct HalfOffsets {
+  int row0;
+  int tr0[2];
+  template <int D> __device__ __forceinline__ void init(int lane) {
     using S = SwTile<__bf16, D>;
-    const int g = lane >> 5, m = lane & 15, q = lane >> 4;
+    const int r32 = lane & 31, g = lane >> 5, m = lane & 15, q = lane >> 4;
+    row0 = 2 * S::off(r32, 8 * g);
     const int rb = 4 * g + (m >> 2), cb = 16 * (q & 1) + 4 * (m & 3);
-#pragma unroll
-    for (int j = 0; j < kBlocks; ++j)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) tr[j][h] = 2 * S::off(rb + 8 * h, (hf * kBlocks + j) * 32 + cb);
+    tr0[0] = 2 * S::off(rb, cb);
+    tr0[1] = 2 * S::off(rb + 8, cb);
   }
+  __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(row0), "+v"(tr0[0]), "+v"(tr0[1])); }
 };
 
 // out[j] += Xᵀ (d block j of the half) B over the 32 rows of block blk of a
 // bf16 tile; B is the pair of packed bf16x8 operands of the block.
 template <int D>
-__device__ __forceinline__ void contract_half(f32x16* out, const char* __restrict__ base, const HalfTrOffsets<D>& to,
+__device__ __forceinline__ void contract_half(f32x16* out, const char* __restrict__ base, const HalfOffsets& o, int hf,
                                               const u32x4* b, int blk) {
 #pragma unroll
   for (int j = 0; j < D / 64; ++j)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const char* p0 = base + to.tr[j][0] + (blk * 32 + 16 * u) * D * 2;
-      const char* p1 = base + to.tr[j][1] + (blk * 32 + 16 * u) * D * 2;
+      const int jj = hf * (D / 64) + j;  // d block of the head
+      const char* p0 = base + (o.tr0[0] ^ (jj << 6)) + (blk * 32 + 16 * u) * D * 2;
+      const char* p1 = base + (o.tr0[1] ^ (jj << 6)) + (blk * 32 + 16 * u) * D * 2;
       const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
       const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
       const short __attribute__((ext_vector_type(8))) a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
@@ -782,20 +789,21 @@ __device__ __forceinline__ void contract_half(f32x16* out, const char* __restric
 template <int D>
 __device__ __forceinline__ void sdp_products(f32x16& s, f32x16& dp, const char* __restrict__ qb,
                                              const char* __restrict__ db, const char* __restrict__ vb,
-                                             const LaneOffsets<D>& lo, int blk, int vblk, const bf16x8* kop) {
+                                             const HalfOffsets& o, int blk, int vblk, const bf16x8* kop) {
   s = f32x16{};
   dp = f32x16{};
   const int qo = blk * 32 * D * 2, vo = vblk * 32 * D * 2;
-  u32x4 qa = *reinterpret_cast<const u32x4*>(qb + lo.row[0] + qo);
-  u32x4 da = *reinterpret_cast<const u32x4*>(db + lo.row[0] + qo);
-  u32x4 va = *reinterpret_cast<const u32x4*>(vb + lo.row[0] + vo);
+  u32x4 qa = *reinterpret_cast<const u32x4*>(qb + o.row0 + qo);
+  u32x4 da = *reinterpret_cast<const u32x4*>(db + o.row0 + qo);
+  u32x4 va = *reinterpret_cast<const u32x4*>(vb + o.row0 + vo);
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 qn = qa, dn = da, vn = va;
     if (kk + 1 < D / 16) {
-      qn = *reinterpret_cast<const u32x4*>(qb + lo.row[kk + 1] + qo);
-      dn = *reinterpret_cast<const u32x4*>(db + lo.row[kk + 1] + qo);
-      vn = *reinterpret_cast<const u32x4*>(vb + lo.row[kk + 1] + vo);
+      const int r = o.row0 ^ ((kk + 1) << 5);
+      qn = *reinterpret_cast<const u32x4*>(qb + r + qo);
+      dn = *reinterpret_cast<const u32x4*>(db + r + qo);
+      vn = *reinterpret_cast<const u32x4*>(vb + r + vo);
     }
     s = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, qa), kop[kk], s);
     dp = Mma<__bf16>::mma(__builtin_bit_cast(bf16x8, da), __builtin_bit_cast(bf16x8, va), dp);
@@ -813,15 +821,6 @@ __device__ __forceinline__ void pack16(u32x4* dst, const float* v) {
                    pack_bf16x2(v[8 * u + 4], v[8 * u + 5]), pack_bf16x2(v[8 * u + 6], v[8 * u + 7])};
 }
 
-// SiLU and its gradient for one element: P = a' (scaled SiLU) and G.
-__device__ __forceinline__ void silu_grad(float s, float dp, float beta, float c, float& a, float& gg) {
-  const float y = fmaf(s, beta, c);
-  const float sg = sigmoid_y(y);
-  a = y * sg;
-  const float u = fmaf(-a, sg, a);  // a' (1 - sigma)
-  gg = dp * fmaf(u, kNegLn2, sg);
-}
-
 // Elementwise part of an unmasked step under a plan mode (kModeConst, Thr1,
 // Thr3): each element's bias by compares of the other row's timestamp offset
 // (rows[], this lane's four-row runs) with the lane's thresholds, SiLU and its
@@ -835,32 +834,58 @@ __device__ __forceinline__ void pair_plan(u32x4* own_p, u32x4* own_g, float* dw4
                                           float c3, int32_t t1, int32_t t2, int32_t t3) {
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
   float pa[16], pg[16];
+  // Runs of four values, each computed stage by stage (the four bias
+  // selections, then the four fmas, the four exponentials, ...) with the
+  // scheduler held to that order: four independent chains hide the latency
+  // of the transcendental steps, which one chain at a time would expose.
+  int4 rv[4] = {};  // the other rows' timestamp offsets, all read up front
+  if constexpr (MODE != kModeConst)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) rv[q4] = *reinterpret_cast<const int4*>(rows + q4 * 8);
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    int4 v4 = {0, 0, 0, 0};
-    if constexpr (MODE != kModeConst) v4 = *reinterpret_cast<const int4*>(rows + q4 * 8);
-    const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+    const int32_t vv[4] = {rv[q4].x, rv[q4].y, rv[q4].z, rv[q4].w};
+    float c[4], y[4], t[4], a[4], h[4];
+    bool p1[4] = {false, false, false, false}, p2[4] = {false, false, false, false},
+         p3[4] = {false, false, false, false};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = c0;
+      if constexpr (MODE != kModeConst) {
+        p1[e] = vv[e] <= t1;
+        c[e] = p1[e] ? c1 : c[e];
+      }
+      if constexpr (MODE == kModeThr3) {
+        p2[e] = vv[e] <= t2;
+        p3[e] = vv[e] <= t3;
+        c[e] = p2[e] ? c2 : c[e];
+        c[e] = p3[e] ? c3 : c[e];
+      }
+      y[e] = fmaf(s[4 * q4 + e], beta, c[e]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = __builtin_amdgcn_exp2f(y[e]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = __builtin_amdgcn_rcpf(1.0f + t[e]);  // sigma
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = y[e] * t[e];
+      h[e] = fmaf(fmaf(-a[e], t[e], a[e]), kNegLn2, t[e]);  // a' (1 - sigma) (-ln 2) + sigma
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * q4 + e;
-      float c = c0;
-      bool p1 = false, p2 = false, p3 = false;
-      if constexpr (MODE != kModeConst) {
-        p1 = vv[e] <= t1;
-        c = p1 ? c1 : c;
-      }
-      if constexpr (MODE == kModeThr3) {
-        p2 = vv[e] <= t2;
-        p3 = vv[e] <= t3;
-        c = p2 ? c2 : c;
-        c = p3 ? c3 : c;
-      }
-      silu_grad(s[i], dp[i], beta, c, pa[i], pg[i]);
+      pa[i] = a[e];
+      pg[i] = dp[i] * h[e];
       s0 += pg[i];
-      if constexpr (MODE != kModeConst) s1 += p1 ? pg[i] : 0.0f;
+      if constexpr (MODE != kModeConst) s1 += p1[e] ? pg[i] : 0.0f;
       if constexpr (MODE == kModeThr3) {
-        s2 += p2 ? pg[i] : 0.0f;
-        s3 += p3 ? pg[i] : 0.0f;
+        s2 += p2[e] ? pg[i] : 0.0f;
+        s3 += p3[e] ? pg[i] : 0.0f;
       }
     }
   }
@@ -887,43 +912,96 @@ __device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dw
   float pa[16], pg[16];
   int cur = 0;        // bucket of the running d(ts_weights) sum
   float run = 0.0f;   // the running sum
+  // row r0 + e = 8 q4 + e + 4g is visible iff 8 q4 + e lies in [lo_g, hi_g)
+  // (the compile-time part compared with two lane values)
+  const int lo_g = lo_row - 4 * g, hi_g = hi_row - 4 * g;
+  // Runs of four values, stage by stage (as in pair_plan): the four table
+  // lookups of the buckets are in flight together, then the four bias
+  // values, then the four SiLU chains.
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int r0 = q4 * 8 + 4 * g;
-    int4 v4 = {0, 0, 0, 0};
-    if constexpr (!WIDE) v4 = *reinterpret_cast<const int4*>(ts.un[0] + blk * 32 + r0);
-    const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+    uint32_t m[4];
+    bool far[4] = {false, false, false, false};  // |delta| >= 2^32: the last bucket
+    if constexpr (WIDE) {
+      const longlong2* t = reinterpret_cast<const longlong2*>(ts.t64 + blk * 32 + r0);
+      const longlong2 a0 = t[0], a1 = t[1];
+      const int64_t w64[4] = {a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t d = w64[e] - tsr64;
+        const uint64_t am = d < 0 ? (uint64_t)(-d) : (uint64_t)d;
+        far[e] = (am >> 32) != 0;
+        m[e] = (uint32_t)am;
+      }
+    } else {
+      const int4 v4 = *reinterpret_cast<const int4*>(ts.un[0] + blk * 32 + r0);
+      const int32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int32_t d = vv[e] - tsr;
+        m[e] = (uint32_t)(d < 0 ? -d : d);
+      }
+    }
+    // exact bucket: table entry {E, b} of the leading-zero count and the
+    // five bits after the leading one; bucket = b + [m >= E] (buckets of 0
+    // and 1 agree)
+    u32x2 L[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[e] = m[e] > 1u ? m[e] : 1u;
+      const int z = __builtin_clz(m[e]);
+      L[e] = bl.lut[(z << 5) | (int)(((m[e] << z) >> 26) & 31u)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int b[4];
+    float c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      b[e] = far[e] ? nb - 1 : (int)L[e].y + (m[e] >= L[e].x ? 1 : 0);
+      c[e] = bl.c[b[e]];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float y[4], t[4], a[4], h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = fmaf(s[4 * q4 + e], beta, c[e]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = __builtin_amdgcn_exp2f(y[e]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = __builtin_amdgcn_rcpf(1.0f + t[e]);  // sigma
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = y[e] * t[e];
+      h[e] = fmaf(fmaf(-a[e], t[e], a[e]), kNegLn2, t[e]);  // a' (1 - sigma) (-ln 2) + sigma
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * q4 + e;
-      int b;
-      if constexpr (WIDE) {
-        b = lut_bucket64(ts.t64[blk * 32 + r0 + e] - tsr64, nb, bl.lut);
-      } else {
-        const int32_t d = vv[e] - tsr;
-        b = lut_bucket((uint32_t)(d < 0 ? -d : d), bl.lut);
-      }
-      float a, gg;
-      silu_grad(s[i], dp[i], beta, bl.c[b], a, gg);
+      float av = a[e], gg = dp[i] * h[e];
+      int bb = b[e];
       if constexpr (MASKED) {
-        const bool vis = r0 + e >= lo_row && r0 + e < hi_row;
-        a = vis ? a : 0.0f;
+        const bool vis = q4 * 8 + e >= lo_g && q4 * 8 + e < hi_g;
+        av = vis ? av : 0.0f;
         gg = vis ? gg : 0.0f;
-        if (i > 0) b = vis ? b : cur;  // a masked element never ends a run
+        if (i > 0) bb = vis ? bb : cur;  // a masked element never ends a run
       }
-      pa[i] = a;
+      pa[i] = av;
       pg[i] = gg;
       // d(ts_weights): a lane's rows come in order and their bucket changes
       // rarely, so each lane keeps a running sum per bucket and adds it to
       // the bins when the bucket changes (one atomic per element would make
       // the lanes that share a bucket collide on one address)
       if (i == 0) {
-        cur = b;
+        cur = bb;
         run = gg;
       } else {
-        if (b != cur) {
+        if (bb != cur) {
           atomicAdd(&dwl[cur], run);
-          cur = b;
+          cur = bb;
           run = 0.0f;
         }
         run += gg;
@@ -972,10 +1050,8 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave & 3, hf = wave >> 2;
-  LaneOffsets<D> lo;
-  lo.init(lane);
-  HalfTrOffsets<D> to;
-  to.init(lane, hf);
+  HalfOffsets ofs;
+  ofs.init<D>(lane);
   const int H = p.H, NB = p.NB;
   const int64_t ld = (int64_t)H * D;
   // waves 4-7 load the query/dO tiles (their LDS bin updates are deferred past
@@ -1052,6 +1128,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     const int key_lo = it.pos0 + kg * 32;  // first key of this wave
     int cur = 0;
     while (si.valid()) {
+      ofs.opaque();
       const int q0 = si.q0;
       const int nq = si.nq();
       StepIter nx = si;
@@ -1084,7 +1161,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
       int blo = 0;
       if (live) {
         f32x16 s, dp;
-        sdp_products<D>(s, dp, qb, db, vb, lo, hf, kg, kop);
+        sdp_products<D>(s, dp, qb, db, vb, ofs, hf, kg, kop);
         // rows of the V tile past the item's end repeat its last row: a key
         // lane past the end must have dP = 0 (so G and its d(ts_weights)
         // contributions vanish)
@@ -1119,15 +1196,15 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
       if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cur ^ 1], tsv, nx.nq(), lane, base);
       __syncthreads();
       if (live) {
-        contract_half<D>(dvacc, db, to, own_p, hf);
-        contract_half<D>(dkacc, qb, to, own_g, hf);
+        contract_half<D>(dvacc, db, ofs, hf, own_p, hf);
+        contract_half<D>(dkacc, qb, ofs, hf, own_g, hf);
       }
       if (par_live) {
         const int pw = wave ^ 4;
         const u32x4 par_p[2] = {xch[pw][0][lane], xch[pw][1][lane]};
         const u32x4 par_g[2] = {xch[pw][2][lane], xch[pw][3][lane]};
-        contract_half<D>(dvacc, db, to, par_p, hf ^ 1);
-        contract_half<D>(dkacc, qb, to, par_g, hf ^ 1);
+        contract_half<D>(dvacc, db, ofs, hf, par_p, hf ^ 1);
+        contract_half<D>(dkacc, qb, ofs, hf, par_g, hf ^ 1);
       }
       if (p.g && wave < 4) {
         // stored G, written after the products (the loading waves wait for
