@@ -1081,6 +1081,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     const int64_t base = p.ts[seq0];
     const int kj = kg * 32 + r32;
     const bool kvalid = kj < it.n;
+    const bool partial_keys = 32 * kg + 32 > it.n;  // some key lane of the wave lies past the item's end
     const int kpos = it.pos0 + kj;
     const int64_t krow = (int64_t)it.row0 + kj;
     const int64_t tsk = kvalid ? p.ts[krow] : 0;
@@ -1164,8 +1165,9 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         sdp_products<D>(s, dp, qb, db, vb, ofs, hf, kg, kop);
         // rows of the V tile past the item's end repeat its last row: a key
         // lane past the end must have dP = 0 (so G and its d(ts_weights)
-        // contributions vanish)
-        if (!kvalid) dp = f32x16{};
+        // contributions vanish).  Only a wave whose keys run past the end of
+        // the item has such lanes (a wave-uniform test).
+        if (partial_keys && !kvalid) dp = f32x16{};
         if (masked) {
           if (fast)
             pair_exact<false, true>(own_p, own_g, dwl, s, dp, ts, hf, g, beta, lt.rel, tsk, bl, NB, lo_row, hi_row);
@@ -1192,6 +1194,10 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         xch[wave][1][lane] = own_p[1];
         xch[wave][2][lane] = own_g[0];
         xch[wave][3][lane] = own_g[1];
+      } else if (p.g) {
+        // a block that is not live stores zeros as its G
+        xch[wave][2][lane] = u32x4{};
+        xch[wave][3][lane] = u32x4{};
       }
       if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cur ^ 1], tsv, nx.nq(), lane, base);
       __syncthreads();
@@ -1215,15 +1221,13 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         // stores one 16-byte chunk (8 rows of one key) and each key's 64 rows
         // are one 128-byte line: chunk c of key r holds rows 8c .. 8c+7, whose
         // halves sit with lanes (r, g = 0) and (r, g = 1) as run c % 4 of
-        // their values.  Written once and read once: streamed past the caches.
+        // their values (a block that is not live left zeros in its slots).
+        // Written once and read once: streamed past the caches.
         const int gi = q0 / kGRows;
         const int64_t gidx = gbase + (int64_t)gi * (gi + 1) + gkt;
         if (gidx < p.g_blocks) {
           char* gb = reinterpret_cast<char*>(p.g) + gidx * kGBlockBytes;
           const int c = lane >> 3, j = c & 3;
-          // all ones where this lane's block is live (masks rather than a
-          // select, which the compiler turns into branches)
-          const uint32_t keep = c < 4 ? (live ? ~0u : 0u) : (par_live ? ~0u : 0u);
           const char* x = reinterpret_cast<const char*>(&xch[c < 4 ? wave : wave ^ 4][2 + (j >> 1)][0]) + 8 * (j & 1);
           // the eight reads issued together (in bounds whether or not the
           // block is live), then the four stores
@@ -1237,7 +1241,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int row = gk0 + 8 * k + (lane & 7), col = q0 % kGRows + 8 * c;
-            const u32x4 v = u32x4{lo[k][0], lo[k][1], hi[k][0], hi[k][1]} & keep;
+            const u32x4 v = u32x4{lo[k][0], lo[k][1], hi[k][0], hi[k][1]};
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(gb + (row * kGRows + col) * 2));
           }
         }
