@@ -221,6 +221,36 @@ def test_all_sequences_empty():
     assert float(dw.abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("dtype,dim,recompute", [("bf16", 64, False), ("bf16", 128, True), ("fp32", 32, False)])
+def test_many_short_sequences(dtype, dim, recompute):
+    # more sequences than the scheduler has threads (its scans and offset
+    # arrays run over several chunks), lengths 0..40 with empty and
+    # single-token sequences, tiles that span no sequence boundary
+    rng = np.random.default_rng(2024 + dim)
+    lengths = [int(x) for x in rng.integers(0, 41, size=3000)]
+    lengths[:4] = [0, 1, 40, 0]
+    wl = synth.custom(lengths, num_heads=2, d_qk=dim, d_v=dim, num_buckets=128, dtype=dtype, gap_mean=3600.0,
+                      seed=dim + 7, w_std=0.5)
+    d = upload(wl)
+    assert_close(to_f64(run_fwd(wl, d)), oracle_fwd(wl), dtype, "out")
+    got = hstu().jagged_attn_bwd(d["dout"], d["q"], d["k"], d["v"], d["offsets"], d["ts"], d["w"], wl.max_seq_len,
+                                 recompute=recompute)
+    for name, g, ref in zip(("dq", "dk", "dv", "dw"), got, oracle_bwd(wl)):
+        assert_close(to_f64(g), ref, dtype, name)
+
+
+def test_one_sequence_of_the_maximum_length():
+    # a single sequence of length 8192 (the longest of the skewed batch's
+    # range), every element of O, dQ, dK, dV and d(ts_weights)
+    wl = synth.custom([8192], num_heads=2, d_qk=128, d_v=128, num_buckets=128, dtype="bf16", gap_mean=3600.0,
+                      seed=8192, w_std=0.5)
+    d = upload(wl)
+    assert_close(to_f64(run_fwd(wl, d)), oracle_fwd(wl), "bf16", "out")
+    got = run_bwd(wl, d)
+    for name, g, ref in zip(("dq", "dk", "dv", "dw"), got, oracle_bwd(wl)):
+        assert_close(to_f64(g), ref, "bf16", name)
+
+
 def _wide_timestamp_workload(dtype, dim, seed):
     # one sequence with ordinary gaps next to sequences whose timestamps span
     # more than 2^32 (|ts - first| past 2^30 takes the 64-bit path; pairs with
