@@ -100,7 +100,6 @@ template <int D> struct TileOps<float, D> {
 template <typename T, int D> struct alignas(16) KvSmem {
   T k[2][BN * D];
   T v[2][BN * D];
-  TsTile<BN> ts[2];
 };
 
 template <typename T, int D, int NT = kThreads>
@@ -320,13 +319,13 @@ __device__ __forceinline__ void fwd_tile(f32x16* oacc, const T* kt, const T* vt,
     }
     float cb[16];
     block_bias_mode<+1, BN, false, MASK>(cb, nullptr, mode, pl, ln.tsr, ln.ts64, ts, blk, ln.g, bl, ln.nb);
+    if (blk == 1) mid();
     float pv[16];
     silu_block<MASK>(pv, s, cb, ln.beta, ln.lim - 32 * blk, ln.hlim - 32 * blk, ln.g);
     if constexpr (sizeof(T) == 2)
       tr_mma<D>(oacc, tv, pv);
     else
       ops.contract(oacc, vt, pv, blk);
-    if (blk == 0) mid();
   }
 }
 
@@ -341,6 +340,7 @@ __global__ __launch_bounds__(kThreads, (kFwdBlocks<T, D>)) void fwd_kernel(const
   using M = Mma<T>;
   using op_t = typename M::operand;
   __shared__ KvSmem<T, D> sm;
+  __shared__ TsTile<BN> tsm[2];
   __shared__ BiasLds bl;
   __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
@@ -401,16 +401,26 @@ __global__ __launch_bounds__(kThreads, (kFwdBlocks<T, D>)) void fwd_kernel(const
     ln.nb = NB;
     ln.ts64 = tsq;
     ln.tsr = lt.rel;
-    int64_t tsv = 0;
     // key tile at position pos of the walk; the item covers positions
     // [it.w0, it.w1) (the whole walk unless the tile is split)
     const auto walk = [&](int pos) { return pos < ht ? pos : d0 + (pos - ht); };
+    // wave 0 reads the timestamps of a tile one step before it stages them
+    // (half-way through the tile before), so staging never waits for the
+    // tile loads in flight
+    const auto tile_ts = [&](int pos) {
+      const int k0 = walk(pos) * BN;
+      return p.ts[seq0 + k0 + min(lane, min(BN, kv_len - k0) - 1)];
+    };
+    int64_t tsv = 0;
     int kt = walk(it.w0);
     {
       const int nv0 = min(BN, kv_len - kt * BN);
       issue_kv<T, D>(sm, 0, Kh, Vh, ld, kt * BN, nv0, tid, lane_off);
-      if (wave == 0) tsv = p.ts[seq0 + kt * BN + min(lane, nv0 - 1)];
-      if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, nv0, lane, base);
+      if (wave == 0) {
+        const int64_t t0 = tile_ts(it.w0);
+        if (it.w0 + 1 < it.w1) tsv = tile_ts(it.w0 + 1);
+        ts_tile_fill<BN>(tsm[0], t0, nv0, lane, base);
+      }
     }
     wait_loads();
     __syncthreads();
@@ -421,17 +431,16 @@ __global__ __launch_bounds__(kThreads, (kFwdBlocks<T, D>)) void fwd_kernel(const
       const int nkt = walk(pos + 1);
       const bool more = pos + 1 < it.w1;
       const int nk0 = nkt * BN, nnv = more ? min(BN, kv_len - nk0) : 0;
+      int64_t tsn = 0;
       if (more) {
-        // the timestamps first: they are staged half-way through the tile
-        // (below), where waiting for them leaves the tile loads in flight
-        if (wave == 0) tsv = p.ts[seq0 + nk0 + min(lane, nnv - 1)];
+        if (wave == 0 && pos + 2 < it.w1) tsn = tile_ts(pos + 2);
         __builtin_amdgcn_sched_barrier(0);
         issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
       }
       const auto stage = [&] {
-        if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, nnv, lane, base);
+        if (more && wave == 0) ts_tile_fill<BN>(tsm[cur ^ 1], tsv, nnv, lane, base);
       };
-      const TsTile<BN>& ts = sm.ts[cur];
+      const TsTile<BN>& ts = tsm[cur];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       ln.lim = qpos - key0;
@@ -446,6 +455,7 @@ __global__ __launch_bounds__(kThreads, (kFwdBlocks<T, D>)) void fwd_kernel(const
       wait_loads();
       __syncthreads();
       kt = nkt;
+      tsv = tsn;
     }
     if (qvalid) {
       if (it.slot < 0)
@@ -597,6 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
   using M = Mma<T>;
   using op_t = typename M::operand;
   __shared__ KvSmem<T, D> sm;  // k: query rows, v: dO rows
+  __shared__ TsTile<BN> tsm[2];
   __shared__ BiasLds bl;
   constexpr int kCopies = kDwCopies<T, D>;
   __shared__ float dwbins[kCopies][kMaxBuckets + 1];
@@ -664,7 +675,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
     if (si.valid()) {
       issue_kv<T, D>(sm, 0, Q + h * D, dO + h * D, ld, (int)si.lrow(), si.nq(), tid, lane_off);
       if (wave == 0) tsv = p.ts[seq0 + si.q0 + min(lane, si.nq() - 1)];
-      if (wave == 0) ts_tile_fill<BQ>(sm.ts[0], tsv, si.nq(), lane, base);
+      if (wave == 0) ts_tile_fill<BQ>(tsm[0], tsv, si.nq(), lane, base);
     }
     wait_loads();
     __syncthreads();
@@ -677,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
         issue_kv<T, D>(sm, cur ^ 1, Q + h * D, dO + h * D, ld, (int)nx.lrow(), nx.nq(), tid, lane_off);
         if (wave == 0) tsv = p.ts[seq0 + nx.q0 + min(lane, nx.nq() - 1)];
       }
-      const TsTile<BQ>& ts = sm.ts[cur];
+      const TsTile<BQ>& ts = tsm[cur];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       ln.lo_row = kpos - q0;
@@ -710,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kv_kernel(const AttnParams p)
           if (dws.s3 != 0.0f) atomicAdd(&dwl[b0 + 3], dws.s3);
         }
       }
-      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(sm.ts[cur ^ 1], tsv, nx.nq(), lane, base);
+      if (nx.valid() && wave == 0) ts_tile_fill<BQ>(tsm[cur ^ 1], tsv, nx.nq(), lane, base);
       wait_loads();
       __syncthreads();
       si = nx;
@@ -1317,6 +1328,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
   using M = Mma<T>;
   using op_t = typename M::operand;
   __shared__ KvSmem<T, D> sm;
+  __shared__ TsTile<BN> tsm[2];
   __shared__ BiasLds bl;
   __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, g = lane >> 5;
@@ -1379,7 +1391,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
       const int k0 = it.w0 * BN, nv0 = min(BN, kv_len - k0);
       issue_kv<T, D>(sm, 0, Kh, Vh, ld, k0, nv0, tid, lane_off);
       if (wave == 0) tsv = p.ts[seq0 + k0 + min(lane, nv0 - 1)];
-      if (wave == 0) ts_tile_fill<BN>(sm.ts[0], tsv, nv0, lane, base);
+      if (wave == 0) ts_tile_fill<BN>(tsm[0], tsv, nv0, lane, base);
     }
     wait_loads();
     __syncthreads();
@@ -1397,9 +1409,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) 
         issue_kv<T, D>(sm, cur ^ 1, Kh, Vh, ld, nk0, nnv, tid, lane_off);
       }
       const auto stage = [&] {
-        if (more && wave == 0) ts_tile_fill<BN>(sm.ts[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
+        if (more && wave == 0) ts_tile_fill<BN>(tsm[cur ^ 1], tsv, min(BN, kv_len - key0 - BN), lane, base);
       };
-      const TsTile<BN>& ts = sm.ts[cur];
+      const TsTile<BN>& ts = tsm[cur];
       const int4 hdr = ts.hdr;
       const bool fast = lt.fast && hdr.z == 0;
       ln.lim = qpos - key0;
