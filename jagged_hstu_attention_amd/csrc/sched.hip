@@ -98,6 +98,42 @@ __device__ int64_t block_scan(int64_t v, int64_t* buf, int64_t* total) {
   return before + incl - v;
 }
 
+// The same for the 64 lanes of one wave (no barrier): exclusive prefix, and
+// the wave's total in every lane.
+__device__ __forceinline__ int64_t wave_scan(int64_t v, int64_t* total) {
+  const int lane = threadIdx.x & 63;
+  int64_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  *total = __shfl(incl, 63);
+  return incl - v;
+}
+
+// Query tiles, key tiles and stored-G blocks of sequence b, whose rank-local
+// rows start at local0.
+struct SeqCounts {
+  int64_t nq, nk, ng;
+};
+
+__device__ __forceinline__ SeqCounts seq_counts(const SchedParams& p, int b, int64_t local0) {
+  SeqCounts c{0, 0, 0};
+  const SegInfo s = seq_segments(p, b, local0);
+  if (p.q_tile > 0)
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg)  // constant indices keep SegInfo in registers
+      if (sg < s.n) c.nq += (s.len[sg] + p.q_tile - 1) / p.q_tile;
+  const int64_t L = p.offsets[b + 1] - p.offsets[b];
+  if (p.k_tile > 0) c.nk = (L + p.k_tile - 1) / p.k_tile;
+  if (p.gblk_off) {  // stored-G blocks: n(n+1) per head, n = query tiles of kGRows rows
+    const int64_t n = (L + kGRows - 1) / kGRows;
+    c.ng = (int64_t)p.g_heads * n * (n + 1);
+  }
+  return c;
+}
+
 __device__ __forceinline__ int clampc(int64_t c, int hs) { return (int)(c < hs - 1 ? c : hs - 1); }
 
 // Sequence owning flat tile j: the largest b with off[b] <= j.
@@ -137,10 +173,11 @@ __device__ __forceinline__ QTile query_tile(const SchedParams& p, int j) {
   const int sg = i < n0 ? 0 : 1;
   if (sg == 1) i -= n0;
   const int r = i * p.q_tile;
-  const int pos0 = s.pos0[sg] + r, n = min(p.q_tile, s.len[sg] - r);
+  // selects rather than an indexed read keep SegInfo in registers
+  const int pos0 = (sg ? s.pos0[1] : s.pos0[0]) + r, n = min(p.q_tile, (sg ? s.len[1] : s.len[0]) - r);
   const int L = (int)(p.offsets[b + 1] - p.offsets[b]);
   const int hist = L - candidates(p.num_targets, b, L);
-  return QTile{b, pos0, n, s.lrow0[sg] + r, q_tile_cost(pos0, pos0 + n, hist, p.q_cost_tile)};
+  return QTile{b, pos0, n, (sg ? s.lrow0[1] : s.lrow0[0]) + r, q_tile_cost(pos0, pos0 + n, hist, p.q_cost_tile)};
 }
 
 struct KTile {
@@ -155,7 +192,9 @@ __device__ __forceinline__ KTile key_tile(const SchedParams& p, int j) {
   const int k0 = (j - p.ktile_off[b]) * p.k_tile;
   const SegInfo s = seq_segments(p, b, p.local_off[b]);
   int64_t cost = 0;
-  for (int sg = 0; sg < s.n; ++sg) {
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {  // constant indices keep SegInfo in registers
+    if (sg >= s.n) break;
     const int from = max(s.pos0[sg], k0), to = s.pos0[sg] + s.len[sg];
     if (to > from) cost += (to - from + p.k_cost_tile - 1) / p.k_cost_tile;
   }
@@ -227,50 +266,66 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   }
   if (t == 0) qcost_max = 0;
 
-  // Rank-local offsets.
-  int64_t carry = 0;
-  for (int64_t base = 0; base < p.B; base += kSchedThreads) {
-    const int64_t b = base + t;
-    const int64_t len = b < p.B ? local_len(p, (int)b) : 0;
-    int64_t tot;
-    const int64_t pre = block_scan(len, scan, &tot);
-    if (b < p.B) p.local_off[b] = carry + pre;
-    carry += tot;
-  }
-  if (t == 0) p.local_off[p.B] = carry;
-  __syncthreads();
-
-  // Tile counts per sequence, scanned: sequence b owns query tiles
-  // [qtile_off[b], qtile_off[b+1]) and key tiles [ktile_off[b], ktile_off[b+1])
-  // of the flat tile order, so that the passes below run one thread per tile.
+  // Rank-local offsets, then tile counts per sequence, scanned: sequence b
+  // owns query tiles [qtile_off[b], qtile_off[b+1]) and key tiles
+  // [ktile_off[b], ktile_off[b+1]) of the flat tile order, so that the passes
+  // below run one thread per tile.  Key tiles and stored-G blocks share one
+  // scan: both totals stay below 2^31 (the stored-G path is only taken for at
+  // most 2^20 blocks).  Up to 64 sequences, one wave does all of it.
   int64_t qcarry = 0, kcarry = 0, gcarry = 0;
-  for (int64_t base = 0; base < p.B; base += kSchedThreads) {
-    const int64_t b = base + t;
-    int64_t nq = 0, nk = 0, ng = 0;
-    if (b < p.B) {
-      const SegInfo s = seq_segments(p, (int)b, p.local_off[b]);
-      if (p.q_tile > 0)
-        for (int sg = 0; sg < s.n; ++sg) nq += (s.len[sg] + p.q_tile - 1) / p.q_tile;
-      const int64_t L = p.offsets[b + 1] - p.offsets[b];
-      if (p.k_tile > 0) nk = (L + p.k_tile - 1) / p.k_tile;
-      if (p.gblk_off) {  // stored-G blocks: n(n+1) per head, n = query tiles of kGRows rows
-        const int64_t n = (L + kGRows - 1) / kGRows;
-        ng = (int64_t)p.g_heads * n * (n + 1);
+  if (p.B <= 64) {
+    if (t < 64) {
+      const int b = t;
+      const bool in = b < p.B;
+      int64_t tot;
+      const int64_t pre = wave_scan(in ? local_len(p, b) : 0, &tot);
+      if (in) p.local_off[b] = pre;
+      if (t == 0) p.local_off[p.B] = tot;
+      const SeqCounts c = in ? seq_counts(p, b, pre) : SeqCounts{0, 0, 0};
+      int64_t qtot, kgtot;
+      const int64_t qpre = wave_scan(c.nq, &qtot);
+      const int64_t kgpre = wave_scan(c.nk | (c.ng << 32), &kgtot);
+      if (in) {
+        p.qtile_off[b] = (int)qpre;
+        p.ktile_off[b] = (int)(kgpre & 0xFFFFFFFF);
+        if (p.gblk_off) p.gblk_off[b] = kgpre >> 32;
+      }
+      if (t == 0) {
+        scan[0] = qtot;
+        scan[1] = kgtot;
       }
     }
-    // key tiles and stored-G blocks share one scan: both totals stay below
-    // 2^31 (the stored-G path is only taken for at most 2^20 blocks)
-    int64_t qtot, kgtot;
-    const int64_t qpre = block_scan(nq, scan, &qtot);
-    const int64_t kgpre = block_scan(nk | (ng << 32), scan, &kgtot);
-    if (b < p.B) {
-      p.qtile_off[b] = (int)(qcarry + qpre);
-      p.ktile_off[b] = (int)(kcarry + (kgpre & 0xFFFFFFFF));
-      if (p.gblk_off) p.gblk_off[b] = gcarry + (kgpre >> 32);
+    __syncthreads();
+    qcarry = scan[0];
+    kcarry = scan[1] & 0xFFFFFFFF;
+    gcarry = scan[1] >> 32;
+  } else {
+    int64_t carry = 0;
+    for (int64_t base = 0; base < p.B; base += kSchedThreads) {
+      const int64_t b = base + t;
+      const int64_t len = b < p.B ? local_len(p, (int)b) : 0;
+      int64_t tot;
+      const int64_t pre = block_scan(len, scan, &tot);
+      if (b < p.B) p.local_off[b] = carry + pre;
+      carry += tot;
     }
-    qcarry += qtot;
-    kcarry += kgtot & 0xFFFFFFFF;
-    gcarry += kgtot >> 32;
+    if (t == 0) p.local_off[p.B] = carry;
+    __syncthreads();
+    for (int64_t base = 0; base < p.B; base += kSchedThreads) {
+      const int64_t b = base + t;
+      const SeqCounts c = b < p.B ? seq_counts(p, (int)b, p.local_off[b]) : SeqCounts{0, 0, 0};
+      int64_t qtot, kgtot;
+      const int64_t qpre = block_scan(c.nq, scan, &qtot);
+      const int64_t kgpre = block_scan(c.nk | (c.ng << 32), scan, &kgtot);
+      if (b < p.B) {
+        p.qtile_off[b] = (int)(qcarry + qpre);
+        p.ktile_off[b] = (int)(kcarry + (kgpre & 0xFFFFFFFF));
+        if (p.gblk_off) p.gblk_off[b] = gcarry + (kgpre >> 32);
+      }
+      qcarry += qtot;
+      kcarry += kgtot & 0xFFFFFFFF;
+      gcarry += kgtot >> 32;
+    }
   }
   if (t == 0) {
     p.qtile_off[p.B] = (int)qcarry;
@@ -338,18 +393,30 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   // Descending exclusive scans of both histograms at once (query counts in
   // the low half, key counts in the high half; both totals stay below 2^31):
   // start[c] = number of tiles with cost > c.  Each thread rewrites only the
-  // bin it read.
+  // bin it read.  Up to 64 bins, one wave scans them.
   int64_t carry2 = 0;
-  for (int base = 0; base < hs; base += kSchedThreads) {
-    const int c = hs - 1 - (base + t);
-    const int64_t v = c >= 0 ? ((int64_t)histk[c] << 32) | (uint32_t)histq[c] : 0;
-    int64_t tot;
-    const int64_t pre = carry2 + block_scan(v, scan, &tot);
-    if (c >= 0) {
-      histq[c] = (int)(pre & 0xFFFFFFFF);
-      histk[c] = (int)(pre >> 32);
+  if (hs <= 64) {
+    if (t < 64) {
+      const int c = hs - 1 - t;
+      const int64_t v = c >= 0 ? ((int64_t)histk[c] << 32) | (uint32_t)histq[c] : 0;
+      const int64_t pre = wave_scan(v, &carry2);
+      if (c >= 0) {
+        histq[c] = (int)(pre & 0xFFFFFFFF);
+        histk[c] = (int)(pre >> 32);
+      }
     }
-    carry2 += tot;
+  } else {
+    for (int base = 0; base < hs; base += kSchedThreads) {
+      const int c = hs - 1 - (base + t);
+      const int64_t v = c >= 0 ? ((int64_t)histk[c] << 32) | (uint32_t)histq[c] : 0;
+      int64_t tot;
+      const int64_t pre = carry2 + block_scan(v, scan, &tot);
+      if (c >= 0) {
+        histq[c] = (int)(pre & 0xFFFFFFFF);
+        histk[c] = (int)(pre >> 32);
+      }
+      carry2 += tot;
+    }
   }
   if (t == 0) {
     p.ctr[kCtrQTiles] = (int)(carry2 & 0xFFFFFFFF);
