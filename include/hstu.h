@@ -172,12 +172,14 @@ int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q,
  * With cp_size > 1, dk, dv and d_ts_weights are this rank's partial sums (zero
  * rows for keys no local query reaches); summing them over the C ranks gives
  * the gradients of the unsharded problem.  Nothing is normalised, so no
- * forward statistics are needed: the score tile is recomputed.  With bf16,
- * d_qk >= 64 and cp_size == 1 the key-major pass also stores the score
- * gradient G = dS (bf16, one 64-key x 128-query block per causal tile pair,
- * H * sum_b n_b (n_b + 1) blocks of 16 KiB, n_b = ceil(L_b / 128)) in the
- * workspace and the query-major pass computes dQ = G K from it (unless
- * p->flags has HSTU_FLAG_RECOMPUTE_BWD);
+ * forward statistics are needed: the score tile is recomputed.  With bf16
+ * and d_qk >= 64 the key-major pass also stores the score gradient G = dS
+ * (bf16, one 64-key x 128-query block per causal tile pair, H * sum_b n_b
+ * (n_b + 1) blocks of 16 KiB, n_b = ceil(L_b / 128)) in the workspace and the
+ * query-major pass computes dQ = G K from it (unless p->flags has
+ * HSTU_FLAG_RECOMPUTE_BWD; with cp_size > 1 only when every boundary of this
+ * rank's two chunks, other than a sequence's end, is a multiple of 128 rows,
+ * which the library checks on the device: otherwise G is recomputed);
  * hstu_workspace_size(p, 1) then includes room for H (N + 1)
  * (ceil(total_kv / 128) + B) blocks, N = ceil(max_seq_len / 128), or, when
  * p->sum_sq_len is stated and gives fewer, H ceil((sum_sq_len + 382 total_kv

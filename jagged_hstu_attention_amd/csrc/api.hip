@@ -186,8 +186,10 @@ int64_t q_extra_for(const hstu_problem_t* p, int64_t max_qtiles) {
                            cdiv(max_qtiles * tile_cost, hstu::kMinPartTiles));
 }
 
-// Stored score gradients (backward, bf16, d >= 64, cp_size 1): the dK/dV pass
-// writes G, the dQ pass reads it instead of recomputing it.  Blocks needed:
+// Stored score gradients (backward, bf16, d >= 64): the dK/dV pass writes G,
+// the dQ pass reads it instead of recomputing it (for a context-parallel
+// share only when its chunk boundaries fall on 128-row boundaries, which the
+// scheduler checks on the device; the blocks cover the whole sequences).  Blocks needed:
 // sum over sequences and heads of n(n+1), n = ceil(L / kGRows).  Bound from
 // host metadata (every L <= max_seq_len): n <= N = ceil(max_seq_len / kGRows)
 // and sum n <= ceil(T / kGRows) + B, so H (N + 1) (ceil(T / kGRows) + B); when
@@ -196,8 +198,7 @@ int64_t q_extra_for(const hstu_problem_t* p, int64_t max_qtiles) {
 // memory-efficient backward, or the bound passes kGMaxBytes.
 constexpr int64_t kGMaxBytes = 16ll << 30;
 int64_t g_blocks_for(const hstu_problem_t* p) {
-  if (p->dtype != HSTU_BF16 || p->d_qk < 64 || p->cp_size != 1 || p->total_kv == 0 ||
-      (p->flags & HSTU_FLAG_RECOMPUTE_BWD))
+  if (p->dtype != HSTU_BF16 || p->d_qk < 64 || p->total_kv == 0 || (p->flags & HSTU_FLAG_RECOMPUTE_BWD))
     return 0;
   const int64_t n = cdiv(p->max_seq_len, hstu::kGRows);
   int64_t per_head = (n + 1) * (cdiv(p->total_kv, hstu::kGRows) + p->num_seqs);

@@ -35,8 +35,10 @@ struct AttnParams {
   // targets_only the query rows are those candidates alone.  NULL: none.
   const int64_t* num_targets;
   int targets_only;
-  // Stored score gradients (backward, bf16, d >= 64, cp_size 1; NULL: the dQ
-  // pass recomputes them).  G of sequence b, head h is kept in blocks of
+  // Stored score gradients (backward, bf16, d >= 64; NULL: the dQ pass
+  // recomputes them).  They are written and read only when the scheduler set
+  // ctr[kCtrGMode] (a context-parallel share whose chunk boundaries are not
+  // 128-row aligned recomputes them).  G of sequence b, head h is kept in blocks of
   // kGKeys keys x kGRows query rows, block (query tile i, key tile t) at
   // index gblk_off[b] + h n(n+1) + i(i+1) + t with n = ceil(L_b / kGRows)
   // (query tile i sees key tiles 0 .. 2i+1), each block a row-major

@@ -1082,6 +1082,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
   const int n_work = p.ctr[kCtrKTiles] * H;
   float* dwl = dwbins[lane % kHalfDwCopies];
   const float beta = kNegLog2e * p.alpha;
+  const bool g_on = p.g && p.ctr[kCtrGMode];  // stored score gradient written by this pass
 
   for (;;) {
     const int w = pop_item(&item_slot, p.ctr + kCtrKNext, tid);
@@ -1118,7 +1119,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
     // stored G: this item's blocks start at gbase (query tile 0); the wave's
     // key tile and first row within it
     int64_t gbase = 0;
-    if (p.g) {
+    if (g_on) {
       const int64_t nt = (p.offsets[it.b + 1] - seq0 + kGRows - 1) / kGRows;
       gbase = p.gblk_off[it.b] + h * nt * (nt + 1);
     }
@@ -1205,7 +1206,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         xch[wave][1][lane] = own_p[1];
         xch[wave][2][lane] = own_g[0];
         xch[wave][3][lane] = own_g[1];
-      } else if (p.g) {
+      } else if (g_on) {
         // a block that is not live stores zeros as its G
         xch[wave][2][lane] = u32x4{};
         xch[wave][3][lane] = u32x4{};
@@ -1223,7 +1224,7 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
         contract_half<D>(dvacc, db, ofs, hf, par_p, hf ^ 1);
         contract_half<D>(dkacc, qb, ofs, hf, par_g, hf ^ 1);
       }
-      if (p.g && wave < 4) {
+      if (g_on && wave < 4) {
         // stored G, written after the products (the loading waves wait for
         // their tile loads here): this wave's 32 keys over the step's 64 rows,
         // its own block (rows 0-31) and its partner's (rows 32-63; zero where a
@@ -1327,6 +1328,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(const AttnParams p) {
   using M = Mma<T>;
   using op_t = typename M::operand;
+  if (p.g && p.ctr[kCtrGMode]) return;  // bwd_q_g_kernel does the pass from the stored gradient
   __shared__ KvSmem<T, D> sm;
   __shared__ TsTile<BN> tsm[2];
   __shared__ BiasLds bl;
@@ -1459,6 +1461,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_g_kernel(const AttnParams p
   using T = __bf16;
   using Ptr = __attribute__((address_space(3))) s16x4*;
   static_assert(BN == kGKeys && BM == kGRows, "one stored-G block per key tile of a query tile");
+  if (!p.ctr[kCtrGMode]) return;  // the schedule's shares are not aligned: bwd_q_kernel does the pass
   __shared__ QgSmem<D> sm;
   __shared__ int item_slot;
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, g = lane >> 5;
@@ -1641,9 +1644,13 @@ hipError_t launch_all(const AttnParams& p, int which, int max_items, int cus, hi
   } else {
     if constexpr (sizeof(T) == 2 && D >= 64) {
       if (p.g) {
+        // the scheduler decides on the device whether the stored gradient
+        // applies (ctr[kCtrGMode]); a context-parallel share launches both
+        // passes and the one that does not apply returns at once (without
+        // context parallelism it always applies)
         auto k = bwd_q_g_kernel<D>;
         hipLaunchKernelGGL(k, dim3(grid_for(k, max_items, cus)), dim3(kThreads), 0, s, p);
-        return hipGetLastError();
+        if (p.cp_size == 1) return hipGetLastError();
       }
     }
     auto k = bwd_q_kernel<T, D>;

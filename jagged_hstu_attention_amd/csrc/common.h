@@ -51,6 +51,8 @@ enum Ctr : int {
   kCtrKNext = 3,    // work counter popped by the dK/dV kernel
   kCtrQNext2 = 4,   // second query-tile counter (backward dQ pass)
   kCtrSplits = 5,   // number of split query tiles
+  kCtrGMode = 6,    // 1: the stored score gradient applies to this schedule (every query
+                    // segment starts, and ends or meets the sequence end, on a 128-row boundary)
   kCtrCount = 64
 };
 

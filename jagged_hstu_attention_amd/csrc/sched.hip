@@ -112,6 +112,23 @@ __device__ __forceinline__ int64_t wave_scan(int64_t v, int64_t* total) {
   return incl - v;
 }
 
+// Whether the stored score gradient can serve sequence b: its blocks cover
+// 128-row query tiles at multiples of 128, so every query segment must start
+// on such a boundary and end on one or at the sequence end (always so without
+// context parallelism: one segment from 0 to L).
+__device__ __forceinline__ bool g_aligned(const SchedParams& p, int b, int64_t local0) {
+  const SegInfo s = seq_segments(p, b, local0);
+  const int L = (int)(p.offsets[b + 1] - p.offsets[b]);
+  bool ok = true;
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    if (sg >= s.n) break;
+    const int end = s.pos0[sg] + s.len[sg];
+    ok = ok && s.pos0[sg] % kGRows == 0 && (end % kGRows == 0 || end == L);
+  }
+  return ok;
+}
+
 // Query tiles, key tiles and stored-G blocks of sequence b, whose rank-local
 // rows start at local0.
 struct SeqCounts {
@@ -253,6 +270,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
   __shared__ QTile qcache[kSplitTileCache];
   __shared__ int qslot[kSplitTileCache];
   __shared__ int qcost_max;
+  __shared__ int g_ok;
   const int t = threadIdx.x;
   const int hs = p.hist_size;
 
@@ -264,7 +282,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
     histq[i] = 0;
     histk[i] = 0;
   }
-  if (t == 0) qcost_max = 0;
+  if (t == 0) {
+    qcost_max = 0;
+    g_ok = 1;
+  }
 
   // Rank-local offsets, then tile counts per sequence, scanned: sequence b
   // owns query tiles [qtile_off[b], qtile_off[b+1]) and key tiles
@@ -282,6 +303,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
       if (in) p.local_off[b] = pre;
       if (t == 0) p.local_off[p.B] = tot;
       const SeqCounts c = in ? seq_counts(p, b, pre) : SeqCounts{0, 0, 0};
+      if (p.gblk_off && in && !g_aligned(p, b, pre)) g_ok = 0;
       int64_t qtot, kgtot;
       const int64_t qpre = wave_scan(c.nq, &qtot);
       const int64_t kgpre = wave_scan(c.nk | (c.ng << 32), &kgtot);
@@ -314,6 +336,8 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
     for (int64_t base = 0; base < p.B; base += kSchedThreads) {
       const int64_t b = base + t;
       const SeqCounts c = b < p.B ? seq_counts(p, (int)b, p.local_off[b]) : SeqCounts{0, 0, 0};
+      // (read by thread 0 after the barriers of the scans below)
+      if (p.gblk_off && b < p.B && !g_aligned(p, (int)b, p.local_off[b])) g_ok = 0;
       int64_t qtot, kgtot;
       const int64_t qpre = block_scan(c.nq, scan, &qtot);
       const int64_t kgpre = block_scan(c.nk | (c.ng << 32), scan, &kgtot);
@@ -331,6 +355,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const SchedParams 
     p.qtile_off[p.B] = (int)qcarry;
     p.ktile_off[p.B] = (int)kcarry;
     if (p.gblk_off) p.gblk_off[p.B] = gcarry;
+    p.ctr[kCtrGMode] = p.gblk_off ? g_ok : 0;
   }
   __syncthreads();
   const int nqt = (int)qcarry, nkt = (int)kcarry;

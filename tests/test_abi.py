@@ -75,14 +75,16 @@ def test_workspace_size_valid_and_monotone():
 
 @pytest.mark.parametrize("kw,stored", [
     (dict(), True), (dict(d_qk=128, d_v=128, max_seq_len=300, num_seqs=1), True),
-    (dict(dtype=1), False), (dict(d_qk=32, d_v=32), False), (dict(cp_size=2, total_q=150), False),
+    (dict(dtype=1), False), (dict(d_qk=32, d_v=32), False), (dict(cp_size=2, total_q=150), True),
 ])
 def test_backward_workspace_holds_score_gradient_blocks(kw, stored):
-    # bf16, d >= 64, one CP rank: the backward workspace holds the stored score
-    # gradient, 16 KiB blocks of 64 keys x 128 query rows, bounded by
-    # H (N + 1) (ceil(T / 128) + B) with N = ceil(max_seq_len / 128), plus the
-    # per-sequence block offsets (int64 [B + 1], 256-byte aligned); the
-    # memory-efficient flag drops both.  Otherwise the flag changes nothing.
+    # bf16, d >= 64: the backward workspace holds the stored score gradient,
+    # 16 KiB blocks of 64 keys x 128 query rows over the whole sequences (also
+    # for a context-parallel share, which uses them when its chunk boundaries
+    # are 128-row aligned), bounded by H (N + 1) (ceil(T / 128) + B) with
+    # N = ceil(max_seq_len / 128), plus the per-sequence block offsets
+    # (int64 [B + 1], 256-byte aligned); the memory-efficient flag drops both.
+    # Otherwise the flag changes nothing.
     p = make_problem(**kw)
     lean = make_problem(flags=hstu.HSTU_FLAG_RECOMPUTE_BWD, **kw)
     full, small = hstu.workspace_size(p, True), hstu.workspace_size(lean, True)

@@ -127,6 +127,42 @@ def test_cp_share_matches_oracle_and_unsharded(dtype, lengths, cps):
         assert_close(sdw.cpu().numpy(), to_f64(fdw), dtype, f"cp{cp} summed dw vs unsharded")
 
 
+# With bf16 and d >= 64 a share whose chunk boundaries all fall on 128-row
+# boundaries uses the stored score gradient for dQ; any other share
+# recomputes it.  The scheduler takes that decision on the device and leaves
+# it in the workspace's counters (the first 64 int32 of the workspace; the
+# decision is counter 6), which the test reads back.
+@pytest.mark.parametrize("lengths,cp,aligned", [([512, 1024, 1536], 2, True), ([1024, 2048], 4, True),
+                                                ([1024, 2048, 640], 4, False), ([512, 1000], 2, False)])
+def test_cp_share_stored_gradient(lengths, cp, aligned):
+    import torch
+    wl = synth.custom(lengths, num_heads=2, d_qk=64, d_v=64, num_buckets=128, dtype="bf16", seed=33, w_std=0.5)
+    d = upload(wl)
+    m = hstu()
+    for r in range(cp):
+        ql, dol, lo, hi = rank_inputs(m, d, wl, cp, r)
+        args = (dol, ql, d["k"], d["v"], d["offsets"], d["ts"], d["w"], wl.max_seq_len)
+        p = m.problem(ql, d["k"], d["v"], d["offsets"], d["w"], wl.max_seq_len, cp_size=cp, cp_rank=r)
+        ws = torch.zeros(m.workspace_size(p, True), dtype=torch.uint8, device=ql.device)
+        dq, dk, dv, dw = m.jagged_attn_bwd(*args, cp_size=cp, cp_rank=r, workspace=ws)
+        torch.cuda.synchronize()
+        assert ws[24:28].view(torch.int32).item() == int(aligned), f"cp{cp} r{r} stored-gradient decision"
+        lq, lk, lv, lw = m.jagged_attn_bwd(*args, cp_size=cp, cp_rank=r, recompute=True)
+        q_re, _ = oracle.reorder(wl.q.f64, wl.offsets, cp)
+        d_re, _ = oracle.reorder(wl.dout.f64, wl.offsets, cp)
+        rq, rk, rv, rw = oracle.cp_attn_bwd(d_re[lo:hi], q_re[lo:hi], wl.k.f64, wl.v.f64, wl.offsets, wl.ts,
+                                            wl.w.f64, 128, cp, r)
+        tag = f"cp{cp} r{r}"
+        assert_close(to_f64(dq), rq, "bf16", tag + " dq")
+        assert_close(to_f64(dk), rk, "bf16", tag + " dk")
+        assert_close(to_f64(dv), rv, "bf16", tag + " dv")
+        assert_close(to_f64(dw), rw, "bf16", tag + " dw")
+        # dK and dV come from the same key pass either way (d(ts_weights) too,
+        # but its sums are fp32 atomics whose order varies from run to run)
+        assert torch.equal(dk, lk) and torch.equal(dv, lv), tag
+        assert_close(to_f64(lq), rq, "bf16", tag + " dq (recomputed)")
+
+
 @pytest.mark.parametrize("seed", [1004, 1104])
 def test_cp8_rank3_len16384_full(seed):
     # every element of the rank's O and dQ and of its partial dK, dV and
