@@ -222,18 +222,22 @@ def profile_workload(m, name, steps, warmup):
     kernel are the timed ones)."""
     import torch
     import synth
+    cp = {}
     if name == "len3072":
         wl = synth.config("bf16_len3072")
     elif name == "skewed":
         wl = synth.config("skewed_powerlaw")
+    elif name == "cp8":  # rank 3's share of the CP=8 batch of length 16384
+        wl = synth.config("cp8_rank3_len16384")
+        cp = dict(cp_size=synth.CP_SIZE, cp_rank=synth.CP_RANK)
     else:  # the skewed batch's head shape on uniform lengths: 16 x 3072, H = 8, d = 64, 256 buckets
         wl = synth.custom([3072] * 16, num_heads=8, d_qk=64, d_v=64, num_buckets=256, dtype="bf16",
                           gap_mean=600.0, seed=1008)
-    case = Case(wl)
+    case = Case(wl, **cp)
     for _ in range(warmup):
         case.step()
     kms = time_kernels(case, steps)
-    pairs = causal_pairs(wl.lengths)
+    pairs = cp_rank_pairs(wl.lengths, cp["cp_size"], cp["cp_rank"]) if cp else causal_pairs(wl.lengths)
     kfl = kernel_flops(pairs, wl.num_heads, wl.d_qk, wl.d_v)
     torch.cuda.synchronize()
     return {"profile": name, "warmup": warmup, "steps": steps, "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
@@ -519,7 +523,7 @@ def main():
     ap.add_argument("--counter-run", action="store_true",
                     help="for rocprofv3 --pmc: a 256 MiB device copy (calibration), then 3 forward+backward "
                          "steps of the 3072-length workload; no timing")
-    ap.add_argument("--profile", choices=["len3072", "skewed", "uniform_d64"],
+    ap.add_argument("--profile", choices=["len3072", "skewed", "uniform_d64", "cp8"],
                     help="for rocprofv3 --kernel-trace: W warmup then K timed steps of one workload (one schedule "
                          "per step); prints the per-kernel HIP-event averages of the timed steps as JSON")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
