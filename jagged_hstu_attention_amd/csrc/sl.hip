@@ -123,11 +123,16 @@ __global__ __launch_bounds__(kSelThreads) void sl_select_kernel(const int64_t* _
       if ((x & himask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (t == 0) {
-      uint32_t acc = 0, d = 0;
-      while (acc + hist[d] < need) acc += hist[d++];
-      s_prefix = prefix | (d << shift);
-      s_need = need - acc;
+    // the digit holding the need-th smallest key: one bin per thread, an
+    // exclusive scan of the counts, and the one bin whose range [before,
+    // before + count) contains need - 1 publishes it
+    static_assert(kSelThreads == 256, "one histogram bin per thread");
+    const uint32_t c = hist[t];
+    uint32_t all;
+    const uint32_t before = scan_sel(c, sbuf, &all);
+    if (before < need && need <= before + c) {
+      s_prefix = prefix | ((uint32_t)t << shift);
+      s_need = need - before;
     }
     __syncthreads();
     prefix = s_prefix;
@@ -135,21 +140,23 @@ __global__ __launch_bounds__(kSelThreads) void sl_select_kernel(const int64_t* _
     __syncthreads();
   }
   // Order-preserving compaction: a row is kept if its key is below the
-  // threshold key, or equal to it and among the first `need` such rows.
-  uint32_t kept_before = 0, eq_before = 0;
+  // threshold key, or equal to it and among the first `need` such rows.  The
+  // rows kept before row j are the smaller keys before it and the first
+  // min(#equal keys before it, need) equal ones, so one scan of both counts
+  // (smaller in the low half, equal in the high half: at most kSelThreads
+  // each per chunk) places every kept row.
+  uint32_t lt_before = 0, eq_before = 0;
   for (int64_t base = 0; base < n; base += kSelThreads) {
     const int64_t j = base + t;
     const uint32_t x = j < n ? k[j] : 0xFFFFFFFFu;
     const uint32_t lt = j < n && x < prefix ? 1u : 0u;
     const uint32_t eq = j < n && x == prefix ? 1u : 0u;
-    uint32_t eq_total;
-    const uint32_t eq_rank = eq_before + scan_sel(eq, sbuf, &eq_total);
-    const uint32_t sel = lt | (eq && eq_rank < need ? 1u : 0u);
-    uint32_t sel_total;
-    const uint32_t pos = kept_before + scan_sel(sel, sbuf, &sel_total);
-    if (sel) index[o + pos] = lo + j;
-    kept_before += sel_total;
-    eq_before += eq_total;
+    uint32_t total;
+    const uint32_t pre = scan_sel(lt | (eq << 16), sbuf, &total);
+    const uint32_t lt_rank = lt_before + (pre & 0xFFFFu), eq_rank = eq_before + (pre >> 16);
+    if (lt || (eq && eq_rank < need)) index[o + lt_rank + min(eq_rank, need)] = lo + j;
+    lt_before += total & 0xFFFFu;
+    eq_before += total >> 16;
   }
 }
 
