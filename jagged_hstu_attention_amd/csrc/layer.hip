@@ -120,6 +120,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // 64 x 8 x kNormChunks): each lane holds whole 16-byte chunks.
 constexpr int kNormChunks = 8;
 
+template <int CH>  // 16-byte chunks per lane: the row width is at most 64 x 8 x CH
 __global__ __launch_bounds__(kNormThreads) void norm_gate_kernel(const __bf16* __restrict__ o,
                                                                  const __bf16* __restrict__ u,
                                                                  __bf16* __restrict__ y, int64_t T, int width,
@@ -131,13 +132,17 @@ __global__ __launch_bounds__(kNormThreads) void norm_gate_kernel(const __bf16* _
   const u32x4* orow = reinterpret_cast<const u32x4*>(o + t * width);
   const u32x4* urow = reinterpret_cast<const u32x4*>(u + t * width);
   u32x4* yrow = reinterpret_cast<u32x4*>(y + t * width);
-  float x[kNormChunks][8];
+  // both rows are loaded up front, so that the U row's latency passes during
+  // the two reductions
+  float x[CH][8];
+  bf16x8 gate[CH];
   float sum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kNormChunks; ++j) {
+  for (int j = 0; j < CH; ++j) {
     const int ch = lane + 64 * j;
     if (ch < nchunks) {
       const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(orow + ch));
+      gate[j] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(urow + ch));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[j][e] = (float)v[e];
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_gate_kernel(const __bf16* _
   const float mean = wave_sum(sum) / (float)width;
   float sq = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kNormChunks; ++j) {
+  for (int j = 0; j < CH; ++j) {
     if (lane + 64 * j < nchunks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -159,10 +164,10 @@ __global__ __launch_bounds__(kNormThreads) void norm_gate_kernel(const __bf16* _
   }
   const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)width + eps);
 #pragma unroll
-  for (int j = 0; j < kNormChunks; ++j) {
+  for (int j = 0; j < CH; ++j) {
     const int ch = lane + 64 * j;
     if (ch < nchunks) {
-      const bf16x8 g = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(urow + ch));
+      const bf16x8 g = gate[j];
       float r[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = (x[j][e] - mean) * rstd * (float)g[e];
@@ -188,9 +193,15 @@ hipError_t launch_proj(const ProjParams& p, hipStream_t s) {
 
 hipError_t launch_norm_gate(const void* o, const void* u, void* y, int64_t T, int width, float eps, hipStream_t s) {
   const int64_t blocks = (T + (kNormThreads / 64) - 1) / (kNormThreads / 64);
-  hipLaunchKernelGGL(norm_gate_kernel, dim3((unsigned)blocks), dim3(kNormThreads), 0, s,
-                     static_cast<const __bf16*>(o), static_cast<const __bf16*>(u), static_cast<__bf16*>(y), T, width,
-                     eps);
+  // the fewest chunks per lane that hold the row: registers (and so the
+  // waves in flight) follow the row width
+  const int per_lane = (width / 8 + 63) / 64;
+  const auto k = per_lane <= 1 ? norm_gate_kernel<1>
+                 : per_lane <= 2 ? norm_gate_kernel<2>
+                 : per_lane <= 4 ? norm_gate_kernel<4>
+                                 : norm_gate_kernel<kNormChunks>;
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kNormThreads), 0, s, static_cast<const __bf16*>(o),
+                     static_cast<const __bf16*>(u), static_cast<__bf16*>(y), T, width, eps);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ def test_projection_matches_oracle(T, Dm, H, d):
         assert_close(to_f64(g), r, "bf16", name)
 
 
-@pytest.mark.parametrize("T,width", [(300, 512), (7, 8), (1000, 4096), (49152, 512)])
+@pytest.mark.parametrize("T,width", [(300, 512), (7, 8), (64, 1024), (5, 1536), (33, 2048), (1000, 4096), (49152, 512)])
 def test_norm_gate_matches_oracle(T, width):
     rng = np.random.default_rng(T + width)
     o = synth.from_f32((rng.standard_normal((T, width)) * 3 + 1).astype(np.float32), "bf16")
