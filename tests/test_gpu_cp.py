@@ -163,6 +163,38 @@ def test_cp_share_stored_gradient(lengths, cp, aligned):
         assert_close(to_f64(lq), rq, "bf16", tag + " dq (recomputed)")
 
 
+@pytest.mark.parametrize("lengths,cp,r", [([1024, 2048], 4, 1), ([512, 1000], 2, 1)])
+def test_cp_share_shared_schedule(lengths, cp, r):
+    # one schedule per step for a share too: the forward builds both passes'
+    # lists (and the stored-gradient decision) in a backward-sized workspace,
+    # the backward reuses them; two steps give the bits of separately
+    # scheduled calls
+    import torch
+    wl = synth.custom(lengths, num_heads=2, d_qk=128, d_v=128, num_buckets=128, dtype="bf16", seed=35, w_std=0.5)
+    d = upload(wl)
+    m = hstu()
+    ql, dol, lo, hi = rank_inputs(m, d, wl, cp, r)
+    args = (ql, d["k"], d["v"], d["offsets"], d["ts"], d["w"], wl.max_seq_len)
+    o_ref = m.jagged_attn_fwd(*args, cp_size=cp, cp_rank=r)
+    g_ref = m.jagged_attn_bwd(dol, *args, cp_size=cp, cp_rank=r)
+    p = m.problem(ql, d["k"], d["v"], d["offsets"], d["w"], wl.max_seq_len, cp_size=cp, cp_rank=r,
+                  shared_schedule=True)
+    ws = torch.empty(m.workspace_size(p, True), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        o = m.jagged_attn_fwd(*args, cp_size=cp, cp_rank=r, workspace=ws, shared_schedule=True)
+        g = m.jagged_attn_bwd(dol, *args, cp_size=cp, cp_rank=r, workspace=ws, shared_schedule=True)
+        assert torch.equal(o, o_ref)
+        for name, a, b in zip(("dq", "dk", "dv"), g, g_ref):
+            assert torch.equal(a, b), name
+        assert_close(to_f64(g[3]), to_f64(g_ref[3]), "bf16", "dw")
+    q_re, _ = oracle.reorder(wl.q.f64, wl.offsets, cp)
+    d_re, _ = oracle.reorder(wl.dout.f64, wl.offsets, cp)
+    rq, rk, rv, rw = oracle.cp_attn_bwd(d_re[lo:hi], q_re[lo:hi], wl.k.f64, wl.v.f64, wl.offsets, wl.ts, wl.w.f64,
+                                        128, cp, r)
+    assert_close(to_f64(g[0]), rq, "bf16", "dq vs oracle")
+    assert_close(to_f64(g[3]), rw, "bf16", "dw vs oracle")
+
+
 @pytest.mark.parametrize("seed", [1004, 1104])
 def test_cp8_rank3_len16384_full(seed):
     # every element of the rank's O and dQ and of its partial dK, dV and
