@@ -69,29 +69,60 @@ template <int N> struct alignas(16) TsTile {
   int2 blk[N / 32];
 };
 
+// Min and max over each 16-lane row, left in every lane of the row: two
+// quad permutations, then the half-row and row mirrors (DPP moves, no LDS
+// round trip).
+__device__ __forceinline__ void row_min_max(int32_t& mn, int32_t& mx) {
+  int32_t a = __builtin_amdgcn_update_dpp(0, mn, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+  int32_t b = __builtin_amdgcn_update_dpp(0, mx, 0xB1, 0xF, 0xF, false);
+  mn = min(mn, a);
+  mx = max(mx, b);
+  a = __builtin_amdgcn_update_dpp(0, mn, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+  b = __builtin_amdgcn_update_dpp(0, mx, 0x4E, 0xF, 0xF, false);
+  mn = min(mn, a);
+  mx = max(mx, b);
+  a = __builtin_amdgcn_update_dpp(0, mn, 0x141, 0xF, 0xF, false);  // lane 7 - i within 8 lanes
+  b = __builtin_amdgcn_update_dpp(0, mx, 0x141, 0xF, 0xF, false);
+  mn = min(mn, a);
+  mx = max(mx, b);
+  a = __builtin_amdgcn_update_dpp(0, mn, 0x140, 0xF, 0xF, false);  // lane 15 - i within the row
+  b = __builtin_amdgcn_update_dpp(0, mx, 0x140, 0xF, 0xF, false);
+  mn = min(mn, a);
+  mx = max(mx, b);
+}
+
 // Filled by one wave: lane j holds the timestamp of row j; rows >= nvalid
-// (nvalid >= 1) are invalid.
+// (nvalid >= 1, the same in every lane) are invalid.  The ranges are reduced
+// with row-local DPP moves and four lane reads, so the staging costs no LDS
+// round trips of its own.
 template <int N>
 __device__ __forceinline__ void ts_tile_fill(TsTile<N>& t, int64_t ts, int nvalid, int lane, int64_t base) {
   static_assert(N == 64, "one wave fills the tile");
-  const int64_t last = __shfl(ts, nvalid - 1);
+  const int src = __builtin_amdgcn_readfirstlane(nvalid - 1);
+  const uint64_t tsu = (uint64_t)ts;
+  const uint32_t last_lo = __builtin_amdgcn_readlane((uint32_t)tsu, src);
+  const uint32_t last_hi = __builtin_amdgcn_readlane((uint32_t)(tsu >> 32), src);
+  const int64_t last = (int64_t)(((uint64_t)last_hi << 32) | last_lo);
   const int64_t v = lane < nvalid ? ts : last;
   const int64_t rel = v - base;
   const bool wide = __ballot(rel <= -(1ll << 30) || rel >= (1ll << 30)) != 0;
   const int32_t r32 = wide ? 0 : (int32_t)rel;
   int32_t mn = r32, mx = r32;
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) {
-    mn = min(mn, __shfl_xor(mn, off));
-    mx = max(mx, __shfl_xor(mx, off));
-  }
-  // mn/mx now hold the range of this lane's 32-row half
+  row_min_max(mn, mx);
+  const int32_t n0 = __builtin_amdgcn_readlane(mn, 0), n1 = __builtin_amdgcn_readlane(mn, 16);
+  const int32_t n2 = __builtin_amdgcn_readlane(mn, 32), n3 = __builtin_amdgcn_readlane(mn, 48);
+  const int32_t x0 = __builtin_amdgcn_readlane(mx, 0), x1 = __builtin_amdgcn_readlane(mx, 16);
+  const int32_t x2 = __builtin_amdgcn_readlane(mx, 32), x3 = __builtin_amdgcn_readlane(mx, 48);
   t.un[0][lane] = r32;
   t.un[1][lane] = ~r32;
   t.t64[lane] = v;
-  if ((lane & 31) == 0) t.blk[lane >> 5] = int2{mn, mx};
-  const int32_t mn2 = min(mn, __shfl_xor(mn, 32)), mx2 = max(mx, __shfl_xor(mx, 32));
-  if (lane == 0) t.hdr = int4{mn2, mx2, wide ? 1 : 0, 0};
+  if (lane == 0) {
+    // the range of each 32-row half, and of the tile
+    const int32_t b0n = min(n0, n1), b0x = max(x0, x1), b1n = min(n2, n3), b1x = max(x2, x3);
+    t.blk[0] = int2{b0n, b0x};
+    t.blk[1] = int2{b1n, b1x};
+    t.hdr = int4{min(b0n, b1n), max(b0x, b1x), wide ? 1 : 0, 0};
+  }
 }
 
 // Per-lane plan of an unmasked tile.
