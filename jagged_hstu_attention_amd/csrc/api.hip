@@ -830,7 +830,8 @@ int hstu_layer_projection(const void* x, const void* w, int64_t total_rows, int6
   CHECK_PTR(v, "v");
   CHECK_PTR(q, "q");
   CHECK_PTR(k, "k");
-  if ((total_rows + hstu::proj_tile_rows() - 1) / hstu::proj_tile_rows() >= 65536)
+  if ((total_rows + hstu::proj_tile_rows() - 1) / hstu::proj_tile_rows() >= 65536 ||
+      hstu::proj_workgroups(total_rows, num_heads * (2 * d_v + 2 * d_qk)) >= (1ll << 31))
     return fail(HSTU_EUNSUPPORTED, "total_rows %lld too large for the projection grid", (long long)total_rows);
   hstu::ProjParams pp{};
   pp.x = x;

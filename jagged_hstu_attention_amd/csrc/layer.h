@@ -23,6 +23,7 @@ int proj_tile_rows();
 int proj_tile_cols();
 int proj_tile_k();
 int norm_max_width();
+int64_t proj_workgroups(int64_t T, int64_t N);  // the projection launch's grid
 
 hipError_t launch_proj(const ProjParams& p, hipStream_t s);
 hipError_t launch_norm_gate(const void* o, const void* u, void* y, int64_t T, int width, float eps, hipStream_t s);

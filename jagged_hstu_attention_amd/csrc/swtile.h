@@ -101,6 +101,34 @@ __device__ __forceinline__ void tile_load_async(T* __restrict__ dst, const T* __
   }
 }
 
+// Instructions per wave of a full tile's tile_load_async.
+template <typename T, int D, int ROWS, int NT>
+constexpr int tile_load_steps() {
+  return ROWS * SwTile<T, D>::C / 64 / (NT / 64);
+}
+
+// Instruction k (0 <= k < tile_load_steps) of this wave's tile_load_async, so
+// that a caller can spread a tile's loads between its MFMAs: a direct-to-LDS
+// load holds the wave at its issue while the memory pipeline accepts it, and
+// the MFMAs issued before it keep the matrix pipe busy meanwhile.  A partial
+// tile issues all of its (clamped) loads at k = 0.  Together the steps load
+// what tile_load_async loads.
+template <typename T, int D, int ROWS, int NT, int AUX = 0>
+__device__ __forceinline__ void tile_load_step(T* __restrict__ dst, const T* __restrict__ src, int64_t ld,
+                                               int nvalid, int tid, uint32_t lane_off, int k) {
+  using S = SwTile<T, D>;
+  using LdsPtr = __attribute__((address_space(3))) void*;
+  constexpr int kWaves = NT / 64;
+  if (nvalid >= ROWS) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t shift = (uint32_t)(k * (NT / S::C) * ld * (int64_t)sizeof(T));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(src), (LdsPtr)(dst + (wave + k * kWaves) * 64 * S::kElems), 16,
+                                             lane_off, shift, 0, AUX);
+  } else if (k == 0) {
+    tile_load_async<T, D, ROWS, NT, AUX>(dst, src, ld, nvalid, tid, lane_off);
+  }
+}
+
 // Wait for every outstanding memory operation of this wave (the direct-to-LDS
 // loads among them); a barrier afterwards publishes the tile to the workgroup.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }

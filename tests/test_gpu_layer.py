@@ -16,7 +16,8 @@ def hstu():
     return m
 
 
-@pytest.mark.parametrize("T,Dm,H,d", [(300, 128, 2, 64), (1, 64, 1, 128), (129, 256, 4, 32), (49152, 512, 4, 128)])
+@pytest.mark.parametrize("T,Dm,H,d", [(300, 128, 2, 64), (1, 64, 1, 128), (129, 256, 4, 32), (1300, 64, 2, 64),
+                                     (49152, 512, 4, 128)])
 def test_projection_matches_oracle(T, Dm, H, d):
     li = synth.layer_inputs(T, Dm, H, d, d, seed=T + Dm)
     x, w = upload_tensor(li.x), upload_tensor(li.w)
