@@ -1027,6 +1027,7 @@ __device__ __forceinline__ void pair_exact(u32x4* own_p, u32x4* own_g, float* dw
 constexpr int kHalfThreads = 512;
 constexpr int kHalfKeys = 128;
 constexpr int kHalfDwCopies = 4;
+static_assert(kHalfDwCopies >= 4, "the row-summed bin updates use one copy per 16-lane row");
 
 // Workgroup barrier for LDS data only: it waits for this wave's LDS accesses
 // and not for its global memory operations (a __syncthreads waits for all of
@@ -1262,10 +1263,29 @@ __global__ __launch_bounds__(kHalfThreads, 1) void bwd_kv_half_kernel(const Attn
       // tiles and exchange slots, once all waves are here (the loading waves
       // wait for their tile loads; the stored-G writes stay in flight)
       if (loader) wait_loads();
-      if (dw4[0] != 0.0f) atomicAdd(&dwl[blo], dw4[0]);
-      if (dw4[1] != 0.0f) atomicAdd(&dwl[blo + 1], dw4[1]);
-      if (dw4[2] != 0.0f) atomicAdd(&dwl[blo + 2], dw4[2]);
-      if (dw4[3] != 0.0f) atomicAdd(&dwl[blo + 3], dw4[3]);
+      {
+        // d(ts_weights) of a plan step.  Neighbouring keys usually share
+        // their first bin, and lanes adding to one LDS address serialise: a
+        // 16-lane row whose lanes share it sums its four contributions first
+        // (DPP moves) and its first lane adds them, each row to a bin copy of
+        // its own; otherwise every lane adds its own four.
+        int bmn = blo, bmx = blo;
+        row_min_max(bmn, bmx);
+        if (bmn == bmx) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) dw4[k] = row_sum(dw4[k]);
+          if ((lane & 15) == 0) {
+            float* dr = dwbins[lane >> 4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (dw4[k] != 0.0f) atomicAdd(&dr[blo + k], dw4[k]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (dw4[k] != 0.0f) atomicAdd(&dwl[blo + k], dw4[k]);
+        }
+      }
       lds_barrier();
       si = nx;
       cur ^= 1;

@@ -91,6 +91,16 @@ __device__ __forceinline__ void row_min_max(int32_t& mn, int32_t& mx) {
   mx = max(mx, b);
 }
 
+// Sum over each 16-lane row, the same value left in every lane of the row
+// (the moves pair lanes symmetrically, so every lane adds the same operands).
+__device__ __forceinline__ float row_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
 // Filled by one wave: lane j holds the timestamp of row j; rows >= nvalid
 // (nvalid >= 1, the same in every lane) are invalid.  The ranges are reduced
 // with row-local DPP moves and four lane reads, so the staging costs no LDS
