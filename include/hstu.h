@@ -50,6 +50,11 @@
  *     (one host synchronisation, so not for use under stream capture) and
  *     returns HSTU_EINVAL, naming what is broken, before launching anything
  *     else.  Off by default: the calls then never synchronise.
+ *   - HSTU_LOG: when set to anything but "" or "0" (read once per process),
+ *     every entry point that validates or launches work writes one line to
+ *     stderr: its name, the problem's sizes when it takes a problem, and the
+ *     status it returns with hstu_last_error's message when that is not
+ *     HSTU_OK.  Logging adds no synchronisation.
  */
 #ifndef HSTU_H
 #define HSTU_H

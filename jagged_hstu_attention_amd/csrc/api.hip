@@ -428,6 +428,35 @@ bool validate_enabled() {
   return v && v[0] && std::strcmp(v, "0") != 0;
 }
 
+// Host-side call logging: with HSTU_LOG set to a value other than "0" in the
+// environment, every entry point that launches or validates work writes one
+// line to stderr: its name, the problem's sizes when it takes one, and the
+// status it returns (with the error message when it is not HSTU_OK).
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("HSTU_LOG");
+    return v && v[0] && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+int logged(const char* name, const hstu_problem_t* p, int rc) {
+  if (!log_enabled()) return rc;
+  static const char* const kStatus[] = {"HSTU_OK", "HSTU_EINVAL", "HSTU_EUNSUPPORTED", "HSTU_EWORKSPACE", "HSTU_EHIP"};
+  const char* st = rc >= 0 && rc <= 4 ? kStatus[rc] : "?";
+  if (p)
+    std::fprintf(stderr,
+                 "hstu: %s dtype=%d flags=%d B=%lld H=%lld d_qk=%lld d_v=%lld NB=%lld max_len=%lld T_kv=%lld "
+                 "T_q=%lld cp=%lld/%lld -> %s%s%s\n",
+                 name, (int)p->dtype, (int)p->flags, (long long)p->num_seqs, (long long)p->num_heads,
+                 (long long)p->d_qk, (long long)p->d_v, (long long)p->num_buckets, (long long)p->max_seq_len,
+                 (long long)p->total_kv, (long long)p->total_q, (long long)p->cp_rank, (long long)p->cp_size, st,
+                 rc ? ": " : "", rc ? g_last_error.c_str() : "");
+  else
+    std::fprintf(stderr, "hstu: %s -> %s%s%s\n", name, st, rc ? ": " : "", rc ? g_last_error.c_str() : "");
+  return rc;
+}
+
 int check_offsets(const hstu::CheckParams& cp, hipStream_t s) {
   if (!validate_enabled()) return HSTU_OK;
   static std::mutex mu;  // one flag per device: checks on one device take turns
@@ -502,7 +531,7 @@ int hstu_timing_read(int kernel, double* total_ms, int64_t* launches) {
 
 const char* hstu_last_error(void) { return g_last_error.c_str(); }
 
-int hstu_bucket_edges(int64_t num_buckets, uint32_t* edges_out) {
+static int hstu_bucket_edges_body(int64_t num_buckets, uint32_t* edges_out) {
   if (!edges_out) return fail(HSTU_EINVAL, "edges_out is NULL");
   if (num_buckets < 1) return fail(HSTU_EINVAL, "num_buckets %lld < 1", (long long)num_buckets);
   if (num_buckets > hstu::kMaxBuckets)
@@ -572,7 +601,7 @@ int fwd_impl(const hstu_problem_t* p, const void* q, const void* k, const void* 
 
 }  // namespace
 
-int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+static int hstu_jagged_attn_fwd_body(const hstu_problem_t* p, const void* q, const void* k, const void* v,
                          const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
                          void* workspace, size_t workspace_bytes, void* stream) {
   const int rc = validate(p);
@@ -580,7 +609,7 @@ int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, 
   return fwd_impl(p, q, k, v, offsets, nullptr, 0, timestamps, ts_weights, out, workspace, workspace_bytes, stream);
 }
 
-int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+static int hstu_jagged_attn_fwd_targets_body(const hstu_problem_t* p, const void* q, const void* k, const void* v,
                                  const int64_t* offsets, const int64_t* num_targets, int q_targets_only,
                                  const int64_t* timestamps, const void* ts_weights, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
@@ -600,7 +629,7 @@ int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q, const v
                   workspace_bytes, stream);
 }
 
-int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* q, const void* k, const void* v,
+static int hstu_jagged_attn_bwd_body(const hstu_problem_t* p, const void* dout, const void* q, const void* k, const void* v,
                          const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* dq,
                          void* dk, void* dv, float* d_ts_weights, void* workspace, size_t workspace_bytes,
                          void* stream) {
@@ -725,7 +754,7 @@ extern "C" {
 
 size_t hstu_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
-int hstu_jagged_attn_fwd_noalloc(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+static int hstu_jagged_attn_fwd_noalloc_body(const hstu_problem_t* p, const void* q, const void* k, const void* v,
                                  const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
                                  void* stream) {
   int rc = validate(p);
@@ -758,7 +787,7 @@ int hstu_jagged_attn_fwd_noalloc(const hstu_problem_t* p, const void* q, const v
   return fwd_impl(p, q, k, v, offsets, nullptr, 0, timestamps, ts_weights, out, ws, kScratchBytes, stream, split);
 }
 
-int hstu_sl_select(const int64_t* offsets, int64_t num_seqs, int64_t total_rows, int64_t max_seq_len, double alpha,
+static int hstu_sl_select_body(const int64_t* offsets, int64_t num_seqs, int64_t total_rows, int64_t max_seq_len, double alpha,
                    const float* seq_uniform, const uint32_t* token_keys, int64_t* out_offsets, int64_t* out_index,
                    void* stream) {
   if (num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)num_seqs);
@@ -790,7 +819,7 @@ int hstu_sl_select(const int64_t* offsets, int64_t num_seqs, int64_t total_rows,
   return HSTU_OK;
 }
 
-int hstu_gather_rows(const void* in, void* out, int64_t row_bytes, const int64_t* index, const int64_t* count,
+static int hstu_gather_rows_body(const void* in, void* out, int64_t row_bytes, const int64_t* index, const int64_t* count,
                      int64_t max_rows, void* stream) {
   if (row_bytes < 1) return fail(HSTU_EINVAL, "row_bytes %lld < 1", (long long)row_bytes);
   if (max_rows < 0) return fail(HSTU_EINVAL, "max_rows %lld < 0", (long long)max_rows);
@@ -810,7 +839,7 @@ int hstu_gather_rows(const void* in, void* out, int64_t row_bytes, const int64_t
   return HSTU_OK;
 }
 
-int hstu_layer_projection(const void* x, const void* w, int64_t total_rows, int64_t d_model, int64_t num_heads,
+static int hstu_layer_projection_body(const void* x, const void* w, int64_t total_rows, int64_t d_model, int64_t num_heads,
                           int64_t d_qk, int64_t d_v, void* u, void* v, void* q, void* k, void* stream) {
   if (total_rows < 0) return fail(HSTU_EINVAL, "total_rows %lld < 0", (long long)total_rows);
   if (num_heads < 1 || d_qk < 1 || d_v < 1 || d_model < 1) return fail(HSTU_EINVAL, "sizes must be positive");
@@ -851,7 +880,7 @@ int hstu_layer_projection(const void* x, const void* w, int64_t total_rows, int6
   return HSTU_OK;
 }
 
-int hstu_layer_norm_gate(const void* o, const void* u, void* y, int64_t total_rows, int64_t width, double eps,
+static int hstu_layer_norm_gate_body(const void* o, const void* u, void* y, int64_t total_rows, int64_t width, double eps,
                          void* stream) {
   if (total_rows < 0) return fail(HSTU_EINVAL, "total_rows %lld < 0", (long long)total_rows);
   if (width < 8 || width % 8) return fail(HSTU_EUNSUPPORTED, "width %lld is not a positive multiple of 8", (long long)width);
@@ -871,7 +900,7 @@ int hstu_layer_norm_gate(const void* o, const void* u, void* y, int64_t total_ro
   return HSTU_OK;
 }
 
-int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t num_seqs,
+static int hstu_cp_reorder_body(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t num_seqs,
                     int64_t total_rows, int64_t max_seq_len, int64_t cp_size, int inverse, int64_t* out_offsets,
                     void* stream) {
   if (num_seqs < 0) return fail(HSTU_EINVAL, "num_seqs %lld < 0", (long long)num_seqs);
@@ -913,3 +942,61 @@ int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t*
 }
 
 }  // extern "C"
+
+// Exported entry points: each runs its body and, with HSTU_LOG set, logs the call.
+int hstu_bucket_edges(int64_t num_buckets, uint32_t* edges_out) {
+  return logged("hstu_bucket_edges", nullptr, hstu_bucket_edges_body(num_buckets, edges_out));
+}
+
+int hstu_jagged_attn_fwd(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+                         const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return logged("hstu_jagged_attn_fwd", p, hstu_jagged_attn_fwd_body(p, q, k, v, offsets, timestamps, ts_weights, out, workspace, workspace_bytes, stream));
+}
+
+int hstu_jagged_attn_fwd_targets(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+                                 const int64_t* offsets, const int64_t* num_targets, int q_targets_only,
+                                 const int64_t* timestamps, const void* ts_weights, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return logged("hstu_jagged_attn_fwd_targets", p, hstu_jagged_attn_fwd_targets_body(p, q, k, v, offsets, num_targets, q_targets_only, timestamps, ts_weights, out, workspace, workspace_bytes, stream));
+}
+
+int hstu_jagged_attn_bwd(const hstu_problem_t* p, const void* dout, const void* q, const void* k, const void* v,
+                         const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* dq,
+                         void* dk, void* dv, float* d_ts_weights, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return logged("hstu_jagged_attn_bwd", p, hstu_jagged_attn_bwd_body(p, dout, q, k, v, offsets, timestamps, ts_weights, dq, dk, dv, d_ts_weights, workspace, workspace_bytes, stream));
+}
+
+int hstu_jagged_attn_fwd_noalloc(const hstu_problem_t* p, const void* q, const void* k, const void* v,
+                                 const int64_t* offsets, const int64_t* timestamps, const void* ts_weights, void* out,
+                                 void* stream) {
+  return logged("hstu_jagged_attn_fwd_noalloc", p, hstu_jagged_attn_fwd_noalloc_body(p, q, k, v, offsets, timestamps, ts_weights, out, stream));
+}
+
+int hstu_sl_select(const int64_t* offsets, int64_t num_seqs, int64_t total_rows, int64_t max_seq_len, double alpha,
+                   const float* seq_uniform, const uint32_t* token_keys, int64_t* out_offsets, int64_t* out_index,
+                   void* stream) {
+  return logged("hstu_sl_select", nullptr, hstu_sl_select_body(offsets, num_seqs, total_rows, max_seq_len, alpha, seq_uniform, token_keys, out_offsets, out_index, stream));
+}
+
+int hstu_gather_rows(const void* in, void* out, int64_t row_bytes, const int64_t* index, const int64_t* count,
+                     int64_t max_rows, void* stream) {
+  return logged("hstu_gather_rows", nullptr, hstu_gather_rows_body(in, out, row_bytes, index, count, max_rows, stream));
+}
+
+int hstu_layer_projection(const void* x, const void* w, int64_t total_rows, int64_t d_model, int64_t num_heads,
+                          int64_t d_qk, int64_t d_v, void* u, void* v, void* q, void* k, void* stream) {
+  return logged("hstu_layer_projection", nullptr, hstu_layer_projection_body(x, w, total_rows, d_model, num_heads, d_qk, d_v, u, v, q, k, stream));
+}
+
+int hstu_layer_norm_gate(const void* o, const void* u, void* y, int64_t total_rows, int64_t width, double eps,
+                         void* stream) {
+  return logged("hstu_layer_norm_gate", nullptr, hstu_layer_norm_gate_body(o, u, y, total_rows, width, eps, stream));
+}
+
+int hstu_cp_reorder(const void* in, void* out, int64_t row_bytes, const int64_t* offsets, int64_t num_seqs,
+                    int64_t total_rows, int64_t max_seq_len, int64_t cp_size, int inverse, int64_t* out_offsets,
+                    void* stream) {
+  return logged("hstu_cp_reorder", nullptr, hstu_cp_reorder_body(in, out, row_bytes, offsets, num_seqs, total_rows, max_seq_len, cp_size, inverse, out_offsets, stream));
+}

@@ -394,3 +394,44 @@ def test_layer_step_validation():
     assert N(g, g, g, 10, 512, -1.0, None) == 1
     assert N(None, g, g, 10, 512, 1e-6, None) == 1
     assert N(g, g, g, 0, 512, 1e-6, None) == 0        # nothing to do
+
+
+_LOG_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from jagged_hstu_attention_amd import _lib
+lib = _lib.load()
+p = _lib.Problem()
+for k, v in dict(dtype=0, flags=0, num_seqs=4, num_heads=2, d_qk=64, d_v=64, num_buckets=0, max_seq_len=100,
+                 total_kv=300, total_q=300, cp_size=1, cp_rank=0).items():
+    setattr(p, k, v)
+d = ctypes.c_void_p(16)
+rc = lib.hstu_jagged_attn_fwd(ctypes.byref(p), d, d, d, d, d, d, d, d, 1 << 30, None)
+rc2 = lib.hstu_cp_reorder(d, d, 8, None, 2, 10, 5, 2, 0, None, None)
+print(rc, rc2)
+"""
+
+
+@pytest.mark.parametrize("value,logs", [("1", True), ("0", False), (None, False)])
+def test_log_env_writes_one_line_per_call(value, logs):
+    # HSTU_LOG=1: each entry point writes its name, the problem's sizes and the
+    # status it returns to stderr (read once per process, hence a subprocess
+    # per setting); unset or "0": nothing is written
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("HSTU_LOG", None)
+    if value is not None:
+        env["HSTU_LOG"] = value
+    r = subprocess.run([sys.executable, "-c", _LOG_SCRIPT, ROOT], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["1", "1"]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("hstu: ")]
+    if not logs:
+        assert lines == []
+        return
+    assert len(lines) == 2
+    assert lines[0].startswith("hstu: hstu_jagged_attn_fwd dtype=0 flags=0 B=4 H=2 d_qk=64 d_v=64 NB=0 ")
+    assert "-> HSTU_EINVAL: " in lines[0]
+    assert lines[1].startswith("hstu: hstu_cp_reorder -> HSTU_EINVAL: ")
