@@ -100,7 +100,7 @@ typedef struct {
   int64_t num_seqs;     /* B >= 0 */
   int64_t num_heads;    /* H >= 1 */
   int64_t d_qk;         /* Q/K head width; supported: 32, 64, 128 */
-  int64_t d_v;          /* V head width; must equal d_qk in this build */
+  int64_t d_v;          /* V head width; must equal d_qk (the kernels assume it) */
   int64_t num_buckets;  /* NB in [1, 512] */
   int64_t max_seq_len;  /* host copy of max_b (offsets[b+1] - offsets[b]) (the full
                            global length when cp_size > 1); an upper bound is fine */
