@@ -183,7 +183,7 @@ COUNTER_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o <name>
 # bwd_kv_half_kernel and bwd_q_g_kernel, otherwise bwd_kv_kernel and
 # bwd_q_kernel).
 KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_kv": "bwd_kv_", "bwd_q": "bwd_q_", "sched": "sched_kernel",
-                  "reorder": "reorder_kernel"}
+                  "reorder": "reorder_kernel", "proj": "proj_kernel", "norm_gate": "norm_gate_kernel"}
 
 
 def traffic_summary(fetch_csv, write_csv, out_path):
@@ -522,8 +522,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--counter-run", action="store_true",
                     help="for rocprofv3 --pmc: a 256 MiB device copy (calibration), then 3 forward+backward "
-                         "steps of the 3072-length workload; no timing")
-    ap.add_argument("--profile", choices=["len3072", "skewed", "uniform_d64", "cp8"],
+                         "steps of the 3072-length workload, 15 chunk-pair reorders and 3 calls of each layer "
+                         "step; no timing")
+    ap.add_argument("--profile", choices=["len3072", "skewed", "uniform_d64", "cp8", "layer"],
                     help="for rocprofv3 --kernel-trace: W warmup then K timed steps of one workload (one schedule "
                          "per step); prints the per-kernel HIP-event averages of the timed steps as JSON")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
@@ -580,7 +581,24 @@ def main():
             for a, b in bufs:
                 m.cp_reorder(a, off, 16384, 8, out=b, out_offsets=seg)
         torch.cuda.synchronize()
+        del bufs
+        torch.cuda.empty_cache()
+        # the layer steps at the 3072-length shape (T = 49152, d_model = 512,
+        # H = 4, d = 128), 3 calls each on freshly written inputs
+        T, Dm, H, d = 49152, 512, 4, 128
+        for i in range(3):
+            x = torch.randn(T, Dm, device="cuda").to(torch.bfloat16)
+            w = (torch.randn(4 * H * d, Dm, device="cuda") * 0.05).to(torch.bfloat16)
+            outs = m.layer_projection(x, w, H, d, d)
+            o = torch.randn(T, H * d, device="cuda").to(torch.bfloat16)
+            u = torch.randn(T, H * d, device="cuda").to(torch.bfloat16)
+            m.layer_norm_gate(o, u)
+            torch.cuda.synchronize()
+            del x, w, outs, o, u
         print(json.dumps({"counter_run": True, "copy_bytes": src.numel()}), flush=True)
+        return
+    if args.profile == "layer":  # the layer steps' launches, timed as in the bench line
+        print(json.dumps({"profile": "layer", **layer_steps(m, args.steps)}), flush=True)
         return
     if args.profile:
         print(json.dumps(profile_workload(m, args.profile, args.steps, args.warmup)), flush=True)
